@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against things other than itself: library routines,
+closed forms, exact rational arithmetic, invariants.  CPU only.
+
+The pages print no worked numeric example for the chain, so the fixed values
+used here are closed forms derived from the definitions (written out in
+tests/golden/closed_forms.txt with their derivations).
+"""
+
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from modulate_ln_amd import workloads as W
+
+FP32, FP64 = 1, 0
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return W.bits(t)
+
+
+def f32(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf(vals) -> np.ndarray:
+    """bf16 bits of values that are exactly representable."""
+    t = torch.tensor(vals, dtype=torch.float32)
+    assert torch.equal(t.to(torch.bfloat16).to(torch.float32), t), "not exact in bf16"
+    return bits_of(t.to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_bf16_from_f32_exhaustive_vs_torch(orc):
+    """Every one of the 2^32 fp32 bit patterns: oracle RNE == torch CPU .to(bfloat16)
+    (NaNs compared as NaN-ness only)."""
+    n = 1 << 26
+    base = np.arange(n, dtype=np.uint32)
+    for chunk in range(1 << 6):
+        u = base + np.uint32(chunk * n)
+        f = u.view(np.float32)
+        mine = orc.bf16_from_f32(f)
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(f)
+        assert np.array_equal(mine[~nan], ref[~nan]), "chunk %d" % chunk
+        assert np.all(np.isnan(f32(mine[nan])))
+
+
+def _nearest_bf16_exact(x: Fraction) -> int:
+    """bf16 bits (non-negative) nearest to x >= 0 by exact rational search, ties to even."""
+    lo, hi = 0, 0x7F80
+    val = lambda b: Fraction(float(np.uint32(b << 16).view(np.float32)))  # noqa: E731
+    if x == 0:
+        return 0
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if val(mid) <= x:
+            lo = mid
+        else:
+            hi = mid
+    vlo = val(lo)
+    vup = Fraction(2) ** 128 if lo + 1 == 0x7F80 else val(lo + 1)
+    if x - vlo < vup - x:
+        return lo
+    if vup - x < x - vlo:
+        return lo + 1
+    return lo if lo % 2 == 0 else lo + 1
+
+
+def test_bf16_from_f64_vs_exact_rationals(orc):
+    rng = np.random.default_rng(1)
+    samples = list(rng.standard_normal(400) * 10.0 ** rng.integers(-40, 38, 400))
+    # values straddling bf16 midpoints by one double ulp, and exact midpoints
+    for b in rng.integers(1, 0x7F7F, 200):
+        lo = float(np.uint32(int(b) << 16).view(np.float32))
+        hi = float(np.uint32((int(b) + 1) << 16).view(np.float32))
+        mid = (lo + hi) / 2
+        samples += [mid, math.nextafter(mid, 0), math.nextafter(mid, math.inf)]
+    samples += [0.0, -0.0, 1e-45, 2.0 ** -134, 3.0 * 2.0 ** -135, 3.3895313892515355e38, 3.4e38, 1e300]
+    for d in samples:
+        got = int(orc._load().orc_bf16_from_f64(float(d)))
+        want = _nearest_bf16_exact(Fraction(abs(d)))
+        if math.copysign(1.0, d) < 0:
+            want |= 0x8000
+        assert got == want, (d, hex(got), hex(want))
+
+
+def test_bf16_from_f64_matches_f32_path_on_floats(orc):
+    rng = np.random.default_rng(2)
+    f = rng.standard_normal(100000).astype(np.float32) * np.float32(3.0)
+    assert np.array_equal(orc.bf16_from_f64(f.astype(np.float64)), orc.bf16_from_f32(f))
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_worked_d4(orc, mode):
+    """x = [-3,-1,1,3]: mean 0, var 5, x_hat = x/sqrt(5+eps) -> bf16 +-1.34375, +-0.447265625.
+    With scale = 1 the factor 1+scale = 2 is exact, doubling the result."""
+    x = bf([[-3.0, -1.0, 1.0, 3.0]])
+    zero = bf([[0.0] * 4])
+    one = bf([[1.0] * 4])
+    out, mean, rstd = orc.ln_modulate(x, zero, zero, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[-1.34375, -0.447265625, 0.447265625, 1.34375]]
+    assert mean[0] == 0.0
+    assert abs(rstd[0] - 1 / math.sqrt(5 + 1e-6)) < 1e-7
+    out2, _, _ = orc.ln_modulate(x, one, zero, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out2).tolist() == [[-2.6875, -0.89453125, 0.89453125, 2.6875]]
+    # scale = -1 makes the factor 0: out = shift exactly
+    sh = bf([[0.5, -0.25, 2.0, -8.0]])
+    out3, _, _ = orc.ln_modulate(x, bf([[-1.0] * 4]), sh, 1, 1e-6, mode, V=4, L=64)
+    assert np.array_equal(out3, sh)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+@pytest.mark.parametrize("D", [4, 8, 12, 512, 2240, 4096, 4100])
+@pytest.mark.parametrize("c", [0.0, 1.0, -3.5, 1000.0])
+def test_constant_rows(orc, mode, D, c):
+    """Constant row: mean = c exactly, var = 0, x_hat = +0, out = +0 with scale = shift = 0."""
+    x = bf([[c] * D] * 2)
+    z = bf([[0.0] * D])
+    V = 8 if D % 8 == 0 else 4
+    out, mean, rstd = orc.ln_modulate(x, z, z, 2, 1e-6, mode, V=V, L=64)
+    assert np.all(out == 0)  # +0 bit pattern
+    assert np.all(mean == c)
+    eps32 = float(np.float32(1e-6))
+    if mode == FP32:
+        want = np.float32(1.0) / np.sqrt(np.float32(eps32))
+        assert np.all(rstd == float(want))
+    else:
+        assert np.allclose(rstd, 1 / math.sqrt(eps32), rtol=1e-15)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_moments_of_xhat(orc, mode):
+    """For random rows with var >> eps: mean(x_hat) ~ 0, var(x_hat) ~ var/(var+eps) ~ 1."""
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(64, 2240, generator=g) * 4 + 1.5).to(torch.bfloat16)
+    z = torch.zeros(1, 2240, dtype=torch.bfloat16)
+    out, _, _ = orc.ln_modulate(bits_of(x), bits_of(z), bits_of(z), 64, 1e-6, mode, V=8, L=64)
+    xh = f32(out).astype(np.float64)
+    assert np.all(np.abs(xh.mean(axis=1)) <= 2.0 ** -8)
+    assert np.all(np.abs(xh.var(axis=1) - 1.0) <= 2.0 ** -7)
+
+
+def test_shift_invariance_fp64_bitwise(orc):
+    """Integer rows in [-64, 64], D a power of two: the mean is exact in double, so
+    LN(x + 64) and LN(x) are bit-identical in the two-pass mode."""
+    rng = np.random.default_rng(4)
+    for D in (64, 512, 4096):
+        xi = rng.integers(-64, 65, size=(8, D)).astype(np.float32)
+        a = orc.bf16_from_f32(xi)
+        b = orc.bf16_from_f32(xi + 64.0)
+        z = bf([[0.0] * D])
+        oa, ma, ra = orc.ln_modulate(a, z, z, 8, 1e-6, FP64)
+        ob, mb, rb = orc.ln_modulate(b, z, z, 8, 1e-6, FP64)
+        assert np.array_equal(oa, ob)
+        assert np.array_equal(ra, rb)
+        assert np.array_equal(mb - ma, np.full(8, 64.0))
+
+
+def test_shift_invariance_fp32_close(orc):
+    rng = np.random.default_rng(5)
+    xi = rng.integers(-64, 65, size=(16, 2240)).astype(np.float32)
+    a = orc.bf16_from_f32(xi)
+    b = orc.bf16_from_f32(xi + 64.0)
+    ma, ra = orc.layernorm_stats(a, 1e-6, FP32)
+    mb, rb = orc.layernorm_stats(b, 1e-6, FP32)
+    assert np.allclose(mb - ma, 64.0, rtol=0, atol=1e-4)
+    assert np.allclose(ra, rb, rtol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Welford and the merge against exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+def _exact_stats(vals):
+    fr = [Fraction(float(v)) for v in vals]
+    n = len(fr)
+    mu = sum(fr) / n
+    m2 = sum((v - mu) ** 2 for v in fr)
+    return mu, m2
+
+
+def test_welford_seq_vs_fractions(orc):
+    rng = np.random.default_rng(6)
+    for n in (1, 2, 3, 5, 7, 16, 100, 1000):
+        for _ in range(5):
+            x = rng.integers(-50, 51, n).astype(np.float32) * np.float32(0.25) + np.float32(rng.integers(-4, 5))
+            m, m2 = orc.welford_seq(x)
+            mu, M2 = _exact_stats(x)
+            scale = float(max(abs(x).max(), 1.0))
+            assert abs(float(m) - float(mu)) <= 4 * n * 2 ** -24 * scale
+            assert abs(float(m2) - float(M2)) <= 8 * n * 2 ** -24 * (float(M2) + n * scale * scale * 2 ** -10) + 1e-30
+
+
+def test_welford_small_exact_cases(orc):
+    m, m2 = orc.welford_seq(np.array([3.0], np.float32))
+    assert (m, m2) == (3.0, 0.0)
+    m, m2 = orc.welford_seq(np.array([1.0, 3.0], np.float32))
+    assert (m, m2) == (2.0, 2.0)  # mean (a+b)/2, m2 = (b-a)^2/2
+
+
+def test_combine_identities(orc):
+    a = np.array([1.5, 4.0, 3.0], np.float32)
+    empty = np.zeros(3, np.float32)
+    assert orc.welford_combine(a, empty) == tuple(a)
+    assert orc.welford_combine(empty, a) == tuple(a)
+    # two singletons a, b: mean (a+b)/2, m2 (b-a)^2/2, exact for small integers
+    for x, y in ((1.0, 3.0), (-5.0, 7.0), (2.0, 2.0), (100.0, -28.0)):
+        got = orc.welford_combine(np.array([x, 0, 1], np.float32), np.array([y, 0, 1], np.float32))
+        assert got == ((x + y) / 2, (y - x) ** 2 / 2, 2.0)
+
+
+def test_combine_vs_fractions(orc):
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        na, nb = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        xa = (rng.standard_normal(na) * 3 + 1).astype(np.float32)
+        xb = (rng.standard_normal(nb) * 3 + 1).astype(np.float32)
+        ma, m2a = orc.welford_seq(xa)
+        mb, m2b = orc.welford_seq(xb)
+        m, m2, n = orc.welford_combine(np.array([ma, m2a, na], np.float32), np.array([mb, m2b, nb], np.float32))
+        mu, M2 = _exact_stats(np.concatenate([xa, xb]))
+        assert n == na + nb
+        assert abs(float(m) - float(mu)) <= 1e-5 * 4
+        assert abs(float(m2) - float(M2)) <= 1e-5 * float(M2) + 1e-5
+
+
+@pytest.mark.parametrize("L", [1, 2, 16, 64])
+def test_fp32_stats_vs_fractions(orc, L):
+    """Row statistics in the fixed order agree with exact rationals within fp32 error."""
+    rng = np.random.default_rng(8)
+    for D in (4, 12, 16, 64, 520):
+        x = (rng.standard_normal((3, D)) * 2 - 0.5).astype(np.float32)
+        xb = orc.bf16_from_f32(x)
+        V = 8 if D % 8 == 0 else 4
+        mean, rstd = orc.layernorm_stats(xb, 1e-6, FP32, V=V, L=L)
+        for r in range(3):
+            mu, M2 = _exact_stats(f32(xb[r]))
+            var = M2 / D
+            ex_rstd = 1.0 / math.sqrt(float(var) + float(np.float32(1e-6)))
+            assert abs(mean[r] - float(mu)) <= 1e-5 * (1 + abs(float(mu)))
+            assert abs(rstd[r] - ex_rstd) <= 1e-5 * ex_rstd
+
+
+def test_fp64_stats_vs_fractions(orc):
+    rng = np.random.default_rng(9)
+    for D in (4, 16, 64):
+        x = orc.bf16_from_f32((rng.standard_normal((4, D)) * 3).astype(np.float32))
+        mean, rstd = orc.layernorm_stats(x, 1e-6, FP64)
+        for r in range(4):
+            mu, M2 = _exact_stats(f32(x[r]))
+            getcontext().prec = 50
+            var = Decimal(M2.numerator) / Decimal(M2.denominator) / D + Decimal(float(np.float32(1e-6)))
+            ex = float(1 / var.sqrt())
+            assert abs(mean[r] - float(mu)) <= 2 ** -50 * (1 + abs(float(mu)))
+            assert abs(rstd[r] - ex) <= 1e-14 * ex
+
+
+# ---------------------------------------------------------------------------
+# special cases that reduce to library routines
+# ---------------------------------------------------------------------------
+
+def _midpoint_margin(vals: np.ndarray) -> np.ndarray:
+    """distance of each value from the nearest bf16 rounding midpoint, in units of |value|"""
+    f = vals.astype(np.float32)
+    u = f.view(np.uint32)
+    lo = (u & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    hi = ((u & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+    mid = (lo + hi) / 2
+    return np.abs(vals - mid) / np.maximum(np.abs(vals), 1e-300)
+
+
+def test_fp64_mode_equals_torch_layer_norm(orc):
+    """scale = shift = 0: the chain is bf16(LN(x)); torch's float64 layer_norm rounded to
+    bf16 must agree except where the double value sits within 1e-12 of a bf16 midpoint."""
+    g = torch.Generator().manual_seed(10)
+    x = (torch.randn(128, 2240, generator=g) * 4).to(torch.bfloat16)
+    z = torch.zeros(1, 2240, dtype=torch.bfloat16)
+    out, _, _ = orc.ln_modulate(bits_of(x), bits_of(z), bits_of(z), 128, 1e-6, FP64)
+    ref64 = torch.nn.functional.layer_norm(x.double(), (2240,), eps=float(np.float32(1e-6))).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+    assert diff.mean() < 1e-4
+
+
+def test_elementwise_tail_equals_torch_eager(orc):
+    """Given the oracle's own fp32 mean/rstd, the rest of ln_modulate is torch's eager bf16
+    chain: bf16((x - mean) * rstd), then (1 + scale), *, + shift as bf16 tensor ops."""
+    wl = W.glm_square(seed=11, S=64, D=4096)
+    x, sc, sh = wl.tensors["x"], wl.tensors["scale"], wl.tensors["shift"]
+    xb = bits_of(x.reshape(64, 4096))
+    out, mean, rstd = orc.ln_modulate(xb, bits_of(sc), bits_of(sh), 64, 1e-5, FP32)
+    xf = x.reshape(64, 4096).float()
+    m = torch.from_numpy(mean.astype(np.float32))[:, None]
+    r = torch.from_numpy(rstd.astype(np.float32))[:, None]
+    xhat = ((xf - m) * r).to(torch.bfloat16)
+    eager = xhat * (1 + sc) + sh
+    assert np.array_equal(out, bits_of(eager))
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_residual_gate_add_equals_torch_eager(orc, mode):
+    """The gated residual is two bf16 tensor ops: torch CPU eager is the reference."""
+    g = torch.Generator().manual_seed(12)
+    B, S, D = 3, 17, 520
+    res = torch.randn(B, S, D, generator=g).to(torch.bfloat16)
+    upd = (torch.randn(B, S, D, generator=g) * 5).to(torch.bfloat16)
+    gate = (torch.randn(B, D, generator=g) * 0.1).to(torch.bfloat16)
+    eager = res + gate[:, None, :] * upd
+    out = orc.residual_gate_add(bits_of(res.reshape(B * S, D)), bits_of(gate), bits_of(upd.reshape(B * S, D)), S, mode)
+    assert np.array_equal(out, bits_of(eager.reshape(B * S, D)))
+    # gate = 0 and update >= 0: t = +0, so out = residual except -0 + +0 = +0
+    res[0, 0, :4] = torch.tensor([-0.0, 0.0, 1.0, -2.0])
+    upd = upd.abs()
+    zero = torch.zeros(B, D, dtype=torch.bfloat16)
+    out0 = orc.residual_gate_add(bits_of(res.reshape(B * S, D)), bits_of(zero), bits_of(upd.reshape(B * S, D)), S, mode)
+    want = bits_of(res.reshape(B * S, D)).copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(out0, want)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_qk_identity_affine_equals_no_affine(orc, mode):
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn(96, 128, generator=g).to(torch.bfloat16)
+    one = torch.ones(128, dtype=torch.bfloat16)
+    zero = torch.zeros(128, dtype=torch.bfloat16)
+    a = orc.qk_head_layernorm(bits_of(x), bits_of(one), bits_of(zero), 1e-6, mode)
+    b = orc.qk_head_layernorm(bits_of(x), None, None, 1e-6, mode)
+    assert np.array_equal(a, b)
+
+
+def test_qk_fp64_equals_torch_affine_layer_norm(orc):
+    wl = W.glm_qk(seed=14, S=8, H=32)
+    q = wl.tensors["q"].reshape(-1, 128)
+    w, b = wl.tensors["wq"], wl.tensors["bq"]
+    out = orc.qk_head_layernorm(bits_of(q), bits_of(w), bits_of(b), 1e-6, FP64)
+    ref64 = torch.nn.functional.layer_norm(q.double(), (128,), w.double(), b.double(), eps=float(np.float32(1e-6))).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+
+
+def test_qk_fp32_within_one_ulp_of_fp64(orc):
+    """The fixed-order fp32 statistics move an affine head output by at most one bf16 ulp."""
+    wl = W.glm_qk(seed=16, S=16, H=32)
+    k = wl.tensors["k"].reshape(-1, 128)
+    w, b = wl.tensors["wk"], wl.tensors["bk"]
+    a = f32(orc.qk_head_layernorm(bits_of(k), bits_of(w), bits_of(b), 1e-6, FP32)).astype(np.float64)
+    r = f32(orc.qk_head_layernorm(bits_of(k), bits_of(w), bits_of(b), 1e-6, FP64)).astype(np.float64)
+    ulp = np.maximum(np.abs(r), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(a - r) <= ulp)
+    assert np.mean(a != r) < 0.01
+
+
+def test_gelu_f64_vs_torch(orc):
+    z = np.linspace(-6, 6, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    got = np.array([orc.gelu_tanh_f64(v) for v in z])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_gelu_f64_tail_vs_decimal(orc):
+    """Large negative z, where 1 + tanh(u) cancels in double: 50-digit decimal reference."""
+    getcontext().prec = 60
+    k0 = (Decimal(2) / Decimal("3.14159265358979323846264338327950288419716939937510")).sqrt()
+    for zf in (-4.0, -6.5, -9.0, -10.25, -12.0):
+        zd = Decimal(zf)
+        u = k0 * (zd + Decimal("0.044715") * zd ** 3)
+        t = (2 * u).exp()  # 0.5 (1 + tanh u) = e^{2u} / (1 + e^{2u})
+        exact = zd * t / (1 + t)
+        got = orc.gelu_tanh_f64(zf)
+        assert abs(Decimal(got) - exact) <= abs(exact) * Decimal("1e-13")
+
+
+def test_bias_gelu_rounds_after_bias(orc):
+    """z = bf16(x + bias) then gelu: with bias = 0 the gelu input is x itself."""
+    g = torch.Generator().manual_seed(15)
+    x = torch.randn(4, 64, generator=g).to(torch.bfloat16)
+    zero = torch.zeros(64, dtype=torch.bfloat16)
+    out, val = orc.bias_gelu_tanh(bits_of(x), bits_of(zero))
+    ref = torch.nn.functional.gelu(x.double(), approximate="tanh").numpy()
+    assert np.allclose(val, ref, rtol=1e-12, atol=1e-300)
+    # a bias that changes the rounding of x + bias: z must be the bf16 sum
+    xb = torch.full((1, 2), 1.0, dtype=torch.bfloat16)
+    bias = torch.tensor([2.0 ** -9, 3 * 2.0 ** -9], dtype=torch.bfloat16)  # 1 + 2^-9 ties to 1, 1 + 3*2^-9 -> 1 + 2^-7
+    _, v = orc.bias_gelu_tanh(bits_of(xb), bits_of(bias))
+    assert v[0, 0] == orc.gelu_tanh_f64(1.0)
+    assert v[0, 1] == orc.gelu_tanh_f64(1.0 + 2.0 ** -7)
+
+
+@pytest.mark.parametrize("mode_pair", [(FP32, FP64)])
+def test_fp32_mode_close_to_fp64_mode(orc, mode_pair):
+    """The two statistics modes agree within the stated tolerances on every workload shape."""
+    for wl, S, eps in ((W.ln_small(), 256, 1e-6), (W.glm_square(S=256), 256, 1e-5)):
+        x = wl.tensors["x"]
+        D = x.shape[-1]
+        xb = bits_of(x.reshape(-1, D))
+        m32, r32 = orc.layernorm_stats(xb, eps, FP32)
+        m64, r64 = orc.layernorm_stats(xb, eps, FP64)
+        sig = 1 / r64
+        assert np.all(np.abs(m32 - m64) <= 1e-5 * np.sqrt(m64 ** 2 + sig ** 2))
+        assert np.all(np.abs(r32 - r64) <= 1e-5 * r64)
