@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the adaLN hot path on one MI355X.
+
+A step is one pass of the GLM-Image (1, 4096, 4096) bf16 pair:
+    h   = ln_modulate(x, scale, shift, eps=1e-5)
+    out = residual_gate_add(x, gate, h)
+with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
+between a synchronize on both sides.  Buffers rotate over enough sets
+(>= 1 GiB in total) that the 256 MB MALL cannot serve a step from cache.
+
+Per-kernel durations come from HIP events recorded on the launch stream
+around every kernel of the timed region; the roofline object reports the
+ln_modulate kernel (the kernel the headline metric names).  The CPU oracle
+(fixed-order fp32 mode) is timed on the host on the same step.
+
+Prints ONE JSON line on stdout; everything else goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "µs/call + achieved HBM GB/s (% of peak), ln_modulate bf16 (1,4096,4096)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lnm_bytes(R: int, D: int, B: int) -> int:
+    # one read + one write of every activation element, plus the scale and shift rows
+    return 2 * R * D * 2 + 2 * B * D * 2
+
+
+def rga_bytes(R: int, D: int, B: int) -> int:
+    # residual and update read, out written, plus the gate rows
+    return 3 * R * D * 2 + B * D * 2
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--buffers", type=int, default=12, help="rotated buffer sets (>= 1 GiB total)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall-time budget of the CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log("bench.py measures one GPU: the adaLN path is row-local and its kernels run on one device; "
+            "--gpus %d is not supported (run with --gpus 1)." % args.gpus)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import modulate_ln_amd as m
+    from modulate_ln_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 2
+    m._native.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- the headline workload ------------------------------------------------
+    wl = W.glm_square()
+    eps = wl.meta["eps"]
+    t = wl.tensors
+    B, S, D = t["x"].shape
+    R = B * S
+    scale, shift, gate = t["scale"].to(dev), t["shift"].to(dev), t["gate"].to(dev)
+    x0 = t["x"].to(dev)
+    NB = max(1, args.buffers)
+    xs = [x0.clone() for _ in range(NB)]
+    hs = [torch.empty_like(x0) for _ in range(NB)]
+    outs = [torch.empty_like(x0) for _ in range(NB)]
+    lnm_calls = [m.ln_modulate(xs[i], scale, shift, eps, out=hs[i], prepare=True) for i in range(NB)]
+    rga_calls = [m.residual_gate_add(xs[i], gate, hs[i], out=outs[i], prepare=True) for i in range(NB)]
+    footprint = NB * 3 * x0.numel() * 2
+    log("workload %s, %d rotated buffer sets (%.2f GiB)" % (wl.name, NB, footprint / 2 ** 30))
+
+    K, Wm = args.steps, args.warmup
+    for i in range(Wm):
+        lnm_calls[i % NB]()
+        rga_calls[i % NB]()
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[2 * i].record(stream)
+        lnm_calls[i % NB]()
+        ev[2 * i + 1].record(stream)
+        rga_calls[i % NB]()
+    ev[2 * K].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lnm_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)]
+    rga_ms = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)]
+    total_ms = ev[0].elapsed_time(ev[2 * K])
+    step_ms = total_ms / K
+    lnm_us = 1000.0 * sum(lnm_ms) / K
+    rga_us = 1000.0 * sum(rga_ms) / K
+    lb, rb = lnm_bytes(R, D, B), rga_bytes(R, D, B)
+    step_gbps = (lb + rb) / (step_ms * 1e-3) / 1e9
+    lnm_gbps = lb / (lnm_us * 1e-6) / 1e9
+    rga_gbps = rb / (rga_us * 1e-6) / 1e9
+    log("step %.2f us (wall %.2f us/step): ln_modulate %.2f us (%.0f GB/s), residual_gate_add %.2f us (%.0f GB/s)"
+        % (step_ms * 1e3, wall / K * 1e6, lnm_us, lnm_gbps, rga_us, rga_gbps))
+    med_lnm = 1000.0 * float(np.median(lnm_ms))
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x with 1% x20 outliers, N(0,0.1) adaLN rows; see workloads.glm_square)",
+        "config": {"workload": "ln_modulate + residual_gate_add, x (1,4096,4096) bf16, eps 1e-5",
+                   "B": B, "S": S, "D": D, "rotated_buffer_sets": NB,
+                   "step_bytes": lb + rb},
+        "us_per_call": {"ln_modulate": round(lnm_us, 3), "ln_modulate_median": round(med_lnm, 3),
+                        "residual_gate_add": round(rga_us, 3)},
+        "achieved_GBps": {"ln_modulate": round(lnm_gbps, 1), "residual_gate_add": round(rga_gbps, 1)},
+        "roofline": {"bound": "hbm", "kernel": "ln_modulate", "achieved": round(lnm_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(lnm_gbps / PEAK_HBM_GBPS, 4),
+                     "algorithmic_bytes": lb, "traffic": None},
+    }
+
+    # ---- a plain copy of the same size: the achievable streaming bandwidth ----
+    cp_src = [torch.empty(2 * x0.numel(), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    cp_dst = [torch.empty_like(cp_src[0]) for _ in range(4)]
+    for i in range(8):
+        cp_dst[i % 4].copy_(cp_src[i % 4])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n_cp = 100
+    for i in range(n_cp):
+        cp_dst[i % 4].copy_(cp_src[i % 4])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cp_us = 1000.0 * e0.elapsed_time(e1) / n_cp
+    cp_gbps = 2 * cp_src[0].numel() * 2 / (cp_us * 1e-6) / 1e9
+    result["copy_reference"] = {"bytes": 2 * cp_src[0].numel() * 2, "us": round(cp_us, 3),
+                                "GBps": round(cp_gbps, 1),
+                                "ln_modulate_frac_of_copy": round(lnm_gbps / cp_gbps, 4)}
+    del cp_src, cp_dst
+    log("copy %.1f GB/s; ln_modulate at %.1f%% of copy, %.1f%% of peak"
+        % (cp_gbps, 100 * lnm_gbps / cp_gbps, 100 * lnm_gbps / PEAK_HBM_GBPS))
+
+    if not args.no_extra:
+        result["other_workloads"] = other_workloads(m, W, dev, stream, log)
+
+    # ---- CPU baseline: the oracle on the same step ----------------------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, wl, lb + rb, args.cpu_seconds, log)
+
+    del xs, hs, outs
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def time_loop(calls, n, stream):
+    import torch
+
+    for c in calls[: min(len(calls), 4)]:
+        c()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / n
+
+
+def other_workloads(m, W, dev, stream, log):
+    """The other workload shapes, each timed over back-to-back calls (buffers rotated
+    so every set of calls touches >= 1 GiB)."""
+    import torch
+
+    res = {}
+
+    def rot(nbytes):
+        return max(2, min(64, -(-(1 << 30) // max(nbytes, 1))))
+
+    # (1,256,512) ln_modulate: launch-bound, report us only
+    wl = W.ln_small()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    calls = [m.ln_modulate(t["x"], t["scale"], t["shift"], 1e-6, prepare=True)]
+    us = time_loop(calls, 2000, stream)
+    res["ln_modulate_1x256x512"] = {"us": round(us, 3), "GBps": round(lnm_bytes(256, 512, 1) / us / 1e3, 1)}
+
+    # Sana (2,1024,2240) transposed input
+    wl = W.sana_transposed()
+    xt = wl.tensors["xt"].to(dev)
+    emb = wl.tensors["emb"].to(dev)
+    nb = rot(2 * xt.numel() * 2)
+    xts = [xt.clone() for _ in range(nb)]
+    outs = [torch.empty(2, 1024, 2240, dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    calls = [m.ln_modulate(xts[i].transpose(1, 2), emb[:, 5], emb[:, 0], 1e-6, out=outs[i], prepare=True)
+             for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    b = lnm_bytes(2048, 2240, 2)
+    res["ln_modulate_2x1024x2240_transposed"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                                                  "pages_H200_us": 14.3}
+    xcs = [xt.transpose(1, 2).contiguous() for _ in range(nb)]
+    calls = [m.ln_modulate(xcs[i], emb[:, 5], emb[:, 0], 1e-6, out=outs[i], prepare=True) for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["ln_modulate_2x1024x2240_contiguous"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del xts, xcs, outs
+
+    # GLM-Image q/k heads (1,4360,32,128)
+    wl = W.glm_qk()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    nb = rot(4 * t["q"].numel() * 2)
+    qs = [t["q"].clone() for _ in range(nb)]
+    ks = [t["k"].clone() for _ in range(nb)]
+    calls = [m.qk_head_layernorm(qs[i], ks[i], t["wq"], t["bq"], t["wk"], t["bk"], 1e-6, prepare=True)
+             for i in range(nb)]
+    us = time_loop(calls, 200, stream)
+    b = 4 * t["q"].numel() * 2 + 4 * 128 * 2
+    res["qk_head_layernorm_1x4360x32x128"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                                               "pages_H200_eager_us": 301.0}
+    del qs, ks, calls
+
+    # bias + tanh-GELU (16384, 12288)
+    wl = W.wan_bias_gelu()
+    x = wl.tensors["x"].to(dev)
+    bias = wl.tensors["bias"].to(dev)
+    xs2 = [x, x.clone()]
+    outs = [torch.empty_like(x) for _ in range(2)]
+    calls = [m.bias_gelu_tanh(xs2[i], bias, out=outs[i], prepare=True) for i in range(2)]
+    us = time_loop(calls, 50, stream)
+    b = 2 * x.numel() * 2 + x.shape[1] * 2
+    res["bias_gelu_tanh_16384x12288"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del xs2, outs, x
+
+    # 20-block DiT chain on (4,4096,3072): 80 launches per pass
+    wl = W.dit_chain()
+    x = wl.tensors["x"].to(dev)
+    embs = [e.to(dev) for e in wl.tensors["embs"]]
+    h = torch.empty_like(x)
+    calls = []
+    for emb in embs:
+        for j in (0, 3):
+            calls.append(m.ln_modulate(x, emb[:, j + 1], emb[:, j], 1e-6, out=h, prepare=True))
+            calls.append(m.residual_gate_add(x, emb[:, j + 2], h, out=x, prepare=True))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    reps = 5
+    for _ in range(reps):
+        for c in calls:
+            c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    R, D = 4 * 4096, 3072
+    b = 40 * (lnm_bytes(R, D, 4) + rga_bytes(R, D, 4))
+    res["dit_chain_20_blocks_4x4096x3072"] = {"ms": round(ms, 4), "GBps": round(b / ms / 1e6, 1),
+                                              "launches": len(calls)}
+    for k, v in res.items():
+        log("%-40s %s" % (k, v))
+    return res
+
+
+def cpu_baseline(W, wl, step_bytes, budget_s, log):
+    """The oracle (fixed-order fp32 mode) on the full step, repeated for ~budget_s of wall time."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    t = wl.tensors
+    B, S, D = t["x"].shape
+    x = W.bits(t["x"].reshape(B * S, D))
+    sc, sh, g = W.bits(t["scale"]), W.bits(t["shift"]), W.bits(t["gate"])
+    orc._load()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        h, _, _ = orc.ln_modulate(x, sc, sh, S, wl.meta["eps"], orc.FP32, V=8, L=64)
+        orc.residual_gate_add(x, g, h, S, orc.FP32)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    gbps = step_bytes * reps / dt / 1e9
+    log("cpu oracle: %d step(s) in %.2f s on %d threads -> %.2f GB/s" % (reps, dt, threads, gbps))
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "full (1,4096,4096) ln_modulate + residual_gate_add step x%d (fp32 fixed-order mode)" % reps,
+            "ms_per_step": round(1000 * dt / reps, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,191 @@
+/*
+ * adaln.h -- C ABI of the MI355X (gfx950) adaLN chain kernels.
+ *
+ * The operations are the eager diffusion-transformer chain that the pages on
+ * SGLang-Diffusion's fused kernels replace with bit-exact fused kernels:
+ * affine-free LayerNorm followed by the adaLN modulation, the per-head q/k
+ * LayerNorm, the gated residual add, and bias + tanh-GELU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are bf16 (dtype argument must be ADALN_BF16).  Every tensor
+ *    pointer is a DEVICE pointer, at least 2-byte aligned.  Strides are in
+ *    elements, non-negative.  Outputs are written contiguously (row-major).
+ *  - Ownership: the caller owns every buffer.  The library never allocates,
+ *    frees or synchronises; it keeps no state between calls, so calls are
+ *    reentrant and thread-safe.
+ *  - Execution: each call enqueues its kernel(s) on `stream` (a hipStream_t
+ *    passed as void*, NULL = the null stream) and returns at once.
+ *  - Errors: 0 = ADALN_OK.  Argument errors are negative codes returned
+ *    synchronously BEFORE anything is launched and before any HIP runtime
+ *    call is made (so they can be checked on a machine without a GPU).  A
+ *    launch failure returns ADALN_ERR_HIP.  adaln_status_str() names a code.
+ *  - An empty problem (a zero row count) is a successful no-op.
+ *  - Exact aliasing of an output with an input is allowed only where an
+ *    entry point says so (same base pointer, identical contiguous layout);
+ *    any other overlap between an output and an input is ADALN_ERR_ALIAS.
+ *
+ * Numerics (every op): fp32 arithmetic in between, results rounded to bf16
+ * (round-to-nearest-even) exactly where the eager PyTorch chain rounds, as
+ * the "Fused Kernels" page, section "Numerical contracts and quality tiers",
+ * requires of its bit-exact kernels.  LayerNorm statistics use the fp32
+ * Welford algorithm in one fixed order (see adaln_order_for): lane l of a
+ * row pushes the elements of vectors l, l+L, l+2L, ... (V consecutive
+ * elements each) in increasing position, with 1/n the correctly rounded
+ * reciprocal; lane states are then merged pairwise at offsets 1, 2, 4, ...
+ * with the Chan-Golub-LeVeque update, lower lane first, an empty side
+ * leaving the other unchanged; var = m2/D, rstd = 1/sqrt(var + eps) with
+ * IEEE-correct division and square root.  No fused multiply-add is formed
+ * other than the ones this order names.
+ */
+#ifndef ADALN_H
+#define ADALN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADALN_ABI_VERSION 1
+
+/* status codes */
+#define ADALN_OK 0
+#define ADALN_ERR_NULL -1      /* a required pointer is NULL                      */
+#define ADALN_ERR_SHAPE -2     /* negative size, hidden % 4 != 0, bad head size  */
+#define ADALN_ERR_DTYPE -3     /* dtype is not ADALN_BF16                        */
+#define ADALN_ERR_ALIGN -4     /* a tensor pointer is not 2-byte aligned         */
+#define ADALN_ERR_ALIAS -5     /* an output overlaps an input other than allowed */
+#define ADALN_ERR_TOO_LARGE -6 /* a size exceeds what the kernels address        */
+#define ADALN_ERR_STRIDE -7    /* a stride is negative or unsupported            */
+#define ADALN_ERR_HIP -8       /* the HIP runtime reported a launch error        */
+#define ADALN_ERR_ARG -9       /* any other invalid argument (unknown op, eps)   */
+
+/* dtypes */
+#define ADALN_BF16 1
+
+/* ops, for adaln_order_for */
+#define ADALN_OP_LN_MODULATE 1
+#define ADALN_OP_QK_HEAD_LAYERNORM 2
+
+/*
+ * ln_modulate -- out = LN(x) * (1 + scale) + shift, bf16 at every eager op.
+ *
+ * Source: prhub report on sglang PR #34015 (Sana fused adaLN), 实现拆解 §1
+ * and 关键源码片段 (layernorm_modulate.py, pass 2): x_hat = bf16(rstd*(x-mean)),
+ * one_plus = bf16(1+scale), y = bf16(x_hat*one_plus), out = bf16(y+shift);
+ * hidden % 4 == 0 is the only shape requirement (实现拆解 §1), tails are
+ * masked.  Per-sample broadcast: scale and shift hold one row per batch
+ * sample (the [B,1,D] adaLN rows passed as [B,D] views).
+ *
+ *  x        [B,S,D] logical; element (b,s,d) at x + b*sx_b + s*sx_s + d*sx_d.
+ *           Any non-negative strides; sx_d == 1 (rows contiguous) and
+ *           sx_s == 1 (the transposed [B,D,S] storage of Sana's permuted
+ *           activations) are the fast paths.
+ *  scale    [B,D] with row stride sscale_b (element stride 1).
+ *  shift    [B,D] with row stride sshift_b (element stride 1).
+ *  eps      added to the biased variance; must be finite and >= 0.
+ *  out      [B,S,D] contiguous.  May be exactly x when x is contiguous
+ *           (sx_d == 1, sx_s == D, sx_b == S*D).
+ *  mean_out, rstd_out   optional ([B*S] fp32 each, row-major); NULL = skip.
+ *  D        % 4 == 0, 4 <= D <= 65536.
+ */
+int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                float* rstd_out, void* stream);
+
+/* 1 if ln_modulate accepts these sizes/strides/dtype (no pointer is read). */
+int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s, int64_t sx_d,
+                        int64_t sscale_b, int64_t sshift_b, int dtype);
+
+/*
+ * residual_gate_add -- out = residual + gate * update, two eager ops:
+ * t = bf16(gate*update), out = bf16(residual + t).
+ *
+ * Source: "Fused Kernels" page, table "adaLN modulation and gating"
+ * (residual_gate_add, bit-exact, replaces residual + gate * update); prhub
+ * report on sglang PR #34008, 实现拆解 §2-3 (the GLM-Image ff-gate sites).
+ * The gate is per batch sample ([B,1,D] rows as a [B,D] view).
+ *
+ *  residual [B,S,D], element (b,s,d) at residual + b*sr_b + s*sr_s + d.
+ *  gate     [B,D] with row stride sg_b.
+ *  update   [B,S,D], element (b,s,d) at update + b*su_b + s*su_s + d.
+ *  out      [B,S,D] contiguous; may be exactly residual or exactly update
+ *           when that input is contiguous.
+ *  D        >= 0, any value.
+ */
+int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_s, const void* gate,
+                      int64_t sg_b, const void* update, int64_t su_b, int64_t su_s, int64_t B,
+                      int64_t S, int64_t D, int dtype, void* out, void* stream);
+
+int residual_gate_add_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b, int64_t sr_s,
+                              int64_t sg_b, int64_t su_b, int64_t su_s, int dtype);
+
+/*
+ * qk_head_layernorm -- per-head affine LayerNorm of q and k in one launch.
+ *
+ * Source: "Fused Kernels" page, table "Normalization" (qk_head_layernorm,
+ * bit-exact, per-head LayerNorm on q/k); prhub report on sglang PR #34008,
+ * 实现拆解 §1 and 风险与影响 (head_dim <= 128, % 4 == 0 in the pages' kernel;
+ * this library accepts head_dim % 4 == 0 up to 256).  The affine LayerNorm is
+ * one eager op, so its output is rounded to bf16 once:
+ * out = bf16(fma(w, (x - mean) * rstd, b)), the product (x-mean)*rstd
+ * rounded to fp32 first.  With w and b both NULL: out = bf16((x-mean)*rstd).
+ *
+ *  q        [B,S,H,Dh], element (b,s,h,d) at q + b*sq_b + s*sq_s + h*sq_h + d.
+ *  k        [B,S,H,Dh], same with sk_*.
+ *  wq,bq    [Dh] each, or both NULL; likewise wk,bk.
+ *  q_out, k_out   [B,S,H,Dh] contiguous; q_out may be exactly q (and
+ *           k_out exactly k) when that input is contiguous.
+ *  Dh       % 4 == 0, 4 <= Dh <= 256.
+ */
+int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h, const void* k,
+                      int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B, int64_t S, int64_t H,
+                      int64_t Dh, const void* wq, const void* bq, const void* wk, const void* bk,
+                      float eps, int dtype, void* q_out, void* k_out, void* stream);
+
+int qk_head_layernorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b,
+                              int64_t sq_s, int64_t sq_h, int64_t sk_b, int64_t sk_s,
+                              int64_t sk_h, int dtype);
+
+/*
+ * bias_gelu_tanh -- z = bf16(x + bias); out = bf16(gelu_tanh(z)).
+ *
+ * Source: PR #37075 report (Wan2.2 NVFP4 bias + GELU), 实现拆解 §1 and
+ * 关键源码片段 (bias_gelu.cuh): the bias is added in fp32, the sum is rounded
+ * back to the tensor dtype, and tanh-GELU is evaluated in fp32 on that
+ * rounded value.  gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3)))
+ * (Hendrycks & Gimpel), evaluated here as z * sigmoid(2u) with the hardware
+ * base-2 exponential; the result is within one bf16 ulp of the correctly
+ * rounded value (tanh has no correctly rounded fp32 implementation to match).
+ *
+ *  x        [rows, width], element (r,j) at x + r*sx_row + j.
+ *  bias     [width].
+ *  out      [rows, width] contiguous; may be exactly x when x is contiguous.
+ *  rows, width >= 0.
+ */
+int bias_gelu_tanh(const void* x, int64_t rows, int64_t width, int64_t sx_row, const void* bias,
+                   int dtype, void* out, void* stream);
+
+int bias_gelu_tanh_can_use(int64_t rows, int64_t width, int64_t sx_row, int dtype);
+
+/*
+ * adaln_order_for -- the fixed fp32 reduction order the kernels use for a
+ * row of D elements of op ADALN_OP_*: *V = elements per vector (8 when
+ * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate, 16 for a
+ * q/k head).  Pure host function.  Returns ADALN_OK or an error code.
+ */
+int adaln_order_for(int op, int64_t D, int* V, int* L);
+
+/* static string naming a status code (never NULL) */
+const char* adaln_status_str(int status);
+
+/* ADALN_ABI_VERSION of the built library */
+int adaln_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADALN_H */

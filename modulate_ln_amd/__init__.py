@@ -1,0 +1,22 @@
+"""adaLN chain kernels for MI355X (gfx950): a C-ABI library of hand-written HIP
+kernels (``libadaln.so``) and this thin torch binding.
+
+    from modulate_ln_amd import ln_modulate, residual_gate_add, qk_head_layernorm, bias_gelu_tanh
+
+The binding only marshals arguments; torch provides device memory and
+streams.  Importing the package does not load the library; the first call
+does, and fails loudly if it has not been built.
+"""
+
+from ._native import AdalnError, order_for, status_str  # noqa: F401
+from .ops import bias_gelu_tanh, ln_modulate, qk_head_layernorm, residual_gate_add  # noqa: F401
+
+__all__ = [
+    "ln_modulate",
+    "residual_gate_add",
+    "qk_head_layernorm",
+    "bias_gelu_tanh",
+    "order_for",
+    "status_str",
+    "AdalnError",
+]

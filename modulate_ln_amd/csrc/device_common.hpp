@@ -1,0 +1,213 @@
+// Device helpers shared by the adaLN kernels (gfx950, wave64).
+//
+// Numerics: this file is compiled with -ffp-contract=off, so every fp32
+// operation rounds on its own; the only fused multiply-adds are the explicit
+// __builtin_fmaf calls the reduction order names.  fp32 denormals are kept
+// (the gfx950 default), division and square root are the IEEE-correct
+// sequences hipcc emits by default.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adaln {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  A 32-bit word holds two consecutive bf16 elements: the
+// lower-addressed one in bits 0..15.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+__device__ __forceinline__ float u16_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two fp32 values to bf16 (round-to-nearest-even; one v_cvt_pk_bf16_f32)
+// and pack them, lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Round a pair to bf16 and widen back: the values the eager chain stores.
+__device__ __forceinline__ void round_pair(float& a, float& b) {
+  uint32_t w = pack_bf16(a, b);
+  a = lo_f32(w);
+  b = hi_f32(w);
+}
+
+// ---------------------------------------------------------------------------
+// Welford push with a compile-time count: N is the count after this element,
+// 1/N is folded by the compiler to the correctly rounded fp32 reciprocal.
+// Order (the pages' _welford_push): delta = x - mean; mean += delta/N as one
+// fma with the reciprocal; m2 += delta * (x - mean_new) as one fma.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void welford_push(float& mean, float& m2, float x) {
+  constexpr float r = 1.0f / (float)N;
+  float delta = x - mean;
+  mean = __builtin_fmaf(delta, r, mean);
+  m2 = __builtin_fmaf(delta, x - mean, m2);
+}
+
+// Chan-Golub-LeVeque merge of two partial states; (ma, m2a, na) is the state
+// of the LOWER lane.  An empty side leaves the other unchanged.
+__device__ __forceinline__ void welford_merge(float& ma, float& m2a, float& na, float mb, float m2b,
+                                              float nb) {
+  float n = na + nb;
+  float f = nb / n;
+  float delta = mb - ma;
+  float m = __builtin_fmaf(delta, f, ma);
+  float m2 = (m2a + m2b) + (delta * delta) * (na * f);
+  bool a_empty = (na == 0.0f);
+  bool b_empty = (nb == 0.0f);
+  float rm = b_empty ? ma : (a_empty ? mb : m);
+  float rm2 = b_empty ? m2a : (a_empty ? m2b : m2);
+  float rn = b_empty ? na : (a_empty ? nb : n);
+  ma = rm;
+  m2a = rm2;
+  na = rn;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange: value held by lane (lane ^ OFF) of the same wave.
+// OFF 1, 2: DPP quad permutes; 4: ds_swizzle xor mode; 8: DPP row rotate
+// by 8 (within 16 lanes that is xor 8); 16, 32: gfx950 permlane swaps.
+// ---------------------------------------------------------------------------
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v) {
+  int i = __builtin_bit_cast(int, v);
+  if constexpr (OFF == 1) {
+    i = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (OFF == 2) {
+    i = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (OFF == 4) {
+    i = __builtin_amdgcn_ds_swizzle(i, (4 << 10) | 0x1F);  // and 0x1f, or 0, xor 4
+  } else if constexpr (OFF == 8) {
+    i = __builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (OFF == 16) {
+    // odd rows of the first operand swap with even rows of the second
+    auto p = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    i = (lane & 16) ? (int)p[0] : (int)p[1];
+  } else {
+    static_assert(OFF == 32, "lane_xor: offset must be 1, 2, 4, 8, 16 or 32");
+    // upper half of the first operand swaps with lower half of the second
+    auto p = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    i = (lane & 32) ? (int)p[0] : (int)p[1];
+  }
+  return __builtin_bit_cast(float, i);
+}
+
+// One level of the pairwise merge tree at distance OFF: lanes l and l^OFF
+// both compute merge(lower, upper), so after the levels 1..OFF every lane
+// of an aligned group of 2*OFF lanes holds the group's state.
+template <int OFF>
+__device__ __forceinline__ void merge_level(float& m, float& m2, float& n, int lane) {
+  float pm = lane_xor<OFF>(m);
+  float pm2 = lane_xor<OFF>(m2);
+  float pn = lane_xor<OFF>(n);
+  const bool upper = (lane & OFF) != 0;
+  float am = upper ? pm : m, am2 = upper ? pm2 : m2, an = upper ? pn : n;
+  float bm = upper ? m : pm, bm2 = upper ? m2 : pm2, bn = upper ? n : pn;
+  welford_merge(am, am2, an, bm, bm2, bn);
+  m = am;
+  m2 = am2;
+  n = an;
+}
+
+// Merge the per-lane states of groups of L lanes (L = 16 or 64).
+template <int L>
+__device__ __forceinline__ void merge_lanes(float& m, float& m2, float& n, int lane) {
+  merge_level<1>(m, m2, n, lane);
+  merge_level<2>(m, m2, n, lane);
+  merge_level<4>(m, m2, n, lane);
+  merge_level<8>(m, m2, n, lane);
+  if constexpr (L == 64) {
+    merge_level<16>(m, m2, n, lane);
+    merge_level<32>(m, m2, n, lane);
+  } else {
+    static_assert(L == 16, "merge_lanes: L must be 16 or 64");
+  }
+}
+
+// var = m2/D, rstd = 1/sqrt(var + eps): IEEE division and square root.
+__device__ __forceinline__ float finalize_rstd(float m2, float D, float eps) {
+  float var = m2 / D;
+  float t = var + eps;
+  float s = __builtin_sqrtf(t);
+  return 1.0f / s;
+}
+
+// ---------------------------------------------------------------------------
+// Vectors of V bf16 elements as V/2 packed words.
+// ---------------------------------------------------------------------------
+template <int V>
+struct Vec {
+  uint32_t w[V / 2];
+};
+
+template <int V>
+__device__ __forceinline__ Vec<V> load_vec(const uint16_t* p) {
+  Vec<V> r;
+  if constexpr (V == 8) {
+    uint4 t = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = t.x;
+    r.w[1] = t.y;
+    r.w[2] = t.z;
+    r.w[3] = t.w;
+  } else {
+    static_assert(V == 4, "V must be 4 or 8");
+    uint2 t = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = t.x;
+    r.w[1] = t.y;
+  }
+  return r;
+}
+
+template <int V>
+__device__ __forceinline__ void store_vec(uint16_t* p, const Vec<V>& v) {
+  if constexpr (V == 8) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+  } else {
+    *reinterpret_cast<uint2*>(p) = make_uint2(v.w[0], v.w[1]);
+  }
+}
+
+// element-wise gather of V elements at stride s (any alignment)
+template <int V>
+__device__ __forceinline__ Vec<V> gather_vec(const uint16_t* p, int64_t s) {
+  Vec<V> r;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i)
+    r.w[i] = (uint32_t)p[(2 * i) * s] | ((uint32_t)p[(2 * i + 1) * s] << 16);
+  return r;
+}
+
+template <int V>
+__device__ __forceinline__ void scatter_vec(uint16_t* p, const Vec<V>& v) {
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    p[2 * i] = (uint16_t)(v.w[i] & 0xffffu);
+    p[2 * i + 1] = (uint16_t)(v.w[i] >> 16);
+  }
+}
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+}  // namespace adaln

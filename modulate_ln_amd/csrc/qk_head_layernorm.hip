@@ -1,0 +1,267 @@
+// qk_head_layernorm: per-head affine LayerNorm of q and k in one launch.
+//
+// Operation: "Fused Kernels" page, table "Normalization" (qk_head_layernorm:
+// per-head LayerNorm on q/k, bit-exact); prhub report on sglang PR #34008,
+// 实现拆解 §1 (fused_qk_head_layernorm) and §3 (called when attention has
+// both q and k).  The affine LayerNorm is one eager op, so the output is
+// rounded to bf16 once: out = bf16(fma(w, (x - mean) * rstd, b)).
+//
+// Design: a head row (Dh <= 256) is small, so 16 lanes -- one DPP row --
+// own a head and a wave normalizes four heads at once.  Lane l of the group
+// owns vectors l, l+16, ... (16-byte loads for V = 8); the merge tree is the
+// four in-row levels 1, 2, 4, 8 (DPP quad permutes, ds_swizzle, row rotate),
+// so no LDS and no cross-row traffic.  q rows come first, then k rows, in
+// one grid.
+#include <utility>
+
+#include "device_common.hpp"
+#include "host_common.hpp"
+
+namespace adaln {
+namespace {
+
+constexpr int kGroup = 16;                  // lanes per head
+constexpr int kGroupsPerBlock = 256 / kGroup;
+constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
+
+struct QkSide {
+  const uint16_t* x;
+  int64_t s_b, s_s, s_h;
+  const uint16_t* w;
+  const uint16_t* bias;
+  uint16_t* out;
+};
+
+struct QkArgs {
+  QkSide side[2];  // q, k
+  int64_t S, H, Dh;
+  int64_t Rq;  // head rows per side (B*S*H)
+  float eps;
+};
+
+template <int V, int E>
+__device__ __forceinline__ float elem(const Vec<V>& v) {
+  return (E & 1) ? hi_f32(v.w[E / 2]) : lo_f32(v.w[E / 2]);
+}
+
+template <int V, int K, int... E>
+__device__ __forceinline__ void push_vec(const Vec<V>& v, float& mean, float& m2,
+                                         std::integer_sequence<int, E...>) {
+  (welford_push<K * V + E + 1>(mean, m2, elem<V, E>(v)), ...);
+}
+
+template <int V, int... K>
+__device__ __forceinline__ void welford_lane(const Vec<V>* buf, int64_t nvec, int l16, float& mean,
+                                             float& m2, std::integer_sequence<int, K...>) {
+  (
+      [&] {
+        if ((int64_t)K * kGroup + l16 < nvec)
+          push_vec<V, K>(buf[K], mean, m2, std::make_integer_sequence<int, V>{});
+      }(),
+      ...);
+}
+
+// UNIFORM: head rows of a side sit at a constant stride s_h (q viewed as
+// [B*S*H, Dh]); otherwise the row index is decomposed into (b, s, h).
+template <int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
+__global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int l16 = lane & (kGroup - 1);
+  const int64_t nvec = a.Dh / V;
+  const float Df = (float)a.Dh;
+  const int64_t nv_lane = nvec > l16 ? (nvec - l16 + kGroup - 1) / kGroup : 0;
+  const int64_t total = 2 * a.Rq;
+  for (int64_t h = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4); h < total;
+       h += (int64_t)gridDim.x * kGroupsPerBlock) {
+    const int which = h >= a.Rq ? 1 : 0;
+    const int64_t rr = h - which * a.Rq;
+    const QkSide& sd = a.side[which];
+    const uint16_t* xr;
+    if constexpr (UNIFORM) {
+      xr = sd.x + rr * sd.s_h;
+    } else {
+      const int64_t hh = rr % a.H;
+      const int64_t t = rr / a.H;
+      const int64_t s = t % a.S;
+      const int64_t b = t / a.S;
+      xr = sd.x + b * sd.s_b + s * sd.s_s + hh * sd.s_h;
+    }
+
+    Vec<V> buf[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t v = (int64_t)k * kGroup + l16;
+      if (v < nvec) buf[k] = GATHER ? gather_vec<V>(xr + v * V, 1) : load_vec<V>(xr + v * V);
+    }
+
+    float mean = 0.0f, m2 = 0.0f;
+    welford_lane<V>(buf, nvec, l16, mean, m2, std::make_integer_sequence<int, NV>{});
+    float n = (float)(nv_lane * V);
+    merge_lanes<kGroup>(mean, m2, n, lane);
+    const float rstd = finalize_rstd(m2, Df, a.eps);
+
+    uint16_t* orow = sd.out + rr * a.Dh;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t v = (int64_t)k * kGroup + l16;
+      if (v < nvec) {
+        Vec<V> o;
+        Vec<V> wv, bv;
+        if constexpr (AFFINE) {
+          wv = GATHER ? gather_vec<V>(sd.w + v * V, 1) : load_vec<V>(sd.w + v * V);
+          bv = GATHER ? gather_vec<V>(sd.bias + v * V, 1) : load_vec<V>(sd.bias + v * V);
+        }
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+          float y0 = (lo_f32(buf[k].w[i]) - mean) * rstd;
+          float y1 = (hi_f32(buf[k].w[i]) - mean) * rstd;
+          if constexpr (AFFINE) {
+            y0 = __builtin_fmaf(lo_f32(wv.w[i]), y0, lo_f32(bv.w[i]));
+            y1 = __builtin_fmaf(hi_f32(wv.w[i]), y1, hi_f32(bv.w[i]));
+          }
+          o.w[i] = pack_bf16(y0, y1);
+        }
+        if constexpr (GATHER)
+          scatter_vec<V>(orow + v * V, o);
+        else
+          store_vec<V>(orow + v * V, o);
+      }
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t heads) {
+  int64_t blocks = (heads + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  return (unsigned)std::min(blocks, kMaxBlocks);
+}
+
+template <int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
+int launch(const QkArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((qk_rows<V, NV, UNIFORM, AFFINE, GATHER>), dim3(grid_for(2 * a.Rq)), dim3(256),
+                     0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int V, int NV, bool UNIFORM, bool AFFINE>
+int pick_gather(const QkArgs& a, bool gather, hipStream_t st) {
+  return gather ? launch<V, NV, UNIFORM, AFFINE, true>(a, st)
+                : launch<V, NV, UNIFORM, AFFINE, false>(a, st);
+}
+
+template <int V, int NV, bool UNIFORM>
+int pick_affine(const QkArgs& a, bool affine, bool gather, hipStream_t st) {
+  return affine ? pick_gather<V, NV, UNIFORM, true>(a, gather, st)
+                : pick_gather<V, NV, UNIFORM, false>(a, gather, st);
+}
+
+template <int V, int NV>
+int pick_uniform(const QkArgs& a, bool uniform, bool affine, bool gather, hipStream_t st) {
+  return uniform ? pick_affine<V, NV, true>(a, affine, gather, st)
+                 : pick_affine<V, NV, false>(a, affine, gather, st);
+}
+
+}  // namespace
+
+static int qk_check_shape(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b, int64_t sq_s,
+                          int64_t sq_h, int64_t sk_b, int64_t sk_s, int64_t sk_h, int dtype) {
+  if (dtype != ADALN_BF16) return ADALN_ERR_DTYPE;
+  if (B < 0 || S < 0 || H < 0 || Dh < 4 || Dh % 4 != 0) return ADALN_ERR_SHAPE;
+  if (Dh > 256) return ADALN_ERR_TOO_LARGE;
+  if (sq_b < 0 || sq_s < 0 || sq_h < 0 || sk_b < 0 || sk_s < 0 || sk_h < 0) return ADALN_ERR_STRIDE;
+  int64_t BS, R, RD;
+  if (!mul_ok(B, S, &BS) || !mul_ok(BS, H, &R) || !mul_ok(R, Dh, &RD) || !mul_ok(R, 2, &BS))
+    return ADALN_ERR_TOO_LARGE;
+  if (!extent_ok({{B, sq_b}, {S, sq_s}, {H, sq_h}, {Dh, 1}}) ||
+      !extent_ok({{B, sk_b}, {S, sk_s}, {H, sk_h}, {Dh, 1}}))
+    return ADALN_ERR_TOO_LARGE;
+  return ADALN_OK;
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int qk_head_layernorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b,
+                                         int64_t sq_s, int64_t sq_h, int64_t sk_b, int64_t sk_s,
+                                         int64_t sk_h, int dtype) {
+  return qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype) == ADALN_OK;
+}
+
+extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h,
+                                 const void* k, int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B,
+                                 int64_t S, int64_t H, int64_t Dh, const void* wq, const void* bq,
+                                 const void* wk, const void* bk, float eps, int dtype, void* q_out,
+                                 void* k_out, void* stream) {
+  int rc = qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype);
+  if (rc != ADALN_OK) return rc;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return ADALN_ERR_ARG;
+  const int64_t R = B * S * H;
+  if (R == 0) return ADALN_OK;
+  if (!q || !k || !q_out || !k_out) return ADALN_ERR_NULL;
+  if ((wq == nullptr) != (bq == nullptr) || (wk == nullptr) != (bk == nullptr)) return ADALN_ERR_NULL;
+  if ((wq == nullptr) != (wk == nullptr)) return ADALN_ERR_NULL;  // affine on both sides or neither
+  const bool affine = wq != nullptr;
+  for (const void* p : {q, k, (const void*)q_out, (const void*)k_out, wq, bq, wk, bk})
+    if (!aligned(p, 2)) return ADALN_ERR_ALIGN;
+
+  const Span sqo = span_of(q_out, {{R * Dh, 1}});
+  const Span sko = span_of(k_out, {{R * Dh, 1}});
+  const Span sq = span_of(q, {{B, sq_b}, {S, sq_s}, {H, sq_h}, {Dh, 1}});
+  const Span sk = span_of(k, {{B, sk_b}, {S, sk_s}, {H, sk_h}, {Dh, 1}});
+  auto contig = [&](int64_t sb, int64_t ss, int64_t sh) {
+    return (H == 1 || sh == Dh) && (S == 1 || ss == H * Dh) && (B == 1 || sb == S * H * Dh);
+  };
+  if (overlaps(sqo, sko)) return ADALN_ERR_ALIAS;
+  if (overlaps(sqo, sq) && !(q_out == q && contig(sq_b, sq_s, sq_h))) return ADALN_ERR_ALIAS;
+  if (overlaps(sko, sk) && !(k_out == k && contig(sk_b, sk_s, sk_h))) return ADALN_ERR_ALIAS;
+  if (overlaps(sqo, sk) || overlaps(sko, sq)) return ADALN_ERR_ALIAS;
+  if (affine) {
+    for (const void* p : {wq, bq, wk, bk}) {
+      const Span sw = span_of(p, {{Dh, 1}});
+      if (overlaps(sw, sqo) || overlaps(sw, sko)) return ADALN_ERR_ALIAS;
+    }
+  }
+
+  QkArgs a;
+  a.side[0] = QkSide{(const uint16_t*)q, sq_b, sq_s, sq_h, (const uint16_t*)wq, (const uint16_t*)bq,
+                     (uint16_t*)q_out};
+  a.side[1] = QkSide{(const uint16_t*)k, sk_b, sk_s, sk_h, (const uint16_t*)wk, (const uint16_t*)bk,
+                     (uint16_t*)k_out};
+  a.S = S;
+  a.H = H;
+  a.Dh = Dh;
+  a.Rq = R;
+  a.eps = eps;
+
+  int V = 0;
+  order_for(ADALN_OP_QK_HEAD_LAYERNORM, Dh, &V, nullptr);
+  const uintptr_t vb = (uintptr_t)(2 * V);
+  auto st_ok = [&](int64_t n, int64_t s) { return n <= 1 || ((uintptr_t)s * 2u) % vb == 0; };
+  bool vec = true;
+  for (const void* p : {q, k, (const void*)q_out, (const void*)k_out, wq, bq, wk, bk})
+    if (p && !aligned(p, vb)) vec = false;
+  vec = vec && st_ok(B, sq_b) && st_ok(S, sq_s) && st_ok(H, sq_h) && st_ok(B, sk_b) &&
+        st_ok(S, sk_s) && st_ok(H, sk_h);
+  // one row stride per side: head rows of q (and of k) evenly spaced, so
+  // row rr of the [B*S*H, Dh] view starts at rr * stride
+  auto row_stride = [&](int64_t sb, int64_t ss, int64_t sh, int64_t* r) {
+    *r = H > 1 ? sh : (S > 1 ? ss : sb);
+    return (S == 1 || ss == H * *r) && (B == 1 || sb == S * H * *r);
+  };
+  int64_t rq = 0, rk = 0;
+  const bool uniform = row_stride(sq_b, sq_s, sq_h, &rq) && row_stride(sk_b, sk_s, sk_h, &rk);
+  if (uniform) {
+    a.side[0].s_h = rq;
+    a.side[1].s_h = rk;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const bool gather = !vec;
+  const int64_t nv = (Dh / V + kGroup - 1) / kGroup;
+  if (V == 8) {
+    if (nv <= 1) return pick_uniform<8, 1>(a, uniform, affine, gather, st);
+    return pick_uniform<8, 2>(a, uniform, affine, gather, st);
+  }
+  if (nv <= 1) return pick_uniform<4, 1>(a, uniform, affine, gather, st);
+  if (nv <= 2) return pick_uniform<4, 2>(a, uniform, affine, gather, st);
+  return pick_uniform<4, 4>(a, uniform, affine, gather, st);
+}

@@ -1,0 +1,178 @@
+// residual_gate_add: out = bf16(residual + bf16(gate * update)) on gfx950.
+//
+// Operation: "Fused Kernels" page, table "adaLN modulation and gating"
+// (residual_gate_add replaces residual + gate * update, bit-exact); prhub
+// report on sglang PR #34008, 实现拆解 §2-3 (GLM-Image ff-gate sites).  The
+// eager chain is two bf16 ops (a multiply, then an add), so the product is
+// rounded to bf16 before the add.
+//
+// Design: pure streaming (2 reads + 1 write per element).  One wavefront per
+// row; each lane issues U independent 16-byte loads of residual and update
+// before it computes, so a wave keeps 2*U*1 KiB in flight.  The per-sample
+// gate row is shared by every row of a sample and stays in cache.
+#include "device_common.hpp"
+#include "host_common.hpp"
+
+namespace adaln {
+namespace {
+
+struct RgaArgs {
+  const uint16_t* res;
+  int64_t sr_b, sr_s;
+  const uint16_t* gate;
+  int64_t sg_b;
+  const uint16_t* upd;
+  int64_t su_b, su_s;
+  int64_t S, D, R;
+  uint16_t* out;
+};
+
+template <int V>
+__device__ __forceinline__ Vec<V> gate_add_vec(const Vec<V>& rv, const Vec<V>& gv, const Vec<V>& uv) {
+  Vec<V> o;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    float t0 = lo_f32(gv.w[i]) * lo_f32(uv.w[i]);
+    float t1 = hi_f32(gv.w[i]) * hi_f32(uv.w[i]);
+    round_pair(t0, t1);  // bf16(gate * update)
+    o.w[i] = pack_bf16(lo_f32(rv.w[i]) + t0, hi_f32(rv.w[i]) + t1);  // bf16(residual + t)
+  }
+  return o;
+}
+
+constexpr int kRowsPerBlock = 4;
+constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
+
+template <int V, int U>
+__global__ __launch_bounds__(256) void rga_rows_vec(RgaArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nvec = a.D / V;
+  for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
+       r += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int64_t b = r / a.S;
+    const int64_t s = r - b * a.S;
+    const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
+    const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
+    const uint16_t* gr = a.gate + b * a.sg_b;
+    uint16_t* orow = a.out + r * a.D;
+    for (int64_t base = lane; base < nvec; base += (int64_t)U * kWave) {
+      Vec<V> rv[U], uv[U], gv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = base + (int64_t)u * kWave;
+        if (v < nvec) {
+          rv[u] = load_vec<V>(rr + v * V);
+          uv[u] = load_vec<V>(ur + v * V);
+          gv[u] = load_vec<V>(gr + v * V);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = base + (int64_t)u * kWave;
+        if (v < nvec) store_vec<V>(orow + v * V, gate_add_vec<V>(rv[u], gv[u], uv[u]));
+      }
+    }
+  }
+}
+
+// any D, any 2-byte alignment: one element per lane step
+__global__ __launch_bounds__(256) void rga_rows_scalar(RgaArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
+       r += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int64_t b = r / a.S;
+    const int64_t s = r - b * a.S;
+    const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
+    const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
+    const uint16_t* gr = a.gate + b * a.sg_b;
+    uint16_t* orow = a.out + r * a.D;
+    for (int64_t j = lane; j < a.D; j += kWave) {
+      float t = u16_f32(gr[j]) * u16_f32(ur[j]);
+      float tr = u16_f32(to_bf16(t));
+      orow[j] = to_bf16(u16_f32(rr[j]) + tr);
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t R) {
+  int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+  return (unsigned)std::min(blocks, kMaxBlocks);
+}
+
+}  // namespace
+
+static int rga_check_shape(int64_t B, int64_t S, int64_t D, int64_t sr_b, int64_t sr_s,
+                           int64_t sg_b, int64_t su_b, int64_t su_s, int dtype) {
+  if (dtype != ADALN_BF16) return ADALN_ERR_DTYPE;
+  if (B < 0 || S < 0 || D < 0) return ADALN_ERR_SHAPE;
+  if (sr_b < 0 || sr_s < 0 || sg_b < 0 || su_b < 0 || su_s < 0) return ADALN_ERR_STRIDE;
+  int64_t R, RD;
+  if (!mul_ok(B, S, &R) || !mul_ok(R, D, &RD)) return ADALN_ERR_TOO_LARGE;
+  if (!extent_ok({{B, sr_b}, {S, sr_s}, {D, 1}}) || !extent_ok({{B, su_b}, {S, su_s}, {D, 1}}) ||
+      !extent_ok({{B, sg_b}, {D, 1}}))
+    return ADALN_ERR_TOO_LARGE;
+  return ADALN_OK;
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int residual_gate_add_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b,
+                                         int64_t sr_s, int64_t sg_b, int64_t su_b, int64_t su_s,
+                                         int dtype) {
+  return rga_check_shape(B, S, D, sr_b, sr_s, sg_b, su_b, su_s, dtype) == ADALN_OK;
+}
+
+extern "C" int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_s, const void* gate,
+                                 int64_t sg_b, const void* update, int64_t su_b, int64_t su_s,
+                                 int64_t B, int64_t S, int64_t D, int dtype, void* out,
+                                 void* stream) {
+  int rc = rga_check_shape(B, S, D, sr_b, sr_s, sg_b, su_b, su_s, dtype);
+  if (rc != ADALN_OK) return rc;
+  const int64_t R = B * S;
+  if (R == 0 || D == 0) return ADALN_OK;
+  if (!residual || !gate || !update || !out) return ADALN_ERR_NULL;
+  if (!aligned(residual, 2) || !aligned(gate, 2) || !aligned(update, 2) || !aligned(out, 2))
+    return ADALN_ERR_ALIGN;
+
+  const Span so = span_of(out, {{R * D, 1}});
+  const Span sres = span_of(residual, {{B, sr_b}, {S, sr_s}, {D, 1}});
+  const Span supd = span_of(update, {{B, su_b}, {S, su_s}, {D, 1}});
+  const Span sg = span_of(gate, {{B, sg_b}, {D, 1}});
+  auto contig = [&](int64_t sb, int64_t ss) {
+    return (S == 1 || ss == D) && (B == 1 || sb == S * D);
+  };
+  if (overlaps(so, sres) && !(residual == out && contig(sr_b, sr_s))) return ADALN_ERR_ALIAS;
+  if (overlaps(so, supd) && !(update == out && contig(su_b, su_s))) return ADALN_ERR_ALIAS;
+  if (overlaps(so, sg)) return ADALN_ERR_ALIAS;
+
+  RgaArgs a;
+  a.res = (const uint16_t*)residual;
+  a.sr_b = sr_b;
+  a.sr_s = sr_s;
+  a.gate = (const uint16_t*)gate;
+  a.sg_b = sg_b;
+  a.upd = (const uint16_t*)update;
+  a.su_b = su_b;
+  a.su_s = su_s;
+  a.S = S;
+  a.D = D;
+  a.R = R;
+  a.out = (uint16_t*)out;
+
+  hipStream_t st = (hipStream_t)stream;
+  auto vec_ok = [&](uintptr_t vb) {
+    auto so_ = [&](int64_t n, int64_t s) { return n <= 1 || ((uintptr_t)s * 2u) % vb == 0; };
+    return D % (int64_t)(vb / 2) == 0 && aligned(residual, vb) && aligned(update, vb) &&
+           aligned(gate, vb) && aligned(out, vb) && so_(B, sr_b) && so_(S, sr_s) && so_(B, su_b) &&
+           so_(S, su_s) && so_(B, sg_b);
+  };
+  if (vec_ok(16))
+    hipLaunchKernelGGL((rga_rows_vec<8, 8>), dim3(grid_for(R)), dim3(256), 0, st, a);
+  else if (vec_ok(8))
+    hipLaunchKernelGGL((rga_rows_vec<4, 8>), dim3(grid_for(R)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(rga_rows_scalar, dim3(grid_for(R)), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}

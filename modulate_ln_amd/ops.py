@@ -1,0 +1,182 @@
+"""Torch-facing binding of the adaLN C ABI: argument marshalling only.
+
+Every function here checks dtypes/devices, allocates outputs with torch when
+the caller passes none, reads pointers and strides, and calls the C entry
+point of the same name on the current HIP stream.  All arithmetic runs in
+the library's kernels.  With ``prepare=True`` a function returns the
+marshalled call (a ``Prepared``) instead of issuing it.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _native as N
+
+
+class Prepared:
+    """A marshalled call: the C function and its argument tuple, ready to issue.
+
+    Calling it enqueues the kernel(s) again with the same pointers, sizes and
+    stream (for tight loops where per-call marshalling would dominate)."""
+
+    __slots__ = ("name", "fn", "args", "result")
+
+    def __init__(self, name, fn, args, result):
+        self.name, self.fn, self.args, self.result = name, fn, args, result
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != N.OK:
+            raise N.AdalnError(self.name, rc)
+        return self.result
+
+
+def _stream_handle(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device, got %s" % (name, t.device))
+
+
+def _rows_view(t: torch.Tensor, B: int, D: int, name: str):
+    """[B,D] or [B,1,D] adaLN rows -> (tensor, batch stride); element stride must be 1."""
+    if t.dim() == 3:
+        if t.shape[1] != 1:
+            raise ValueError("%s must be [B,1,D] or [B,D], got %s" % (name, tuple(t.shape)))
+        t = t[:, 0]
+    if t.dim() != 2 or t.shape[1] != D or t.shape[0] not in (B, 1):
+        raise ValueError("%s must be [B,D] with B=%d D=%d, got %s" % (name, B, D, tuple(t.shape)))
+    if D > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit stride along the hidden dim" % name)
+    sb = t.stride(0) if t.shape[0] == B else 0  # one row broadcast to every sample
+    return t, sb
+
+
+def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
+                out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
+                rstd_out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """LN(x) * (1 + scale) + shift with every eager bf16 rounding (x: [B,S,D], any strides)."""
+    _require(x, "x")
+    _require(scale, "scale")
+    _require(shift, "shift")
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D], got %s" % (tuple(x.shape),))
+    B, S, D = x.shape
+    scale, ssc = _rows_view(scale, B, D, "scale")
+    shift, ssh = _rows_view(shift, B, D, "shift")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, "out")
+        if tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B,S,D] tensor")
+    for name, t in (("mean_out", mean_out), ("rstd_out", rstd_out)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * S or not t.is_contiguous()
+                              or t.device != x.device):
+            raise ValueError("%s must be a contiguous float32 tensor of B*S elements on x's device" % name)
+    st = _stream_handle(x, stream)
+    call = Prepared("ln_modulate", N.lib().ln_modulate, (
+        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
+        mean_out.data_ptr() if mean_out is not None else None,
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+    return call if prepare else call()
+
+
+def residual_gate_add(residual: torch.Tensor, gate: torch.Tensor, update: torch.Tensor, *,
+                      out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """residual + gate * update with the eager roundings (residual/update [B,S,D], gate [B,D])."""
+    _require(residual, "residual")
+    _require(gate, "gate")
+    _require(update, "update")
+    if residual.dim() != 3 or update.shape != residual.shape:
+        raise ValueError("residual and update must both be [B,S,D]")
+    B, S, D = residual.shape
+    gate, sg = _rows_view(gate, B, D, "gate")
+    for name, t in (("residual", residual), ("update", update)):
+        if D > 1 and t.stride(2) != 1:
+            raise ValueError("%s must have unit stride along the hidden dim" % name)
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=residual.device)
+    else:
+        _require(out, "out")
+        if tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B,S,D] tensor")
+    st = _stream_handle(residual, stream)
+    call = Prepared("residual_gate_add", N.lib().residual_gate_add, (
+        residual.data_ptr(), residual.stride(0), residual.stride(1), gate.data_ptr(), sg,
+        update.data_ptr(), update.stride(0), update.stride(1), B, S, D, N.BF16, out.data_ptr(), st), out)
+    return call if prepare else call()
+
+
+def qk_head_layernorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None = None,
+                      bq: torch.Tensor | None = None, wk: torch.Tensor | None = None,
+                      bk: torch.Tensor | None = None, eps: float = 1e-6, *,
+                      q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None, stream=None,
+                      prepare: bool = False):
+    """Per-head affine LayerNorm of q and k ([B,S,H,Dh] each) in one launch."""
+    _require(q, "q")
+    _require(k, "k")
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must both be [B,S,H,Dh]")
+    B, S, H, Dh = q.shape
+    for name, t in (("q", q), ("k", k)):
+        if Dh > 1 and t.stride(3) != 1:
+            raise ValueError("%s must have unit stride along head_dim" % name)
+    ws = (wq, bq, wk, bk)
+    if any(w is None for w in ws) and not all(w is None for w in ws):
+        raise ValueError("wq, bq, wk, bk go together (all or none)")
+    for name, w in zip(("wq", "bq", "wk", "bk"), ws):
+        if w is not None:
+            _require(w, name)
+            if w.numel() != Dh or not w.is_contiguous():
+                raise ValueError("%s must be a contiguous [Dh] tensor" % name)
+    if q_out is None:
+        q_out = torch.empty((B, S, H, Dh), dtype=torch.bfloat16, device=q.device)
+    if k_out is None:
+        k_out = torch.empty((B, S, H, Dh), dtype=torch.bfloat16, device=q.device)
+    for name, t in (("q_out", q_out), ("k_out", k_out)):
+        _require(t, name)
+        if tuple(t.shape) != (B, S, H, Dh) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous [B,S,H,Dh] tensor" % name)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    st = _stream_handle(q, stream)
+    call = Prepared("qk_head_layernorm", N.lib().qk_head_layernorm, (
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        B, S, H, Dh, ptr(wq), ptr(bq), ptr(wk), ptr(bk), float(eps), N.BF16,
+        q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out))
+    return call if prepare else call()
+
+
+def bias_gelu_tanh(x: torch.Tensor, bias: torch.Tensor, *, out: torch.Tensor | None = None,
+                   stream=None, prepare: bool = False):
+    """bf16(gelu_tanh(bf16(x + bias))) for x [rows, width] (unit stride along width)."""
+    _require(x, "x")
+    _require(bias, "bias")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, width]")
+    rows, width = x.shape
+    if bias.numel() != width or not bias.is_contiguous():
+        raise ValueError("bias must be a contiguous [width] tensor")
+    if width > 1 and x.stride(1) != 1:
+        raise ValueError("x must have unit stride along width")
+    if out is None:
+        out = torch.empty((rows, width), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, "out")
+        if tuple(out.shape) != (rows, width) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [rows, width] tensor")
+    st = _stream_handle(x, stream)
+    call = Prepared("bias_gelu_tanh", N.lib().bias_gelu_tanh,
+                    (x.data_ptr(), rows, width, x.stride(0), bias.data_ptr(), N.BF16, out.data_ptr(), st), out)
+    return call if prepare else call()

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented codes BEFORE
+any HIP call (so these run without a GPU).  No compute call is made here:
+every entry-point call below is one the validator rejects.
+"""
+
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from modulate_ln_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adaln.h")
+
+# fake, never dereferenced device addresses (256-byte aligned, far apart)
+P0, P1, P2, P3, P4 = (0x10000000 * (i + 1) for i in range(5))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return N.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_exactly_the_exports():
+    assert declared_functions() == set(N.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], check=True, stdout=subprocess.PIPE,
+                         text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.adaln_abi_version() == N.ABI_VERSION == 1
+    codes = [N.OK, N.ERR_NULL, N.ERR_SHAPE, N.ERR_DTYPE, N.ERR_ALIGN, N.ERR_ALIAS, N.ERR_TOO_LARGE,
+             N.ERR_STRIDE, N.ERR_HIP, N.ERR_ARG]
+    names = [N.status_str(c) for c in codes]
+    assert len(set(names)) == len(codes)
+    assert N.status_str(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("D,V", [(4, 4), (8, 8), (12, 4), (512, 8), (2240, 8), (4100, 4), (65536, 8)])
+def test_order_for(D, V):
+    assert N.order_for(N.OP_LN_MODULATE, D) == (V, 64)
+    assert N.order_for(N.OP_QK_HEAD_LAYERNORM, D) == (V, 16)
+
+
+@pytest.mark.parametrize("D", [0, -4, 6, 2242])
+def test_order_for_rejects(D):
+    with pytest.raises(N.AdalnError):
+        N.order_for(N.OP_LN_MODULATE, D)
+    with pytest.raises(N.AdalnError):
+        N.order_for(7, 512)
+
+
+def test_ln_modulate_can_use(L):
+    ok = lambda *a: L.ln_modulate_can_use(*a, N.BF16)  # noqa: E731
+    assert ok(1, 4096, 4096, 4096 * 4096, 4096, 1, 4096, 4096)
+    assert ok(2, 1024, 2240, 2240 * 1024, 1, 1024, 13440, 13440)  # transposed view
+    assert ok(0, 0, 4, 0, 0, 1, 0, 0)  # empty
+    assert ok(1, 1, 65536, 0, 65536, 1, 0, 0)
+    assert not ok(1, 1, 65540, 0, 65540, 1, 0, 0)  # too large
+    assert not ok(1, 1, 6, 0, 6, 1, 0, 0)  # D % 4
+    assert not ok(1, 1, 0, 0, 0, 1, 0, 0)
+    assert not ok(-1, 1, 8, 0, 8, 1, 0, 0)
+    assert not ok(1, 2, 8, 16, -8, 1, 0, 0)
+    assert not L.ln_modulate_can_use(1, 1, 8, 8, 8, 1, 8, 8, 2)  # dtype
+
+
+def test_other_can_use(L):
+    assert L.residual_gate_add_can_use(1, 4096, 4096, 4096 * 4096, 4096, 4096, 4096 * 4096, 4096, N.BF16)
+    assert L.residual_gate_add_can_use(2, 3, 5, 15, 5, 5, 15, 5, N.BF16)  # any D
+    assert not L.residual_gate_add_can_use(2, 3, 5, 15, -5, 5, 15, 5, N.BF16)
+    assert not L.residual_gate_add_can_use(2, 3, 5, 15, 5, 5, 15, 5, 0)
+    assert L.qk_head_layernorm_can_use(1, 4360, 32, 128, 4360 * 4096, 4096, 128, 4360 * 4096, 4096, 128, N.BF16)
+    assert L.qk_head_layernorm_can_use(1, 2, 3, 256, 1536, 768, 256, 1536, 768, 256, N.BF16)
+    assert not L.qk_head_layernorm_can_use(1, 2, 3, 260, 1560, 780, 260, 1560, 780, 260, N.BF16)
+    assert not L.qk_head_layernorm_can_use(1, 2, 3, 126, 756, 378, 126, 756, 378, 126, N.BF16)
+    assert L.bias_gelu_tanh_can_use(16384, 12288, 12288, N.BF16)
+    assert L.bias_gelu_tanh_can_use(3, 7, 7, N.BF16)
+    assert not L.bias_gelu_tanh_can_use(3, 7, -1, N.BF16)
+    assert not L.bias_gelu_tanh_can_use(3, 7, 7, 5)
+
+
+def lnm(L, x=P0, B=1, S=4, D=8, sx=None, scale=P1, ssc=8, shift=P2, ssh=8, eps=1e-6, dtype=N.BF16, out=P3,
+        mean=None, rstd=None):
+    sx_b, sx_s, sx_d = sx if sx is not None else (S * D, D, 1)
+    return L.ln_modulate(x, B, S, D, sx_b, sx_s, sx_d, scale, ssc, shift, ssh, eps, dtype, out, mean, rstd, None)
+
+
+def test_ln_modulate_rejections(L):
+    assert lnm(L, dtype=2) == N.ERR_DTYPE
+    assert lnm(L, D=6) == N.ERR_SHAPE
+    assert lnm(L, D=0) == N.ERR_SHAPE
+    assert lnm(L, B=-1) == N.ERR_SHAPE
+    assert lnm(L, D=65540) == N.ERR_TOO_LARGE
+    assert lnm(L, sx=(32, -8, 1)) == N.ERR_STRIDE
+    assert lnm(L, eps=float("nan")) == N.ERR_ARG
+    assert lnm(L, eps=-1.0) == N.ERR_ARG
+    assert lnm(L, x=None) == N.ERR_NULL
+    assert lnm(L, scale=None) == N.ERR_NULL
+    assert lnm(L, out=None) == N.ERR_NULL
+    assert lnm(L, x=P0 + 1) == N.ERR_ALIGN
+    assert lnm(L, mean=P4 + 2) == N.ERR_ALIGN
+    # out overlapping x other than the exact contiguous alias
+    assert lnm(L, out=P0 + 16) == N.ERR_ALIAS
+    assert lnm(L, out=P0, sx=(64, 16, 1)) == N.ERR_ALIAS  # same base, x not contiguous
+    assert lnm(L, out=P1) == N.ERR_ALIAS  # out over scale
+    assert lnm(L, out=P2 - 16) == N.ERR_ALIAS  # out tail over shift
+    assert lnm(L, mean=P3 + 8) == N.ERR_ALIAS  # stats over out
+    assert lnm(L, mean=P4, rstd=P4 + 8) == N.ERR_ALIAS  # mean and rstd overlap
+    # an empty problem is a successful no-op even with NULL pointers
+    assert lnm(L, x=None, scale=None, shift=None, out=None, B=0) == N.OK
+    assert lnm(L, x=None, scale=None, shift=None, out=None, S=0) == N.OK
+
+
+def test_residual_gate_add_rejections(L):
+    def rga(res=P0, gate=P1, upd=P2, out=P3, B=2, S=3, D=8, dtype=N.BF16, sr=(24, 8), su=(24, 8), sg=8):
+        return L.residual_gate_add(res, sr[0], sr[1], gate, sg, upd, su[0], su[1], B, S, D, dtype, out, None)
+
+    assert rga(dtype=0) == N.ERR_DTYPE
+    assert rga(D=-1) == N.ERR_SHAPE
+    assert rga(sr=(24, -8)) == N.ERR_STRIDE
+    assert rga(res=None) == N.ERR_NULL
+    assert rga(gate=P1 + 1) == N.ERR_ALIGN
+    assert rga(out=P0 + 2) == N.ERR_ALIAS
+    assert rga(out=P2 + 2) == N.ERR_ALIAS
+    assert rga(out=P1) == N.ERR_ALIAS
+    assert rga(out=P0, sr=(48, 16)) == N.ERR_ALIAS  # exact base but residual not contiguous
+    assert rga(res=None, gate=None, upd=None, out=None, B=0) == N.OK
+    assert rga(res=None, gate=None, upd=None, out=None, D=0) == N.OK
+
+
+def test_qk_rejections(L):
+    def qk(q=P0, k=P1, wq=P2, bq=P2 + 512, wk=P2 + 1024, bk=P2 + 1536, qo=P3, ko=P4, B=1, S=2, H=3, Dh=128,
+           eps=1e-6, dtype=N.BF16):
+        sb, ss, sh = S * H * Dh, H * Dh, Dh
+        return L.qk_head_layernorm(q, sb, ss, sh, k, sb, ss, sh, B, S, H, Dh, wq, bq, wk, bk, eps, dtype, qo, ko,
+                                   None)
+
+    assert qk(dtype=3) == N.ERR_DTYPE
+    assert qk(Dh=126) == N.ERR_SHAPE
+    assert qk(Dh=260) == N.ERR_TOO_LARGE
+    assert qk(eps=float("inf")) == N.ERR_ARG
+    assert qk(q=None) == N.ERR_NULL
+    assert qk(bq=None) == N.ERR_NULL  # w without b
+    assert qk(wk=None, bk=None) == N.ERR_NULL  # affine on one side only
+    assert qk(ko=P4 + 1) == N.ERR_ALIGN
+    assert qk(qo=P1) == N.ERR_ALIAS  # q_out over k
+    assert qk(ko=P3 + 64) == N.ERR_ALIAS  # q_out and k_out overlap
+    assert qk(qo=P2 - 64) == N.ERR_ALIAS  # q_out over the weights
+    assert qk(q=None, k=None, qo=None, ko=None, S=0) == N.OK
+
+
+def test_bias_gelu_rejections(L):
+    def bg(x=P0, rows=4, width=64, sx=64, bias=P1, dtype=N.BF16, out=P2):
+        return L.bias_gelu_tanh(x, rows, width, sx, bias, dtype, out, None)
+
+    assert bg(dtype=0) == N.ERR_DTYPE
+    assert bg(rows=-1) == N.ERR_SHAPE
+    assert bg(sx=-64) == N.ERR_STRIDE
+    assert bg(bias=None) == N.ERR_NULL
+    assert bg(out=P2 + 1) == N.ERR_ALIGN
+    assert bg(out=P0 + 2) == N.ERR_ALIAS
+    assert bg(out=P1 - 2) == N.ERR_ALIAS
+    assert bg(out=P0, sx=128) == N.ERR_ALIAS
+    assert bg(x=None, bias=None, out=None, rows=0) == N.OK
