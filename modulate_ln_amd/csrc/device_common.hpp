@@ -144,6 +144,55 @@ __device__ __forceinline__ void merge_lanes(float& m, float& m2, float& n, int l
   }
 }
 
+// Value held by lane (lane + OFF) of the same wave, for the merge tree that
+// collects the row's state in lane 0.  Lanes whose partner falls outside
+// their DPP row (OFF <= 8) or outside the wave receive unspecified values;
+// the tree never reads them for a lane it keeps.
+template <int OFF>
+__device__ __forceinline__ float lane_down(float v) {
+  int i = __builtin_bit_cast(int, v);
+  if constexpr (OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8) {
+    i = __builtin_amdgcn_update_dpp(0, i, 0x100 + OFF, 0xF, 0xF, false);  // row_shl:OFF
+  } else if constexpr (OFF == 16) {
+    auto p = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+    i = (int)p[1];  // even rows receive the odd row above them
+  } else {
+    static_assert(OFF == 32, "lane_down: offset must be 1, 2, 4, 8, 16 or 32");
+    auto p = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+    i = (int)p[1];  // the lower half receives the upper half
+  }
+  return __builtin_bit_cast(float, i);
+}
+
+// One level of the merge tree toward lane 0: lane l merges lane l + OFF into
+// its own state (lower lane first).  After levels 1, 2, ..., 32 lane 0 holds
+// the state of the whole wave -- the same pairwise tree as merge_lanes.
+template <int OFF>
+__device__ __forceinline__ void merge_down(float& m, float& m2, float& n) {
+  const float mb = lane_down<OFF>(m);
+  const float m2b = lane_down<OFF>(m2);
+  const float nb = lane_down<OFF>(n);
+  welford_merge(m, m2, n, mb, m2b, nb);
+}
+
+// The same level when every lane of the wave holds `cnt` elements: the
+// merged halves are equal, so nb/n = 0.5 exactly and the update needs no
+// division (bit-identical to welford_merge with those counts).
+template <int OFF>
+__device__ __forceinline__ void merge_down_equal(float& m, float& m2, float cnt) {
+  const float mb = lane_down<OFF>(m);
+  const float m2b = lane_down<OFF>(m2);
+  const float na = cnt * (float)OFF;  // lower half's count (exact)
+  const float delta = mb - m;
+  const float mm = __builtin_fmaf(delta, 0.5f, m);
+  m2 = (m2 + m2b) + (delta * delta) * (na * 0.5f);
+  m = mm;
+}
+
+__device__ __forceinline__ float bcast_lane0(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 // var = m2/D, rstd = 1/sqrt(var + eps): IEEE division and square root.
 __device__ __forceinline__ float finalize_rstd(float m2, float D, float eps) {
   float var = m2 / D;
@@ -184,6 +233,38 @@ __device__ __forceinline__ void store_vec(uint16_t* p, const Vec<V>& v) {
     *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
   } else {
     *reinterpret_cast<uint2*>(p) = make_uint2(v.w[0], v.w[1]);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) vector load/store: data touched once per call.
+template <int V>
+__device__ __forceinline__ Vec<V> load_vec_nt(const uint16_t* p) {
+  Vec<V> r;
+  if constexpr (V == 8) {
+    u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    r.w[0] = t[0];
+    r.w[1] = t[1];
+    r.w[2] = t[2];
+    r.w[3] = t[3];
+  } else {
+    u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    r.w[0] = t[0];
+    r.w[1] = t[1];
+  }
+  return r;
+}
+
+template <int V>
+__device__ __forceinline__ void store_vec_nt(uint16_t* p, const Vec<V>& v) {
+  if constexpr (V == 8) {
+    u32x4 t = {v.w[0], v.w[1], v.w[2], v.w[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+  } else {
+    u32x2 t = {v.w[0], v.w[1]};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
   }
 }
 

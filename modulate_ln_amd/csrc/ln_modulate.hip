@@ -20,6 +20,7 @@
 // Rows whose storage is not vector-aligned or not contiguous take the same
 // code with element-wise gathers; the order of arithmetic is identical, so
 // the result depends only on the logical values.
+#include <atomic>
 #include <utility>
 
 #include "device_common.hpp"
@@ -100,16 +101,17 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
     const int64_t s = r - b * a.S;
     const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
 
+    // every lane loads every step (past the tail it re-reads the row's last
+    // vector): unguarded loads issue back to back instead of one at a time
     Vec<V> buf[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t v = (int64_t)k * kWave + lane;
-      if (v < nvec) {
-        if constexpr (GATHER)
-          buf[k] = gather_vec<V>(xr + v * V * a.sx_d, a.sx_d);
-        else
-          buf[k] = load_vec<V>(xr + v * V);
-      }
+      const int64_t vc = v < nvec ? v : nvec - 1;
+      if constexpr (GATHER)
+        buf[k] = gather_vec<V>(xr + vc * V * a.sx_d, a.sx_d);
+      else
+        buf[k] = load_vec<V>(xr + vc * V);
     }
 
     float mean = 0.0f, m2 = 0.0f;
@@ -125,20 +127,248 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
     const uint16_t* sc = a.scale + b * a.ssc_b;
     const uint16_t* sh = a.shift + b * a.ssh_b;
     uint16_t* orow = a.out + r * a.D;
+    Vec<V> sv[NV], hv[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t v = (int64_t)k * kWave + lane;
+      const int64_t vc = v < nvec ? v : nvec - 1;
+      sv[k] = GATHER ? gather_vec<V>(sc + vc * V, 1) : load_vec<V>(sc + vc * V);
+      hv[k] = GATHER ? gather_vec<V>(sh + vc * V, 1) : load_vec<V>(sh + vc * V);
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t v = (int64_t)k * kWave + lane;
       if (v < nvec) {
-        if constexpr (GATHER) {
-          Vec<V> sv = gather_vec<V>(sc + v * V, 1);
-          Vec<V> hv = gather_vec<V>(sh + v * V, 1);
-          scatter_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv, hv, mean, rstd));
-        } else {
-          Vec<V> sv = load_vec<V>(sc + v * V);
-          Vec<V> hv = load_vec<V>(sh + v * V);
-          store_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv, hv, mean, rstd));
-        }
+        if constexpr (GATHER)
+          scatter_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv[k], hv[k], mean, rstd));
+        else
+          store_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv[k], hv[k], mean, rstd));
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: contiguous, vector-aligned rows with D <= 8192.
+//
+// A block serves one batch sample b.  It first turns that sample's adaLN
+// rows into two fp32 tables in LDS -- bf16(1 + scale) and shift -- laid out
+// [quarter q][vector v][4] so a lane's 16-byte LDS reads are contiguous
+// across the wave.  Each wave then streams rows s = j*4 + wave, += 4*bpb:
+// the next row's loads are in flight while the current row is reduced,
+// normalized, modulated and stored (non-temporal: every byte is touched
+// once).  The first row's loads are issued before the table is built, so
+// the table's latency hides under them.  UNIF (D % (64*V) == 0): every lane
+// holds the same count and the merge tree needs no division.
+// ---------------------------------------------------------------------------
+template <int V, int K, int... E>
+__device__ __forceinline__ void push_f32(const float* xk, float& mean, float& m2,
+                                         std::integer_sequence<int, E...>) {
+  (welford_push<K * V + E + 1>(mean, m2, xk[E]), ...);
+}
+
+template <int V, bool UNIF, int... K>
+__device__ __forceinline__ void welford_f32(const float (*xf)[V], int nvec, int lane, float& mean,
+                                            float& m2, std::integer_sequence<int, K...>) {
+  (
+      [&] {
+        if (UNIF || K * kWave + lane < nvec)
+          push_f32<V, K>(xf[K], mean, m2, std::make_integer_sequence<int, V>{});
+      }(),
+      ...);
+}
+
+// Launch shape of the fast path, measured on MI355X (all variants give the
+// same bits).  Rows of 7-8 vectors per lane prefetch the next row into a
+// second buffer and re-widen x from bf16 when normalizing, to stay at three
+// waves per SIMD; shorter rows keep one buffer and an fp32 copy of x;
+// longer rows (up to 16 vectors per lane, 64 KiB of tables) keep one
+// buffer and re-widen.  Grid: blocks per compute unit in total.
+template <int NV>
+struct TabShape {
+  static constexpr bool kPrefetch = NV == 7 || NV == 8;
+  static constexpr bool kXf32 = NV <= 6;
+  static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (NV <= 8 ? 3 : 2);
+};
+
+// bf16 -> fp32 widening the compiler may not merge with an earlier one:
+// re-widening a row from its packed form costs one VALU op per element but
+// spares the VGPRs an fp32 copy of the row would hold.
+__device__ __forceinline__ float lo_f32_again(uint32_t w) {
+  uint32_t r;
+  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
+  return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float hi_f32_again(uint32_t w) {
+  uint32_t r;
+  asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
+  return __builtin_bit_cast(float, r);
+}
+
+template <int V, int NV, bool UNIF>
+__global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
+  constexpr bool kPrefetch = TabShape<NV>::kPrefetch;
+  constexpr bool kXf32 = TabShape<NV>::kXf32;
+  extern __shared__ float4 tab[];  // [2][V/4][nvec] float4: bf16(1+scale), then shift
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int D = (int)a.D;
+  const int nvec = D / V;
+  const int S = (int)a.S;
+  const int b = blockIdx.x / bpb;
+  const int j = blockIdx.x - b * bpb;
+  const int row_step = 4 * bpb;
+  const int shift_off = (V / 4) * nvec;  // float4 index of the shift table
+  int s = 4 * j + wave;
+
+  const uint16_t* xb = a.x + (int64_t)b * a.sx_b;
+  auto load_row = [&](Vec<V>* buf, int ss) {
+    const uint16_t* xr = xb + (int64_t)ss * a.sx_s;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * kWave + lane;
+      const int vc = (UNIF || v < nvec) ? v : nvec - 1;
+      buf[k] = load_vec_nt<V>(xr + vc * V);
+    }
+  };
+
+  Vec<V> bufA[NV];
+  Vec<V> bufB[kPrefetch ? NV : 1];
+  if (s < S) load_row(bufA, s);
+
+  {
+    const uint16_t* sc = a.scale + (int64_t)b * a.ssc_b;
+    const uint16_t* sh = a.shift + (int64_t)b * a.ssh_b;
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+      const Vec<V> sv = load_vec<V>(sc + v * V);
+      const Vec<V> hv = load_vec<V>(sh + v * V);
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
+        float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
+        round_pair(o0, o1);  // bf16(1 + scale)
+        round_pair(o2, o3);
+        tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
+        tab[shift_off + q * nvec + v] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
+                                                    lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
+      }
+    }
+  }
+  __syncthreads();
+  if (s >= S) return;
+
+  const float Df = (float)D;
+  const int nv_lane = nvec / kWave + (lane < nvec % kWave ? 1 : 0);
+
+  auto process = [&](const Vec<V>* buf, int ss) {
+    // kXf32: widen the row once and keep it in fp32 for both passes;
+    // otherwise widen it for the reduction and again (opaque to the
+    // compiler, so no fp32 copy stays live) when normalizing
+    float xf[NV][V];
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        xf[k][2 * i] = lo_f32(buf[k].w[i]);
+        xf[k][2 * i + 1] = hi_f32(buf[k].w[i]);
+      }
+    auto xval = [&](int k, int e) -> float {
+      if constexpr (kXf32) return xf[k][e];
+      return (e & 1) ? hi_f32_again(buf[k].w[e / 2]) : lo_f32_again(buf[k].w[e / 2]);
+    };
+    float mean = 0.0f, m2 = 0.0f;
+    welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
+    if constexpr (UNIF) {
+      const float c = (float)(NV * V);
+      merge_down_equal<1>(mean, m2, c);
+      merge_down_equal<2>(mean, m2, c);
+      merge_down_equal<4>(mean, m2, c);
+      merge_down_equal<8>(mean, m2, c);
+      merge_down_equal<16>(mean, m2, c);
+      merge_down_equal<32>(mean, m2, c);
+    } else {
+      float n = (float)(nv_lane * V);
+      merge_down<1>(mean, m2, n);
+      merge_down<2>(mean, m2, n);
+      merge_down<4>(mean, m2, n);
+      merge_down<8>(mean, m2, n);
+      merge_down<16>(mean, m2, n);
+      merge_down<32>(mean, m2, n);
+    }
+    mean = bcast_lane0(mean);
+    m2 = bcast_lane0(m2);
+    const float rstd = finalize_rstd(m2, Df, a.eps);
+    const int64_t r = (int64_t)b * S + ss;
+    if (lane == 0) {
+      if (a.mean_out) a.mean_out[r] = mean;
+      if (a.rstd_out) a.rstd_out[r] = rstd;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint16_t* orow = a.out + r * D;
+    // table values for step k are read one step ahead of their use
+    float4 ot[V / 4], ht[V / 4];
+    auto read_tab = [&](int k) {
+      const int v = k * kWave + lane;
+      const int vc = (UNIF || v < nvec) ? v : nvec - 1;
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        ot[q] = tab[q * nvec + vc];
+        ht[q] = tab[shift_off + q * nvec + vc];
+      }
+    };
+    read_tab(0);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float4 oc[V / 4], hc[V / 4];
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        oc[q] = ot[q];
+        hc[q] = ht[q];
+      }
+      if (k + 1 < NV) read_tab(k + 1);
+      const int v = k * kWave + lane;
+      if (UNIF || v < nvec) {
+        Vec<V> o;
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          float n0 = (xval(k, 4 * q) - mean) * rstd, n1 = (xval(k, 4 * q + 1) - mean) * rstd;
+          float n2 = (xval(k, 4 * q + 2) - mean) * rstd, n3 = (xval(k, 4 * q + 3) - mean) * rstd;
+          round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
+          round_pair(n2, n3);
+          float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
+          round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
+          round_pair(y2, y3);
+          o.w[2 * q] = pack_bf16(y0 + hc[q].x, y1 + hc[q].y);  // bf16(y + shift)
+          o.w[2 * q + 1] = pack_bf16(y2 + hc[q].z, y3 + hc[q].w);
+        }
+        store_vec_nt<V>(orow + v * V, o);
+      }
+      // keep two steps' table values live at a time (the scheduler would
+      // otherwise hoist every LDS read and halve the occupancy)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if constexpr (kPrefetch) {
+    // double buffer: row s is in A (or B) while the next row loads into B (or A)
+    while (true) {
+      int s1 = s + row_step;
+      if (s1 < S) load_row(bufB, s1);
+      process(bufA, s);
+      if (s1 >= S) break;
+      s = s1;
+      s1 = s + row_step;
+      if (s1 < S) load_row(bufA, s1);
+      process(bufB, s);
+      if (s1 >= S) break;
+      s = s1;
+    }
+  } else {
+    while (true) {
+      process(bufA, s);
+      s += row_step;
+      if (s >= S) break;
+      load_row(bufA, s);
     }
   }
 }
@@ -229,6 +459,63 @@ int launch_stream(const LnArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+// Compute units of the current device (cached; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
+
+template <int V, int NV, bool UNIF>
+int launch_tab(const LnArgs& a, hipStream_t st) {
+  // TabShape<NV>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
+  const int64_t B = a.R / a.S;
+  const int cus = cu_count();
+  const int64_t target = (int64_t)TabShape<NV>::kBlocksPerCu * (cus > 0 ? cus : 256);
+  int64_t bpb = (target + B - 1) / B;
+  bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
+  const int64_t blocks = B * bpb;
+  const size_t lds = (size_t)2 * a.D * sizeof(float);
+  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)blocks), dim3(256), lds, st, a,
+                     (int)bpb);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int V>
+int dispatch_tab(const LnArgs& a, hipStream_t st) {
+  const int64_t nvec = a.D / V;
+  const int64_t nv = (nvec + kWave - 1) / kWave;
+  const bool unif = nvec % kWave == 0;
+#define ADALN_TAB_CASE(N)                                                           \
+  if (nv == N) return unif ? launch_tab<V, N, true>(a, st) : launch_tab<V, N, false>(a, st);
+  ADALN_TAB_CASE(1)
+  ADALN_TAB_CASE(2)
+  ADALN_TAB_CASE(3)
+  ADALN_TAB_CASE(4)
+  ADALN_TAB_CASE(5)
+  ADALN_TAB_CASE(6)
+  ADALN_TAB_CASE(7)
+  ADALN_TAB_CASE(8)
+  ADALN_TAB_CASE(9)
+  ADALN_TAB_CASE(10)
+  ADALN_TAB_CASE(11)
+  ADALN_TAB_CASE(12)
+  ADALN_TAB_CASE(13)
+  ADALN_TAB_CASE(14)
+  ADALN_TAB_CASE(15)
+  ADALN_TAB_CASE(16)
+#undef ADALN_TAB_CASE
+  return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
+}
+
 // vectors per lane -> the register-resident instantiation that covers it
 template <int V, bool GATHER>
 int dispatch(const LnArgs& a, hipStream_t st) {
@@ -245,8 +532,6 @@ int dispatch(const LnArgs& a, hipStream_t st) {
   ADALN_NV_CASE(10)
   ADALN_NV_CASE(12)
   ADALN_NV_CASE(16)
-  ADALN_NV_CASE(24)
-  ADALN_NV_CASE(32)
 #undef ADALN_NV_CASE
   return launch_stream<V, GATHER>(a, st);
 }
@@ -333,6 +618,10 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
                    aligned(out, vb) && stride_ok(B, sx_b) && stride_ok(S, sx_s) &&
                    stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
   hipStream_t st = (hipStream_t)stream;
+  // the tabled fast path indexes rows, samples and offsets in 32 bits
+  const bool tab = vec && D <= kTabMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
+                   B <= INT32_MAX;
+  if (tab) return V == 8 ? dispatch_tab<8>(a, st) : dispatch_tab<4>(a, st);
   if (V == 8) return vec ? dispatch<8, false>(a, st) : dispatch<8, true>(a, st);
   return vec ? dispatch<4, false>(a, st) : dispatch<4, true>(a, st);
 }
