@@ -7,13 +7,16 @@
 //
 // GELU: gelu_tanh(z) = 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3)
 // (Hendrycks & Gimpel).  Using 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)) it is
-// z * sigmoid(2u); the exponential is taken of -|2u| only (never overflows),
-// through the hardware base-2 exponential, and the sigmoid of a negative
-// argument is e/(1+e).  Result within one bf16 ulp of the correctly rounded
-// value.
+// z * sigmoid(2u), evaluated with one base-2 exponential and one hardware
+// reciprocal (see gelu_tanh_f32).  Result within one bf16 ulp of the
+// correctly rounded value.
 //
-// Design: streaming, one wavefront per row, U independent 16-byte loads per
-// lane in flight; the bias row stays in cache.
+// Design: streaming.  Vector-aligned rows take a column-chunk kernel: wave w
+// of chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it
+// visits, keeps that chunk of the bias in VGPRs for the whole launch and
+// issues a row's U loads (non-temporal, unguarded) before computing.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "host_common.hpp"
 
@@ -28,15 +31,16 @@ struct GeluArgs {
   int64_t rows, width;
 };
 
+// t = 2u log2(e) = z (c0 + c1 z^2) with c0 = 2 sqrt(2/pi) log2(e) and
+// c1 = 0.044715 c0; t has the sign of z.  sigmoid(2u) = 1 / (1 + 2^-t) for
+// t >= 0 and 2^t / (1 + 2^t) otherwise, so the exponential is only ever
+// taken of -|t| (in (0, 1], no overflow; exp2f keeps denormal results).
 __device__ __forceinline__ float gelu_tanh_f32(float z) {
-  const float k0 = 0.797884560802865355f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float log2e = 1.44269504088896341f;
-  float z3 = (z * z) * z;
-  float u = k0 * (z + k1 * z3);
-  float t = 2.0f * u;
-  float e = __builtin_exp2f(-__builtin_fabsf(t) * log2e);  // e^(-|t|) in [0, 1]
-  float num = (t >= 0.0f) ? z : z * e;
+  const float c0 = 2.302208198144324889f;  // 2 * sqrt(2/pi) * log2(e)
+  const float c1 = 0.102943239580023487f;  // 0.044715 * c0
+  const float t = z * __builtin_fmaf(z * z, c1, c0);
+  const float e = __builtin_exp2f(-__builtin_fabsf(t));
+  const float num = (t >= 0.0f) ? z : z * e;
   return num * __builtin_amdgcn_rcpf(1.0f + e);  // 1 + e in [1, 2]
 }
 
@@ -57,29 +61,32 @@ constexpr int kRowsPerBlock = 4;
 constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
 
 template <int V, int U>
-__global__ __launch_bounds__(256) void gelu_rows_vec(GeluArgs a) {
+__global__ __launch_bounds__(256) void gelu_chunks(GeluArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nvec = a.width / V;
-  for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.rows;
-       r += (int64_t)gridDim.x * kRowsPerBlock) {
+  const int64_t step = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  if (r >= a.rows) return;
+  bool ok[U];
+  int64_t off[U];  // element offset of the lane's u-th vector (clamped in-bounds)
+  Vec<V> bv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = (int64_t)blockIdx.y * kWave * U + (int64_t)u * kWave + lane;
+    ok[u] = v < nvec;
+    off[u] = (ok[u] ? v : nvec - 1) * V;
+    bv[u] = load_vec<V>(a.bias + off[u]);
+  }
+  for (; r < a.rows; r += step) {
     const uint16_t* xr = a.x + r * a.sx_row;
+    Vec<V> xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) xv[u] = load_vec_nt<V>(xr + off[u]);
     uint16_t* orow = a.out + r * a.width;
-    for (int64_t base = lane; base < nvec; base += (int64_t)U * kWave) {
-      Vec<V> xv[U], bv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t v = base + (int64_t)u * kWave;
-        if (v < nvec) {
-          xv[u] = load_vec<V>(xr + v * V);
-          bv[u] = load_vec<V>(a.bias + v * V);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t v = base + (int64_t)u * kWave;
-        if (v < nvec) store_vec<V>(orow + v * V, bias_gelu_vec<V>(xv[u], bv[u]));
-      }
-    }
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) store_vec_nt<V>(orow + off[u], bias_gelu_vec<V>(xv[u], bv[u]));
   }
 }
 
@@ -99,6 +106,52 @@ __global__ __launch_bounds__(256) void gelu_rows_scalar(GeluArgs a) {
 inline unsigned grid_for(int64_t R) {
   int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
   return (unsigned)std::min(blocks, kMaxBlocks);
+}
+
+// Compute units of the current device (cached; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kChunkBlocksPerCu = 4;
+
+template <int V, int U>
+int launch_chunks(const GeluArgs& a, hipStream_t st) {
+  const int64_t nvec = a.width / V;
+  const int64_t nchunks = (nvec + kWave * U - 1) / (kWave * U);
+  if (nchunks > 65535) {  // grid.y limit: very long rows go element-wise
+    hipLaunchKernelGGL(gelu_rows_scalar, dim3(grid_for(a.rows)), dim3(256), 0, st, a);
+    return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+  }
+  const int cus = cu_count();
+  const int64_t target = (int64_t)kChunkBlocksPerCu * (cus > 0 ? cus : 256);
+  int64_t gx = (target + nchunks - 1) / nchunks;
+  gx = std::max<int64_t>(1, std::min<int64_t>(gx, (a.rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((gelu_chunks<V, U>), dim3((unsigned)gx, (unsigned)nchunks), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int V>
+int dispatch_chunks(const GeluArgs& a, hipStream_t st) {
+  const int64_t per_lane = (a.width / V + kWave - 1) / kWave;
+  switch (std::min<int64_t>(per_lane, 8)) {
+    case 1: return launch_chunks<V, 1>(a, st);
+    case 2: return launch_chunks<V, 2>(a, st);
+    case 3: return launch_chunks<V, 3>(a, st);
+    case 4: return launch_chunks<V, 4>(a, st);
+    case 5: return launch_chunks<V, 5>(a, st);
+    case 6: return launch_chunks<V, 6>(a, st);
+    case 7: return launch_chunks<V, 7>(a, st);
+    default: return launch_chunks<V, 8>(a, st);
+  }
 }
 
 }  // namespace
@@ -141,11 +194,8 @@ extern "C" int bias_gelu_tanh(const void* x, int64_t rows, int64_t width, int64_
            aligned(out, vb) && (rows <= 1 || ((uintptr_t)sx_row * 2u) % vb == 0);
   };
   hipStream_t st = (hipStream_t)stream;
-  if (vec_ok(16))
-    hipLaunchKernelGGL((gelu_rows_vec<8, 8>), dim3(grid_for(rows)), dim3(256), 0, st, a);
-  else if (vec_ok(8))
-    hipLaunchKernelGGL((gelu_rows_vec<4, 8>), dim3(grid_for(rows)), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(gelu_rows_scalar, dim3(grid_for(rows)), dim3(256), 0, st, a);
+  if (vec_ok(16)) return dispatch_chunks<8>(a, st);
+  if (vec_ok(8)) return dispatch_chunks<4>(a, st);
+  hipLaunchKernelGGL(gelu_rows_scalar, dim3(grid_for(rows)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }

@@ -129,6 +129,28 @@ __device__ __forceinline__ void merge_level(float& m, float& m2, float& n, int l
   n = an;
 }
 
+// Butterfly level when both halves hold `cnt_half` elements: nb/n = 0.5
+// exactly, so no division (bit-identical to merge_level with those counts).
+template <int OFF>
+__device__ __forceinline__ void merge_level_equal(float& m, float& m2, float cnt_half, int lane) {
+  const float pm = lane_xor<OFF>(m);
+  const float pm2 = lane_xor<OFF>(m2);
+  const bool upper = (lane & OFF) != 0;
+  const float am = upper ? pm : m, bm = upper ? m : pm;  // lower lane's mean, upper lane's mean
+  const float delta = bm - am;
+  const float mm = __builtin_fmaf(delta, 0.5f, am);
+  m2 = (m2 + pm2) + (delta * delta) * (cnt_half * 0.5f);
+  m = mm;
+}
+
+// Merge groups of 16 lanes that each hold `cnt` elements.
+__device__ __forceinline__ void merge_lanes16_equal(float& m, float& m2, float cnt, int lane) {
+  merge_level_equal<1>(m, m2, cnt, lane);
+  merge_level_equal<2>(m, m2, 2.0f * cnt, lane);
+  merge_level_equal<4>(m, m2, 4.0f * cnt, lane);
+  merge_level_equal<8>(m, m2, 8.0f * cnt, lane);
+}
+
 // Merge the per-lane states of groups of L lanes (L = 16 or 64).
 template <int L>
 __device__ __forceinline__ void merge_lanes(float& m, float& m2, float& n, int lane) {

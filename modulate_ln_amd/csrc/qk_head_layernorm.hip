@@ -10,8 +10,12 @@
 // own a head and a wave normalizes four heads at once.  Lane l of the group
 // owns vectors l, l+16, ... (16-byte loads for V = 8); the merge tree is the
 // four in-row levels 1, 2, 4, 8 (DPP quad permutes, ds_swizzle, row rotate),
-// so no LDS and no cross-row traffic.  q rows come first, then k rows, in
-// one grid.
+// so no LDS and no cross-row traffic.  Vector-aligned inputs take qk_heads:
+// grid row 0 normalizes q, grid row 1 k; each lane keeps its slice of that
+// side's weight and bias in fp32 VGPRs for the whole launch, and each
+// 16-lane group loads HP heads (non-temporal, unguarded) before reducing
+// them, so several heads per lane are in flight.
+#include <atomic>
 #include <utility>
 
 #include "device_common.hpp"
@@ -128,6 +132,130 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
       }
     }
   }
+}
+
+// Fast path: vector-aligned q/k.  HP heads per group per iteration.
+template <int V, int NV, int HP, bool UNIFORM, bool AFFINE, bool EQ>
+__global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
+  const QkSide& sd = a.side[blockIdx.y];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int l16 = lane & (kGroup - 1);
+  const int group = threadIdx.x >> 4;
+  const int nvec = (int)(a.Dh / V);
+  const float Df = (float)a.Dh;
+  const int nv_lane = nvec / kGroup + (l16 < nvec % kGroup ? 1 : 0);
+  int off[NV];  // element offset of the lane's k-th vector within a head (clamped)
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = k * kGroup + l16;
+    off[k] = (EQ || v < nvec ? v : nvec - 1) * V;
+  }
+  float wf[NV][V], bf[NV][V];
+  if constexpr (AFFINE) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const Vec<V> wv = load_vec<V>(sd.w + off[k]);
+      const Vec<V> bv = load_vec<V>(sd.bias + off[k]);
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        wf[k][2 * i] = lo_f32(wv.w[i]);
+        wf[k][2 * i + 1] = hi_f32(wv.w[i]);
+        bf[k][2 * i] = lo_f32(bv.w[i]);
+        bf[k][2 * i + 1] = hi_f32(bv.w[i]);
+      }
+    }
+  }
+  const int64_t step = (int64_t)gridDim.x * kGroupsPerBlock * HP;
+  for (int64_t h0 = ((int64_t)blockIdx.x * kGroupsPerBlock + group) * HP; h0 < a.Rq; h0 += step) {
+    Vec<V> buf[HP][NV];
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int64_t rr = h0 + i < a.Rq ? h0 + i : a.Rq - 1;
+      const uint16_t* xr;
+      if constexpr (UNIFORM) {
+        xr = sd.x + rr * sd.s_h;
+      } else {
+        const int64_t hh = rr % a.H;
+        const int64_t t = rr / a.H;
+        xr = sd.x + (t / a.S) * sd.s_b + (t % a.S) * sd.s_s + hh * sd.s_h;
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) buf[i][k] = load_vec_nt<V>(xr + off[k]);
+    }
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      float mean = 0.0f, m2 = 0.0f;
+      welford_lane<V>(buf[i], EQ ? (int64_t)NV * kGroup : (int64_t)nvec, l16, mean, m2,
+                      std::make_integer_sequence<int, NV>{});
+      if constexpr (EQ) {
+        merge_lanes16_equal(mean, m2, (float)(NV * V), lane);
+      } else {
+        float n = (float)(nv_lane * V);
+        merge_lanes<kGroup>(mean, m2, n, lane);
+      }
+      const float rstd = finalize_rstd(m2, Df, a.eps);
+      if (h0 + i < a.Rq) {
+        uint16_t* orow = sd.out + (h0 + i) * a.Dh;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          if (EQ || k * kGroup + l16 < nvec) {
+            Vec<V> o;
+#pragma unroll
+            for (int j = 0; j < V / 2; ++j) {
+              float y0 = (lo_f32(buf[i][k].w[j]) - mean) * rstd;
+              float y1 = (hi_f32(buf[i][k].w[j]) - mean) * rstd;
+              if constexpr (AFFINE) {
+                y0 = __builtin_fmaf(wf[k][2 * j], y0, bf[k][2 * j]);
+                y1 = __builtin_fmaf(wf[k][2 * j + 1], y1, bf[k][2 * j + 1]);
+              }
+              o.w[j] = pack_bf16(y0, y1);
+            }
+            store_vec_nt<V>(orow + off[k], o);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Compute units of the current device (cached; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kHeadsBlocksPerCu = 4;
+
+template <int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
+int launch_heads(const QkArgs& a, hipStream_t st) {
+  constexpr int HP = NV == 1 ? 4 : (NV == 2 ? 2 : 1);
+  const int64_t need = (a.Rq + (int64_t)kGroupsPerBlock * HP - 1) / ((int64_t)kGroupsPerBlock * HP);
+  const int cus = cu_count();
+  const int64_t target = (int64_t)kHeadsBlocksPerCu * (cus > 0 ? cus : 256) / 2;  // per side
+  const int64_t gx = std::max<int64_t>(1, std::min(need, target));
+  hipLaunchKernelGGL((qk_heads<V, NV, HP, UNIFORM, AFFINE, EQ>), dim3((unsigned)gx, 2), dim3(256), 0,
+                     st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int V, int NV, bool UNIFORM, bool AFFINE>
+int pick_eq(const QkArgs& a, hipStream_t st) {
+  const bool eq = (a.Dh / V) == (int64_t)NV * kGroup;
+  return eq ? launch_heads<V, NV, UNIFORM, AFFINE, true>(a, st)
+            : launch_heads<V, NV, UNIFORM, AFFINE, false>(a, st);
+}
+
+template <int V, int NV>
+int dispatch_heads(const QkArgs& a, bool uniform, bool affine, hipStream_t st) {
+  if (uniform) return affine ? pick_eq<V, NV, true, true>(a, st) : pick_eq<V, NV, true, false>(a, st);
+  return affine ? pick_eq<V, NV, false, true>(a, st) : pick_eq<V, NV, false, false>(a, st);
 }
 
 inline unsigned grid_for(int64_t heads) {
@@ -257,6 +385,13 @@ extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int6
   hipStream_t st = (hipStream_t)stream;
   const bool gather = !vec;
   const int64_t nv = (Dh / V + kGroup - 1) / kGroup;
+  if (vec) {
+    if (V == 8) return nv <= 1 ? dispatch_heads<8, 1>(a, uniform, affine, st)
+                               : dispatch_heads<8, 2>(a, uniform, affine, st);
+    if (nv <= 1) return dispatch_heads<4, 1>(a, uniform, affine, st);
+    if (nv <= 2) return dispatch_heads<4, 2>(a, uniform, affine, st);
+    return dispatch_heads<4, 4>(a, uniform, affine, st);
+  }
   if (V == 8) {
     if (nv <= 1) return pick_uniform<8, 1>(a, uniform, affine, gather, st);
     return pick_uniform<8, 2>(a, uniform, affine, gather, st);

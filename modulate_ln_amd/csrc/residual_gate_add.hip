@@ -6,10 +6,14 @@
 // eager chain is two bf16 ops (a multiply, then an add), so the product is
 // rounded to bf16 before the add.
 //
-// Design: pure streaming (2 reads + 1 write per element).  One wavefront per
-// row; each lane issues U independent 16-byte loads of residual and update
-// before it computes, so a wave keeps 2*U*1 KiB in flight.  The per-sample
-// gate row is shared by every row of a sample and stays in cache.
+// Design: pure streaming (2 reads + 1 write per element).  Vector-aligned
+// rows take the column-chunk kernel: wave w of chunk c owns vectors
+// c*64*U + lane + 64*u (u < U) of every row it visits (rows w, w + W, ...),
+// keeps that chunk of the current sample's gate in VGPRs, and issues all
+// 2*U residual/update loads of a row (non-temporal, unguarded) before it
+// computes.  Other layouts take a row-per-wave or element-wise kernel.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "host_common.hpp"
 
@@ -43,34 +47,56 @@ __device__ __forceinline__ Vec<V> gate_add_vec(const Vec<V>& rv, const Vec<V>& g
 constexpr int kRowsPerBlock = 4;
 constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
 
+// Column-chunk streaming kernel (vector-aligned rows, unit element stride).
 template <int V, int U>
-__global__ __launch_bounds__(256) void rga_rows_vec(RgaArgs a) {
+__global__ __launch_bounds__(256) void rga_chunks(RgaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nvec = a.D / V;
-  for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
-       r += (int64_t)gridDim.x * kRowsPerBlock) {
-    const int64_t b = r / a.S;
-    const int64_t s = r - b * a.S;
+  const int64_t step = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  if (r >= a.R) return;
+  int64_t b = r / a.S;
+  int64_t s = r - b * a.S;
+  const int64_t db = step / a.S;
+  const int64_t ds = step - db * a.S;
+
+  bool ok[U];
+  int64_t off[U];  // element offset of the lane's u-th vector (clamped in-bounds)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = (int64_t)blockIdx.y * kWave * U + (int64_t)u * kWave + lane;
+    ok[u] = v < nvec;
+    off[u] = (ok[u] ? v : nvec - 1) * V;
+  }
+  int64_t cached_b = -1;
+  Vec<V> gv[U];
+  while (true) {
+    if (b != cached_b) {
+      const uint16_t* gr = a.gate + b * a.sg_b;
+#pragma unroll
+      for (int u = 0; u < U; ++u) gv[u] = load_vec<V>(gr + off[u]);
+      cached_b = b;
+    }
     const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
     const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
-    const uint16_t* gr = a.gate + b * a.sg_b;
+    Vec<V> rv[U], uv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      rv[u] = load_vec_nt<V>(rr + off[u]);
+      uv[u] = load_vec_nt<V>(ur + off[u]);
+    }
     uint16_t* orow = a.out + r * a.D;
-    for (int64_t base = lane; base < nvec; base += (int64_t)U * kWave) {
-      Vec<V> rv[U], uv[U], gv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t v = base + (int64_t)u * kWave;
-        if (v < nvec) {
-          rv[u] = load_vec<V>(rr + v * V);
-          uv[u] = load_vec<V>(ur + v * V);
-          gv[u] = load_vec<V>(gr + v * V);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t v = base + (int64_t)u * kWave;
-        if (v < nvec) store_vec<V>(orow + v * V, gate_add_vec<V>(rv[u], gv[u], uv[u]));
-      }
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) store_vec<V>(orow + off[u], gate_add_vec<V>(rv[u], gv[u], uv[u]));
+    r += step;
+    if (r >= a.R) break;
+    s += ds;
+    b += db;
+    if (s >= a.S) {
+      s -= a.S;
+      ++b;
     }
   }
 }
@@ -97,6 +123,53 @@ __global__ __launch_bounds__(256) void rga_rows_scalar(RgaArgs a) {
 inline unsigned grid_for(int64_t R) {
   int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
   return (unsigned)std::min(blocks, kMaxBlocks);
+}
+
+// Compute units of the current device (cached; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kChunkBlocksPerCu = 4;
+
+template <int V, int U>
+int launch_chunks(const RgaArgs& a, hipStream_t st) {
+  const int64_t nvec = a.D / V;
+  const int64_t nchunks = (nvec + kWave * U - 1) / (kWave * U);
+  if (nchunks > 65535) {  // grid.y limit: rows of more than 2^25 vectors go element-wise
+    hipLaunchKernelGGL(rga_rows_scalar, dim3(grid_for(a.R)), dim3(256), 0, st, a);
+    return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+  }
+  const int cus = cu_count();
+  const int64_t target = (int64_t)kChunkBlocksPerCu * (cus > 0 ? cus : 256);
+  int64_t gx = (target + nchunks - 1) / nchunks;
+  gx = std::max<int64_t>(1, std::min<int64_t>(gx, (a.R + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((rga_chunks<V, U>), dim3((unsigned)gx, (unsigned)nchunks), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+// vectors per lane in one chunk: as many as a row needs, at most 8
+template <int V>
+int dispatch_chunks(const RgaArgs& a, hipStream_t st) {
+  const int64_t per_lane = (a.D / V + kWave - 1) / kWave;
+  switch (std::min<int64_t>(per_lane, 8)) {
+    case 1: return launch_chunks<V, 1>(a, st);
+    case 2: return launch_chunks<V, 2>(a, st);
+    case 3: return launch_chunks<V, 3>(a, st);
+    case 4: return launch_chunks<V, 4>(a, st);
+    case 5: return launch_chunks<V, 5>(a, st);
+    case 6: return launch_chunks<V, 6>(a, st);
+    case 7: return launch_chunks<V, 7>(a, st);
+    default: return launch_chunks<V, 8>(a, st);
+  }
 }
 
 }  // namespace
@@ -168,11 +241,8 @@ extern "C" int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_
            aligned(gate, vb) && aligned(out, vb) && so_(B, sr_b) && so_(S, sr_s) && so_(B, su_b) &&
            so_(S, su_s) && so_(B, sg_b);
   };
-  if (vec_ok(16))
-    hipLaunchKernelGGL((rga_rows_vec<8, 8>), dim3(grid_for(R)), dim3(256), 0, st, a);
-  else if (vec_ok(8))
-    hipLaunchKernelGGL((rga_rows_vec<4, 8>), dim3(grid_for(R)), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(rga_rows_scalar, dim3(grid_for(R)), dim3(256), 0, st, a);
+  if (vec_ok(16)) return dispatch_chunks<8>(a, st);
+  if (vec_ok(8)) return dispatch_chunks<4>(a, st);
+  hipLaunchKernelGGL(rga_rows_scalar, dim3(grid_for(R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
