@@ -14,7 +14,9 @@
 // Design: streaming.  Vector-aligned rows take a column-chunk kernel: wave w
 // of chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it
 // visits, keeps that chunk of the bias in VGPRs for the whole launch and
-// issues a row's U loads (non-temporal, unguarded) before computing.
+// loads the next row it visits (non-temporal, unguarded) while it computes
+// the current one: the GELU costs enough ALU per byte that the loads must
+// not wait for it.
 #include <atomic>
 
 #include "device_common.hpp"
@@ -34,12 +36,15 @@ struct GeluArgs {
 // t = 2u log2(e) = z (c0 + c1 z^2) with c0 = 2 sqrt(2/pi) log2(e) and
 // c1 = 0.044715 c0; t has the sign of z.  sigmoid(2u) = 1 / (1 + 2^-t) for
 // t >= 0 and 2^t / (1 + 2^t) otherwise, so the exponential is only ever
-// taken of -|t| (in (0, 1], no overflow; exp2f keeps denormal results).
+// taken of -|t|.  The hardware exp2 returns normal numbers only, so it is
+// evaluated at 64 - |t| (normal down to |t| = 190) and scaled back by the
+// exact factor 2^-64, which keeps denormal e; beyond |t| = 190 the result is
+// below every bf16 subnormal anyway.
 __device__ __forceinline__ float gelu_tanh_f32(float z) {
   const float c0 = 2.302208198144324889f;  // 2 * sqrt(2/pi) * log2(e)
   const float c1 = 0.102943239580023487f;  // 0.044715 * c0
   const float t = z * __builtin_fmaf(z * z, c1, c0);
-  const float e = __builtin_exp2f(-__builtin_fabsf(t));
+  const float e = __builtin_amdgcn_exp2f(64.0f - __builtin_fabsf(t)) * 0x1p-64f;  // 2^-|t|
   const float num = (t >= 0.0f) ? z : z * e;
   return num * __builtin_amdgcn_rcpf(1.0f + e);  // 1 + e in [1, 2]
 }
@@ -69,24 +74,41 @@ __global__ __launch_bounds__(256) void gelu_chunks(GeluArgs a) {
   int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
   if (r >= a.rows) return;
   bool ok[U];
-  int64_t off[U];  // element offset of the lane's u-th vector (clamped in-bounds)
+  uint32_t off[U];  // element offset of the lane's u-th vector (clamped in-bounds; width < 2^31)
   Vec<V> bv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t v = (int64_t)blockIdx.y * kWave * U + (int64_t)u * kWave + lane;
     ok[u] = v < nvec;
-    off[u] = (ok[u] ? v : nvec - 1) * V;
+    off[u] = (uint32_t)((ok[u] ? v : nvec - 1) * V);
     bv[u] = load_vec<V>(a.bias + off[u]);
   }
-  for (; r < a.rows; r += step) {
-    const uint16_t* xr = a.x + r * a.sx_row;
-    Vec<V> xv[U];
+  auto load_row = [&](Vec<V>* xv, int64_t rr) {
+    const uint16_t* xr = a.x + rr * a.sx_row;
 #pragma unroll
     for (int u = 0; u < U; ++u) xv[u] = load_vec_nt<V>(xr + off[u]);
-    uint16_t* orow = a.out + r * a.width;
+  };
+  auto store_row = [&](const Vec<V>* xv, int64_t rr) {
+    uint16_t* orow = a.out + rr * a.width;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
       if (ok[u]) store_vec_nt<V>(orow + off[u], bias_gelu_vec<V>(xv[u], bv[u]));
+      __builtin_amdgcn_sched_barrier(0);  // one vector's temporaries live at a time
+    }
+  };
+  Vec<V> xa[U], xb[U];
+  load_row(xa, r);
+  while (true) {  // double buffer: row r in xa (or xb), row r + step loading into the other
+    int64_t r1 = r + step;
+    if (r1 < a.rows) load_row(xb, r1);
+    store_row(xa, r);
+    if (r1 >= a.rows) break;
+    r = r1;
+    r1 = r + step;
+    if (r1 < a.rows) load_row(xa, r1);
+    store_row(xb, r);
+    if (r1 >= a.rows) break;
+    r = r1;
   }
 }
 
@@ -121,7 +143,12 @@ inline int cu_count() {
   return n;
 }
 
-constexpr int kChunkBlocksPerCu = 4;
+// grid size of the column-chunk kernel (blocks per compute unit in total),
+// measured on MI355X; overridable at build time
+#ifndef ADALN_CHUNK_BLOCKS_PER_CU
+#define ADALN_CHUNK_BLOCKS_PER_CU 16
+#endif
+constexpr int kChunkBlocksPerCu = ADALN_CHUNK_BLOCKS_PER_CU;
 
 template <int V, int U>
 int launch_chunks(const GeluArgs& a, hipStream_t st) {
@@ -139,10 +166,15 @@ int launch_chunks(const GeluArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+// most vectors per lane in one chunk (VGPRs: two row buffers and the bias)
+#ifndef ADALN_GELU_MAX_U
+#define ADALN_GELU_MAX_U 4
+#endif
+
 template <int V>
 int dispatch_chunks(const GeluArgs& a, hipStream_t st) {
   const int64_t per_lane = (a.width / V + kWave - 1) / kWave;
-  switch (std::min<int64_t>(per_lane, 8)) {
+  switch (std::min<int64_t>(per_lane, ADALN_GELU_MAX_U)) {
     case 1: return launch_chunks<V, 1>(a, st);
     case 2: return launch_chunks<V, 2>(a, st);
     case 3: return launch_chunks<V, 3>(a, st);
@@ -185,6 +217,7 @@ extern "C" int bias_gelu_tanh(const void* x, int64_t rows, int64_t width, int64_
   const Span sx = span_of(x, {{rows, sx_row}, {width, 1}});
   const Span sb = span_of(bias, {{width, 1}});
   const bool x_contig = rows == 1 || sx_row == width;
+  if (width >= ((int64_t)1 << 31)) return ADALN_ERR_TOO_LARGE;
   if (overlaps(so, sx) && !(x == out && x_contig)) return ADALN_ERR_ALIAS;
   if (overlaps(so, sb)) return ADALN_ERR_ALIAS;
 

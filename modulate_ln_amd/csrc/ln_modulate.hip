@@ -205,6 +205,123 @@ __device__ __forceinline__ float hi_f32_again(uint32_t w) {
   return __builtin_bit_cast(float, r);
 }
 
+// The per-sample tables: bf16(1 + scale) and shift as fp32, float4-packed
+// [table][V/4][nvec] so a lane's reads for vector v are contiguous across
+// the wave.  Built cooperatively by the nthreads threads of a block.
+template <int V>
+__device__ __forceinline__ void build_tables(float4* tab, const uint16_t* sc, const uint16_t* sh,
+                                             int nvec, int tid, int nthreads) {
+  const int shift_off = (V / 4) * nvec;
+  for (int v = tid; v < nvec; v += nthreads) {
+    const Vec<V> sv = load_vec<V>(sc + v * V);
+    const Vec<V> hv = load_vec<V>(sh + v * V);
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
+      float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
+      round_pair(o0, o1);  // bf16(1 + scale)
+      round_pair(o2, o3);
+      tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
+      tab[shift_off + q * nvec + v] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
+                                                  lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
+    }
+  }
+}
+
+// One row, held by one wave as NV packed vectors per lane (lane l owns
+// vectors l, l + 64, ...): Welford, merge tree, statistics, then
+// normalize, modulate with the LDS tables and store (non-temporal).
+// kXf32: widen the row once and keep it in fp32 for both passes; otherwise
+// widen it for the reduction and again (opaque to the compiler, so no fp32
+// copy stays live) when normalizing.
+template <int V, int NV, bool UNIF, bool kXf32>
+__device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* tab, int nvec, int lane,
+                                              float Df, float eps, uint16_t* orow, float* mean_out,
+                                              float* rstd_out) {
+  const int shift_off = (V / 4) * nvec;
+  float xf[NV][V];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      xf[k][2 * i] = lo_f32(buf[k].w[i]);
+      xf[k][2 * i + 1] = hi_f32(buf[k].w[i]);
+    }
+  auto xval = [&](int k, int e) -> float {
+    if constexpr (kXf32) return xf[k][e];
+    return (e & 1) ? hi_f32_again(buf[k].w[e / 2]) : lo_f32_again(buf[k].w[e / 2]);
+  };
+  float mean = 0.0f, m2 = 0.0f;
+  welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
+  if constexpr (UNIF) {
+    const float c = (float)(NV * V);
+    merge_down_equal<1>(mean, m2, c);
+    merge_down_equal<2>(mean, m2, c);
+    merge_down_equal<4>(mean, m2, c);
+    merge_down_equal<8>(mean, m2, c);
+    merge_down_equal<16>(mean, m2, c);
+    merge_down_equal<32>(mean, m2, c);
+  } else {
+    float n = (float)((nvec / kWave + (lane < nvec % kWave ? 1 : 0)) * V);
+    merge_down<1>(mean, m2, n);
+    merge_down<2>(mean, m2, n);
+    merge_down<4>(mean, m2, n);
+    merge_down<8>(mean, m2, n);
+    merge_down<16>(mean, m2, n);
+    merge_down<32>(mean, m2, n);
+  }
+  mean = bcast_lane0(mean);
+  m2 = bcast_lane0(m2);
+  const float rstd = finalize_rstd(m2, Df, eps);
+  if (lane == 0) {
+    if (mean_out) *mean_out = mean;
+    if (rstd_out) *rstd_out = rstd;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // table values for step k are read one step ahead of their use
+  float4 ot[V / 4], ht[V / 4];
+  auto read_tab = [&](int k) {
+    const int v = k * kWave + lane;
+    const int vc = (UNIF || v < nvec) ? v : nvec - 1;
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      ot[q] = tab[q * nvec + vc];
+      ht[q] = tab[shift_off + q * nvec + vc];
+    }
+  };
+  read_tab(0);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float4 oc[V / 4], hc[V / 4];
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      oc[q] = ot[q];
+      hc[q] = ht[q];
+    }
+    if (k + 1 < NV) read_tab(k + 1);
+    const int v = k * kWave + lane;
+    if (UNIF || v < nvec) {
+      Vec<V> o;
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        float n0 = (xval(k, 4 * q) - mean) * rstd, n1 = (xval(k, 4 * q + 1) - mean) * rstd;
+        float n2 = (xval(k, 4 * q + 2) - mean) * rstd, n3 = (xval(k, 4 * q + 3) - mean) * rstd;
+        round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
+        round_pair(n2, n3);
+        float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
+        round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
+        round_pair(y2, y3);
+        o.w[2 * q] = pack_bf16(y0 + hc[q].x, y1 + hc[q].y);  // bf16(y + shift)
+        o.w[2 * q + 1] = pack_bf16(y2 + hc[q].z, y3 + hc[q].w);
+      }
+      store_vec_nt<V>(orow + v * V, o);
+    }
+    // keep two steps' table values live at a time (the scheduler would
+    // otherwise hoist every LDS read and halve the occupancy)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int V, int NV, bool UNIF>
 __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   constexpr bool kPrefetch = TabShape<NV>::kPrefetch;
@@ -218,7 +335,6 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   const int b = blockIdx.x / bpb;
   const int j = blockIdx.x - b * bpb;
   const int row_step = 4 * bpb;
-  const int shift_off = (V / 4) * nvec;  // float4 index of the shift table
   int s = 4 * j + wave;
 
   const uint16_t* xb = a.x + (int64_t)b * a.sx_b;
@@ -235,118 +351,17 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   Vec<V> bufA[NV];
   Vec<V> bufB[kPrefetch ? NV : 1];
   if (s < S) load_row(bufA, s);
-
-  {
-    const uint16_t* sc = a.scale + (int64_t)b * a.ssc_b;
-    const uint16_t* sh = a.shift + (int64_t)b * a.ssh_b;
-    for (int v = threadIdx.x; v < nvec; v += 256) {
-      const Vec<V> sv = load_vec<V>(sc + v * V);
-      const Vec<V> hv = load_vec<V>(sh + v * V);
-#pragma unroll
-      for (int q = 0; q < V / 4; ++q) {
-        float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
-        float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
-        round_pair(o0, o1);  // bf16(1 + scale)
-        round_pair(o2, o3);
-        tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
-        tab[shift_off + q * nvec + v] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
-                                                    lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
-      }
-    }
-  }
+  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
+                  threadIdx.x, 256);
   __syncthreads();
   if (s >= S) return;
 
   const float Df = (float)D;
-  const int nv_lane = nvec / kWave + (lane < nvec % kWave ? 1 : 0);
-
   auto process = [&](const Vec<V>* buf, int ss) {
-    // kXf32: widen the row once and keep it in fp32 for both passes;
-    // otherwise widen it for the reduction and again (opaque to the
-    // compiler, so no fp32 copy stays live) when normalizing
-    float xf[NV][V];
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        xf[k][2 * i] = lo_f32(buf[k].w[i]);
-        xf[k][2 * i + 1] = hi_f32(buf[k].w[i]);
-      }
-    auto xval = [&](int k, int e) -> float {
-      if constexpr (kXf32) return xf[k][e];
-      return (e & 1) ? hi_f32_again(buf[k].w[e / 2]) : lo_f32_again(buf[k].w[e / 2]);
-    };
-    float mean = 0.0f, m2 = 0.0f;
-    welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
-    if constexpr (UNIF) {
-      const float c = (float)(NV * V);
-      merge_down_equal<1>(mean, m2, c);
-      merge_down_equal<2>(mean, m2, c);
-      merge_down_equal<4>(mean, m2, c);
-      merge_down_equal<8>(mean, m2, c);
-      merge_down_equal<16>(mean, m2, c);
-      merge_down_equal<32>(mean, m2, c);
-    } else {
-      float n = (float)(nv_lane * V);
-      merge_down<1>(mean, m2, n);
-      merge_down<2>(mean, m2, n);
-      merge_down<4>(mean, m2, n);
-      merge_down<8>(mean, m2, n);
-      merge_down<16>(mean, m2, n);
-      merge_down<32>(mean, m2, n);
-    }
-    mean = bcast_lane0(mean);
-    m2 = bcast_lane0(m2);
-    const float rstd = finalize_rstd(m2, Df, a.eps);
     const int64_t r = (int64_t)b * S + ss;
-    if (lane == 0) {
-      if (a.mean_out) a.mean_out[r] = mean;
-      if (a.rstd_out) a.rstd_out[r] = rstd;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    uint16_t* orow = a.out + r * D;
-    // table values for step k are read one step ahead of their use
-    float4 ot[V / 4], ht[V / 4];
-    auto read_tab = [&](int k) {
-      const int v = k * kWave + lane;
-      const int vc = (UNIF || v < nvec) ? v : nvec - 1;
-#pragma unroll
-      for (int q = 0; q < V / 4; ++q) {
-        ot[q] = tab[q * nvec + vc];
-        ht[q] = tab[shift_off + q * nvec + vc];
-      }
-    };
-    read_tab(0);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      float4 oc[V / 4], hc[V / 4];
-#pragma unroll
-      for (int q = 0; q < V / 4; ++q) {
-        oc[q] = ot[q];
-        hc[q] = ht[q];
-      }
-      if (k + 1 < NV) read_tab(k + 1);
-      const int v = k * kWave + lane;
-      if (UNIF || v < nvec) {
-        Vec<V> o;
-#pragma unroll
-        for (int q = 0; q < V / 4; ++q) {
-          float n0 = (xval(k, 4 * q) - mean) * rstd, n1 = (xval(k, 4 * q + 1) - mean) * rstd;
-          float n2 = (xval(k, 4 * q + 2) - mean) * rstd, n3 = (xval(k, 4 * q + 3) - mean) * rstd;
-          round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
-          round_pair(n2, n3);
-          float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
-          round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
-          round_pair(y2, y3);
-          o.w[2 * q] = pack_bf16(y0 + hc[q].x, y1 + hc[q].y);  // bf16(y + shift)
-          o.w[2 * q + 1] = pack_bf16(y2 + hc[q].z, y3 + hc[q].w);
-        }
-        store_vec_nt<V>(orow + v * V, o);
-      }
-      // keep two steps' table values live at a time (the scheduler would
-      // otherwise hoist every LDS read and halve the occupancy)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    normalize_row<V, NV, UNIF, kXf32>(buf, tab, nvec, lane, Df, a.eps, a.out + r * D,
+                                      a.mean_out ? a.mean_out + r : nullptr,
+                                      a.rstd_out ? a.rstd_out + r : nullptr);
   };
 
   if constexpr (kPrefetch) {
@@ -371,6 +386,86 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
       load_row(bufA, s);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed input: tokens contiguous (sx_s == 1), hidden elements sx_d apart
+// -- the permuted activations the Sana report describes (实现拆解 §3, the
+// layout copy aten's LayerNorm pays).  A block of 8 waves takes a tile of 8
+// consecutive tokens of one sample.  Thread i loads, for each of its
+// vectors' 8 hidden positions, the 8 tokens as one 16-byte load (so every
+// 128-byte line of the input is read once, by the 8 tiles that share it),
+// transposes the 8x8 bf16 block in registers and writes whole vectors into
+// an LDS tile [token][vector].  Wave w then runs the same per-row routine
+// as the contiguous kernel on token w, reading its row from LDS: identical
+// bits, one HBM read and one HBM write, no layout copy.
+// ---------------------------------------------------------------------------
+constexpr int kTrTokens = 8;
+
+// bytes (lo, hi) of a and bytes (lo, hi) of b -> one word: lo halves or hi halves
+__device__ __forceinline__ uint32_t join_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t join_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <int NV, bool UNIF>
+__global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sample) {
+  constexpr int V = 8;
+  extern __shared__ float4 smem[];  // tables [2][2][nvec], then the x tile [8][nvec] (uint4)
+  const int D = (int)a.D;
+  const int nvec = D / V;
+  const int S = (int)a.S;
+  // tiles of one XCD (blockIdx mod 8) are consecutive, so the 8 tiles that
+  // share each input line run on the same L2
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int tile = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+  const int b = tile / tiles_per_sample;
+  const int t0 = (tile - b * tiles_per_sample) * kTrTokens;
+  float4* tab = smem;
+  uint4* xt = reinterpret_cast<uint4*>(smem + 4 * nvec);
+
+  const uint16_t* xb = a.x + (int64_t)b * a.sx_b + t0;
+  for (int v = threadIdx.x; v < nvec; v += 512) {
+    uint4 c[V];  // c[j]: tokens t0..t0+7 of hidden position 8v + j
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      u32x4 t = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(xb + (int64_t)(V * v + j) * a.sx_d));
+      c[j] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    // token 2q (+1) lives in the low (high) half of word q of every c[j]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w0 = (&c[0].x)[q], w1 = (&c[1].x)[q], w2 = (&c[2].x)[q], w3 = (&c[3].x)[q];
+      const uint32_t w4 = (&c[4].x)[q], w5 = (&c[5].x)[q], w6 = (&c[6].x)[q], w7 = (&c[7].x)[q];
+      xt[(2 * q) * nvec + v] = make_uint4(join_lo(w0, w1), join_lo(w2, w3), join_lo(w4, w5), join_lo(w6, w7));
+      xt[(2 * q + 1) * nvec + v] =
+          make_uint4(join_hi(w0, w1), join_hi(w2, w3), join_hi(w4, w5), join_hi(w6, w7));
+    }
+  }
+  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
+                  threadIdx.x, 512);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // token within the tile
+  Vec<V> buf[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = k * kWave + lane;
+    const uint4 t = xt[w * nvec + ((UNIF || v < nvec) ? v : nvec - 1)];
+    buf[k].w[0] = t.x;
+    buf[k].w[1] = t.y;
+    buf[k].w[2] = t.z;
+    buf[k].w[3] = t.w;
+  }
+  const int64_t r = (int64_t)b * S + t0 + w;
+  normalize_row<V, NV, UNIF, true>(buf, tab, nvec, lane, (float)D, a.eps, a.out + r * D,
+                                   a.mean_out ? a.mean_out + r : nullptr,
+                                   a.rstd_out ? a.rstd_out + r : nullptr);
 }
 
 // Rows too long to hold in registers: the same order, pass 2 re-reads the
@@ -487,6 +582,37 @@ int launch_tab(const LnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)blocks), dim3(256), lds, st, a,
                      (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int NV, bool UNIF>
+int launch_tr(const LnArgs& a, hipStream_t st) {
+  const int64_t B = a.R / a.S;
+  const int64_t tiles_per_sample = a.S / kTrTokens;
+  const int64_t nvec = a.D / 8;
+  const size_t lds = (size_t)nvec * (4 * sizeof(float4) + kTrTokens * sizeof(uint4));
+  hipLaunchKernelGGL((ln_modulate_tr<NV, UNIF>), dim3((unsigned)(B * tiles_per_sample)), dim3(512),
+                     lds, st, a, (int)tiles_per_sample);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+constexpr int kTrMaxD = 4096;  // 96 KiB of LDS (tables + tile)
+
+int dispatch_tr(const LnArgs& a, hipStream_t st) {
+  const int64_t nvec = a.D / 8;
+  const int64_t nv = (nvec + kWave - 1) / kWave;
+  const bool unif = nvec % kWave == 0;
+#define ADALN_TR_CASE(N) \
+  if (nv == N) return unif ? launch_tr<N, true>(a, st) : launch_tr<N, false>(a, st);
+  ADALN_TR_CASE(1)
+  ADALN_TR_CASE(2)
+  ADALN_TR_CASE(3)
+  ADALN_TR_CASE(4)
+  ADALN_TR_CASE(5)
+  ADALN_TR_CASE(6)
+  ADALN_TR_CASE(7)
+  ADALN_TR_CASE(8)
+#undef ADALN_TR_CASE
+  return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
 }
 
 template <int V>
@@ -622,6 +748,12 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
   const bool tab = vec && D <= kTabMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
                    B <= INT32_MAX;
   if (tab) return V == 8 ? dispatch_tab<8>(a, st) : dispatch_tab<4>(a, st);
+  // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
+  const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
+                  B * (S / kTrTokens) < INT32_MAX && aligned(x, 16) && sx_d % 8 == 0 &&
+                  (B == 1 || sx_b % 8 == 0) && aligned(scale, 16) && aligned(shift, 16) &&
+                  aligned(out, 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
+  if (tr) return dispatch_tr(a, st);
   if (V == 8) return vec ? dispatch<8, false>(a, st) : dispatch<8, true>(a, st);
   return vec ? dispatch<4, false>(a, st) : dispatch<4, true>(a, st);
 }

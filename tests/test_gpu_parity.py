@@ -128,6 +128,20 @@ def test_ln_hidden_sizes(ops, orc, D):
     run_ln(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
 
 
+@pytest.mark.parametrize("D", [8, 64, 520, 1000, 2240, 3072, 4096, 4104, 8192])
+@pytest.mark.parametrize("B,S", [(1, 8), (2, 40), (3, 1024)])
+def test_ln_transposed_storage(ops, orc, B, S, D):
+    """x stored [B, D, S] (tokens contiguous) and read through a transposed view, as the
+    permuted DiT activations are: same bits as the logical values give contiguously."""
+    g = torch.Generator().manual_seed(31 * D + S)
+    xt = rand_bf16((B, D, S), g, std=2.0, mean=-0.25).to(DEV)
+    x = xt.transpose(1, 2)
+    emb = rand_bf16((B, 6, D), g, std=0.1).to(DEV)
+    y = run_ln(ops, orc, x, emb[:, 5], emb[:, 0], 1e-6, what="transposed B=%d S=%d D=%d" % (B, S, D))
+    y2 = ops.ln_modulate(x.contiguous(), emb[:, 5], emb[:, 0], 1e-6)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("B,S", [(1, 1), (1, 37), (3, 1), (3, 37), (2, 1024)])
 def test_ln_rows(ops, orc, B, S):
     g = torch.Generator().manual_seed(100 * B + S)
