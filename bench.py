@@ -33,6 +33,43 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "µs/call + achieved HBM GB/s (% of peak), ln_modulate bf16 (1,4096,4096)"
 
+# HBM bytes per ln_modulate launch from rocprofv3 byte counters, valid only
+# while the kernel sources are the ones the counters were taken on
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ln_modulate_1x4096x4096_traffic.txt")
+TRAFFIC_SOURCES = ["modulate_ln_amd/csrc/ln_modulate.hip", "modulate_ln_amd/csrc/device_common.hpp"]
+
+
+def source_sha256(paths) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel,
+    each scaled by the same counter's reading for a plain copy of known size.
+    None when there is no record or the kernel changed since it was taken."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_RECORD):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    try:
+        if rec["source_sha256"] != source_sha256(TRAFFIC_SOURCES):
+            return None
+        copy_bytes = float(rec["copy_bytes_each_way"])
+        rd = float(rec["fetch_kib_per_dispatch"]) / float(rec["copy_fetch_kib_per_dispatch"]) * copy_bytes
+        wr = float(rec["write_kib_per_dispatch"]) / float(rec["copy_write_kib_per_dispatch"]) * copy_bytes
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+    return int(round(rd + wr))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -144,7 +181,7 @@ def main() -> int:
         "achieved_GBps": {"ln_modulate": round(lnm_gbps, 1), "residual_gate_add": round(rga_gbps, 1)},
         "roofline": {"bound": "hbm", "kernel": "ln_modulate", "achieved": round(lnm_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(lnm_gbps / PEAK_HBM_GBPS, 4),
-                     "algorithmic_bytes": lb, "traffic": None},
+                     "algorithmic_bytes": lb, "traffic": measured_traffic()},
     }
 
     # ---- a plain copy of the same size: the achievable streaming bandwidth ----
