@@ -331,6 +331,26 @@ int orc_residual_gate_add(const uint16_t* res, const uint16_t* gate, const uint1
 }
 
 /* ------------------------------------------------------------------ */
+/* residual_gate_add_ln_modulate: the gated residual update, then        */
+/* ln_modulate of the updated residual ("Fused Kernels" page, table      */
+/* "Normalization", scale_residual_norm_scale_shift: the norm + scale/   */
+/* shift with the preceding residual + gate * update folded in).  Both   */
+/* results are outputs: res_out = bf16(res + bf16(gate*upd)) and         */
+/* out = ln_modulate(res_out).  res, upd [B*S, D]; gate, scale, shift    */
+/* [B, D]; res_out, out [B*S, D].                                        */
+/* ------------------------------------------------------------------ */
+
+int orc_residual_gate_add_ln_modulate(const uint16_t* res, const uint16_t* gate, const uint16_t* upd,
+                                      int64_t B, int64_t S, int64_t D, const uint16_t* scale,
+                                      const uint16_t* shift, float eps, int mode, int V, int L,
+                                      uint16_t* res_out, uint16_t* out, double* mean_out,
+                                      double* rstd_out) {
+  int rc = orc_residual_gate_add(res, gate, upd, B, S, D, mode, res_out);
+  if (rc != ORC_OK) return rc;
+  return orc_ln_modulate(res_out, B, S, D, scale, shift, eps, mode, V, L, out, mean_out, rstd_out);
+}
+
+/* ------------------------------------------------------------------ */
 /* qk_head_layernorm: affine LayerNorm over each head row of Dh         */
 /* x [R, Dh]; w, b [Dh] or both NULL (no affine); out [R, Dh]           */
 /* One eager LayerNorm op, so one bf16 rounding at its output.          */

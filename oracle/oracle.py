@@ -83,6 +83,9 @@ def load_library(path: str):
     lib.orc_ln_modulate.argtypes = [u16p, i64, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, u16p, f64p, f64p]
     lib.orc_residual_gate_add.argtypes = [u16p, u16p, u16p, i64, i64, i64, ctypes.c_int, u16p]
+    lib.orc_residual_gate_add_ln_modulate.argtypes = [u16p, u16p, u16p, i64, i64, i64, u16p, u16p,
+                                                      ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_int, u16p, u16p, f64p, f64p]
     lib.orc_qk_head_layernorm.argtypes = [u16p, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, u16p]
     lib.orc_gelu_tanh_f64.argtypes = [ctypes.c_double]
@@ -197,6 +200,31 @@ def residual_gate_add(res, gate, upd, S: int, mode: int = FP32):
                                        _p(upd, ctypes.c_uint16), B, S, D, mode, _p(out, ctypes.c_uint16))
     _check(rc, "residual_gate_add")
     return out
+
+
+def residual_gate_add_ln_modulate(res, gate, upd, scale, shift, S: int, eps: float, mode: int,
+                                  V: int = 8, L: int = 64):
+    """res_out = bf16(res + bf16(gate*upd)), out = ln_modulate(res_out, scale, shift).
+
+    res/upd [B*S, D], gate/scale/shift [B, D] (bf16 bits).  Returns
+    (res_out bits, out bits, mean [B*S] float64, rstd [B*S] float64).
+    """
+    res, gate, upd, scale, shift = _u16(res), _u16(gate), _u16(upd), _u16(scale), _u16(shift)
+    R, D = res.shape
+    B = gate.shape[0]
+    if R != B * S or upd.shape != (R, D) or any(t.shape != (B, D) for t in (gate, scale, shift)):
+        raise ValueError("shape mismatch")
+    res_out = np.empty((R, D), dtype=np.uint16)
+    out = np.empty((R, D), dtype=np.uint16)
+    mean = np.empty(R, dtype=np.float64)
+    rstd = np.empty(R, dtype=np.float64)
+    rc = _load().orc_residual_gate_add_ln_modulate(
+        _p(res, ctypes.c_uint16), _p(gate, ctypes.c_uint16), _p(upd, ctypes.c_uint16), B, S, D,
+        _p(scale, ctypes.c_uint16), _p(shift, ctypes.c_uint16), eps, mode, V, L,
+        _p(res_out, ctypes.c_uint16), _p(out, ctypes.c_uint16), _p(mean, ctypes.c_double),
+        _p(rstd, ctypes.c_double))
+    _check(rc, "residual_gate_add_ln_modulate")
+    return res_out, out, mean, rstd
 
 
 def qk_head_layernorm(x, w, b, eps: float, mode: int, V: int = 8, L: int = 16):

@@ -33,6 +33,8 @@ MUTANTS = {
     "gelu_cubic_coeff": ("const double k1 = 0.044715;", "const double k1 = 0.0447;"),
     "gelu_sign": ("return z / (1.0 + exp(-2.0 * u));", "return z / (1.0 + exp(2.0 * u));"),
     "rne_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", "if (dropped >= 0x8000u) kept += 1u;"),
+    "fused_norms_old_residual": ("return orc_ln_modulate(res_out, B, S, D, scale, shift", "return orc_ln_modulate(res, B, S, D, scale, shift"),
+    "fused_skips_residual_update": ("int rc = orc_residual_gate_add(res, gate, upd, B, S, D, mode, res_out);", "int rc = orc_residual_gate_add(res, gate, upd, B, S, D, mode, res_out); memcpy(res_out, res, (size_t)(B * S * D) * 2);"),
     "bias_not_rounded": ("double z = rb64((double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]));", "double z = (double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]);"),
 }
 
@@ -53,6 +55,8 @@ FAST_PINS = [
     lambda o: P.test_residual_gate_add_equals_torch_eager(o, P.FP32),
     lambda o: P.test_qk_fp64_equals_torch_affine_layer_norm(o),
     lambda o: P.test_qk_fp32_within_one_ulp_of_fp64(o),
+    lambda o: P.test_fused_residual_worked_d4(o, P.FP32),
+    lambda o: P.test_fused_residual_equals_torch_eager_chain(o),
     lambda o: P.test_gelu_f64_vs_torch(o),
     lambda o: P.test_bias_gelu_rounds_after_bias(o),
 ]

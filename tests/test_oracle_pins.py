@@ -416,3 +416,87 @@ def test_fp32_mode_close_to_fp64_mode(orc, mode_pair):
         sig = 1 / r64
         assert np.all(np.abs(m32 - m64) <= 1e-5 * np.sqrt(m64 ** 2 + sig ** 2))
         assert np.all(np.abs(r32 - r64) <= 1e-5 * r64)
+
+
+# ---------------------------------------------------------------------------
+# residual_gate_add_ln_modulate: the gated residual update feeding ln_modulate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_fused_residual_worked_d4(orc, mode):
+    """Three inputs whose updated residual is [-3,-1,1,3] (exact in bf16): the normalized
+    output is the worked closed form of the plain ln_modulate (x / sqrt(5 + eps))."""
+    want = [[-1.34375, -0.447265625, 0.447265625, 1.34375]]
+    zero = bf([[0.0] * 4])
+    cases = [
+        (bf([[0.0] * 4]), bf([[2.0] * 4]), bf([[-1.5, -0.5, 0.5, 1.5]])),  # 0 + 2*u
+        (bf([[1.0] * 4]), bf([[1.0] * 4]), bf([[-4.0, -2.0, 0.0, 2.0]])),  # 1 + u
+        (bf([[-3.0, -1.0, 1.0, 3.0]]), zero, bf([[7.0, -7.0, 0.5, 9.0]])),  # gate 0: residual
+    ]
+    for res, gate, upd in cases:
+        r_out, out, mean, rstd = orc.residual_gate_add_ln_modulate(res, gate, upd, zero, zero, 1, 1e-6, mode,
+                                                                   V=4, L=64)
+        assert f32(r_out).tolist() == [[-3.0, -1.0, 1.0, 3.0]]
+        assert f32(out).tolist() == want
+        assert mean[0] == 0.0
+        assert abs(rstd[0] - 1 / math.sqrt(5 + 1e-6)) < 1e-7
+    # scale = 1 doubles it; gate = 0 with a -0 residual gives +0 in the new residual
+    res = bf([[-3.0, -1.0, 1.0, 3.0]])
+    r_out, out, _, _ = orc.residual_gate_add_ln_modulate(res, zero, bf([[1.0] * 4]), bf([[1.0] * 4]), zero, 1,
+                                                         1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[-2.6875, -0.89453125, 0.89453125, 2.6875]]
+    res = bf([[-0.0, 2.0, -2.0, 0.0]])
+    r_out, _, _, _ = orc.residual_gate_add_ln_modulate(res, zero, bf([[1.0] * 4]), zero, zero, 1, 1e-6, mode,
+                                                       V=4, L=64)
+    assert r_out.tolist() == [[0x0000, 0x4000, 0xC000, 0x0000]]
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+@pytest.mark.parametrize("D", [8, 2240])
+def test_fused_residual_constant_rows(orc, mode, D):
+    """residual c and update u with gate g such that c + g*u is constant: x_hat = +0, so out = +0
+    with scale = shift = 0, and the updated residual is that constant."""
+    res = bf([[1.0] * D, [-2.0] * D])
+    upd = bf([[3.0] * D, [0.5] * D])
+    gate = bf([[0.5] * D])
+    z = bf([[0.0] * D])
+    V = 8 if D % 8 == 0 else 4
+    r_out, out, mean, _ = orc.residual_gate_add_ln_modulate(res, gate, upd, z, z, 2, 1e-6, mode, V=V, L=64)
+    assert np.all(f32(r_out)[0] == 2.5) and np.all(f32(r_out)[1] == -1.75)
+    assert np.all(out == 0)
+    assert mean.tolist() == [2.5, -1.75]
+
+
+def test_fused_residual_equals_torch_eager_chain(orc):
+    """torch CPU eager is the reference for both outputs: the residual is two bf16 tensor ops;
+    with scale = shift = 0 the output is float64 layer_norm of that residual rounded once
+    (two-pass mode, up to values within 1e-12 of a bf16 midpoint); with real scale/shift,
+    the tail after the oracle's own fp32 statistics is the eager bf16 chain."""
+    g = torch.Generator().manual_seed(21)
+    B, S, D = 2, 24, 2240
+    res = torch.randn(B, S, D, generator=g).to(torch.bfloat16)
+    upd = (torch.randn(B, S, D, generator=g) * 3).to(torch.bfloat16)
+    gate = (torch.randn(B, D, generator=g) * 0.5).to(torch.bfloat16)
+    sc = (torch.randn(B, D, generator=g) * 0.1).to(torch.bfloat16)
+    sh = (torch.randn(B, D, generator=g) * 0.1).to(torch.bfloat16)
+    xn = res + gate[:, None, :] * upd
+    R = B * S
+    flat = lambda t: bits_of(t.reshape(R, D))  # noqa: E731
+    z = torch.zeros(B, D, dtype=torch.bfloat16)
+    r_out, out, _, _ = orc.residual_gate_add_ln_modulate(flat(res), bits_of(gate), flat(upd), bits_of(z),
+                                                         bits_of(z), S, 1e-6, FP64)
+    assert np.array_equal(r_out, flat(xn))
+    ref64 = torch.nn.functional.layer_norm(xn.double(), (D,), eps=float(np.float32(1e-6))).reshape(R, D).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+    assert diff.mean() < 1e-4
+    r_out, out, mean, rstd = orc.residual_gate_add_ln_modulate(flat(res), bits_of(gate), flat(upd), bits_of(sc),
+                                                               bits_of(sh), S, 1e-6, FP32)
+    assert np.array_equal(r_out, flat(xn))
+    xf = xn.reshape(R, D).float()
+    m = torch.from_numpy(mean.astype(np.float32))[:, None]
+    r = torch.from_numpy(rstd.astype(np.float32))[:, None]
+    xhat = ((xf - m) * r).to(torch.bfloat16).reshape(B, S, D)
+    eager = xhat * (1 + sc[:, None, :]) + sh[:, None, :]
+    assert np.array_equal(out, flat(eager))
