@@ -67,6 +67,7 @@ extern "C" {
 /* ops, for adaln_order_for */
 #define ADALN_OP_LN_MODULATE 1
 #define ADALN_OP_QK_HEAD_LAYERNORM 2
+#define ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE 3
 
 /*
  * ln_modulate -- out = LN(x) * (1 + scale) + shift, bf16 at every eager op.
@@ -123,6 +124,48 @@ int residual_gate_add_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b, int
                               int64_t sg_b, int64_t su_b, int64_t su_s, int dtype);
 
 /*
+ * residual_gate_add_ln_modulate -- the gated residual update, then
+ * ln_modulate of the updated residual, in one pass:
+ *   residual_out = bf16(residual + bf16(gate * update))
+ *   out          = ln_modulate(residual_out, scale, shift, eps)
+ * with the roundings and reduction order of the two unfused entry points,
+ * so both results are bit-identical to residual_gate_add followed by
+ * ln_modulate (the statistics use the ln_modulate order).
+ *
+ * Source: "Fused Kernels" page, table "Normalization"
+ * (scale_residual_norm_scale_shift: the norm + scale/shift with the
+ * preceding residual + gate * update folded in, bit-exact); the two parts
+ * are defined where residual_gate_add and ln_modulate cite.  In a DiT block
+ * it joins each gated residual add with the LayerNorm that reads its result.
+ *
+ *  residual [B,S,D], element (b,s,d) at residual + b*sr_b + s*sr_s + d.
+ *  gate     [B,D] with row stride sg_b.
+ *  update   [B,S,D], element (b,s,d) at update + b*su_b + s*su_s + d.
+ *  scale, shift   [B,D] with row strides sscale_b, sshift_b.
+ *  eps      added to the biased variance; must be finite and >= 0.
+ *  residual_out   [B,S,D] contiguous; may be exactly residual when that
+ *           input is contiguous.
+ *  out      [B,S,D] contiguous; may be exactly update when that input is
+ *           contiguous.  No other overlap between an output and any input
+ *           or the other output is accepted.
+ *  mean_out, rstd_out   optional statistics of the updated residual
+ *           ([B*S] fp32 each); NULL = skip.
+ *  D        % 4 == 0, 4 <= D <= 65536.  One launch for 16-byte-aligned rows
+ *           (8-byte when D % 8 != 0) with D <= 8192; otherwise the two
+ *           unfused kernels run back to back on the stream.
+ */
+int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b, int64_t sr_s,
+                                  const void* gate, int64_t sg_b, const void* update, int64_t su_b,
+                                  int64_t su_s, int64_t B, int64_t S, int64_t D, const void* scale,
+                                  int64_t sscale_b, const void* shift, int64_t sshift_b, float eps,
+                                  int dtype, void* residual_out, void* out, float* mean_out,
+                                  float* rstd_out, void* stream);
+
+int residual_gate_add_ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b,
+                                          int64_t sr_s, int64_t sg_b, int64_t su_b, int64_t su_s,
+                                          int64_t sscale_b, int64_t sshift_b, int dtype);
+
+/*
  * qk_head_layernorm -- per-head affine LayerNorm of q and k in one launch.
  *
  * Source: "Fused Kernels" page, table "Normalization" (qk_head_layernorm,
@@ -173,8 +216,8 @@ int bias_gelu_tanh_can_use(int64_t rows, int64_t width, int64_t sx_row, int dtyp
 /*
  * adaln_order_for -- the fixed fp32 reduction order the kernels use for a
  * row of D elements of op ADALN_OP_*: *V = elements per vector (8 when
- * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate, 16 for a
- * q/k head).  Pure host function.  Returns ADALN_OK or an error code.
+ * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate and the
+ * residual-fused ln_modulate, 16 for a q/k head).  Pure host function.  Returns ADALN_OK or an error code.
  */
 int adaln_order_for(int op, int64_t D, int* V, int* L);
 

@@ -2,6 +2,7 @@
 kernels (``libadaln.so``) and this thin torch binding.
 
     from modulate_ln_amd import ln_modulate, residual_gate_add, qk_head_layernorm, bias_gelu_tanh
+    from modulate_ln_amd import residual_gate_add_ln_modulate
 
 The binding only marshals arguments; torch provides device memory and
 streams.  Importing the package does not load the library; the first call
@@ -9,11 +10,18 @@ does, and fails loudly if it has not been built.
 """
 
 from ._native import AdalnError, order_for, status_str  # noqa: F401
-from .ops import bias_gelu_tanh, ln_modulate, qk_head_layernorm, residual_gate_add  # noqa: F401
+from .ops import (  # noqa: F401
+    bias_gelu_tanh,
+    ln_modulate,
+    qk_head_layernorm,
+    residual_gate_add,
+    residual_gate_add_ln_modulate,
+)
 
 __all__ = [
     "ln_modulate",
     "residual_gate_add",
+    "residual_gate_add_ln_modulate",
     "qk_head_layernorm",
     "bias_gelu_tanh",
     "order_for",

@@ -26,6 +26,7 @@ ERR_ARG = -9
 BF16 = 1
 OP_LN_MODULATE = 1
 OP_QK_HEAD_LAYERNORM = 2
+OP_RESIDUAL_GATE_ADD_LN_MODULATE = 3
 ABI_VERSION = 1
 
 # every symbol include/adaln.h declares
@@ -38,6 +39,8 @@ EXPORTS = (
     "qk_head_layernorm_can_use",
     "bias_gelu_tanh",
     "bias_gelu_tanh_can_use",
+    "residual_gate_add_ln_modulate",
+    "residual_gate_add_ln_modulate_can_use",
     "adaln_order_for",
     "adaln_status_str",
     "adaln_abi_version",
@@ -75,6 +78,10 @@ def lib():
     L.qk_head_layernorm_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.bias_gelu_tanh.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp]
     L.bias_gelu_tanh_can_use.argtypes = [i64, i64, i64, ci]
+    L.residual_gate_add_ln_modulate.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, i64, i64, i64,
+                                                vp, i64, vp, i64, f32, ci, vp, vp, vp, vp, vp]
+    L.residual_gate_add_ln_modulate_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                                        i64, ci]
     L.adaln_order_for.argtypes = [ci, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.adaln_status_str.argtypes = [ci]
     L.adaln_status_str.restype = ctypes.c_char_p

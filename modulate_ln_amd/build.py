@@ -28,6 +28,7 @@ HIP_SOURCES = [
     "residual_gate_add.hip",
     "qk_head_layernorm.hip",
     "bias_gelu_tanh.hip",
+    "residual_ln_modulate.hip",
 ]
 HOST_SOURCES = ["abi.cpp"]
 

@@ -10,9 +10,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace adaln {
 
 constexpr int kWave = 64;
+
+// Compute units of the current device (cached; 0 if the query fails).
+inline int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  A 32-bit word holds two consecutive bf16 elements: the

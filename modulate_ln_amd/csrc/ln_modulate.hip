@@ -20,11 +20,11 @@
 // Rows whose storage is not vector-aligned or not contiguous take the same
 // code with element-wise gathers; the order of arithmetic is identical, so
 // the result depends only on the logical values.
-#include <atomic>
 #include <utility>
 
 #include "device_common.hpp"
 #include "host_common.hpp"
+#include "ln_row.hpp"
 
 namespace adaln {
 namespace {
@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
   }
 }
 
+
 // ---------------------------------------------------------------------------
 // Fast path: contiguous, vector-aligned rows with D <= 8192.
 //
@@ -161,23 +162,6 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // the table's latency hides under them.  UNIF (D % (64*V) == 0): every lane
 // holds the same count and the merge tree needs no division.
 // ---------------------------------------------------------------------------
-template <int V, int K, int... E>
-__device__ __forceinline__ void push_f32(const float* xk, float& mean, float& m2,
-                                         std::integer_sequence<int, E...>) {
-  (welford_push<K * V + E + 1>(mean, m2, xk[E]), ...);
-}
-
-template <int V, bool UNIF, int... K>
-__device__ __forceinline__ void welford_f32(const float (*xf)[V], int nvec, int lane, float& mean,
-                                            float& m2, std::integer_sequence<int, K...>) {
-  (
-      [&] {
-        if (UNIF || K * kWave + lane < nvec)
-          push_f32<V, K>(xf[K], mean, m2, std::make_integer_sequence<int, V>{});
-      }(),
-      ...);
-}
-
 // Launch shape of the fast path, measured on MI355X (all variants give the
 // same bits).  Rows of 7-8 vectors per lane prefetch the next row into a
 // second buffer and re-widen x from bf16 when normalizing, to stay at three
@@ -191,136 +175,6 @@ struct TabShape {
   static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (NV <= 8 ? 3 : 2);
 };
 
-// bf16 -> fp32 widening the compiler may not merge with an earlier one:
-// re-widening a row from its packed form costs one VALU op per element but
-// spares the VGPRs an fp32 copy of the row would hold.
-__device__ __forceinline__ float lo_f32_again(uint32_t w) {
-  uint32_t r;
-  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
-  return __builtin_bit_cast(float, r);
-}
-__device__ __forceinline__ float hi_f32_again(uint32_t w) {
-  uint32_t r;
-  asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
-  return __builtin_bit_cast(float, r);
-}
-
-// The per-sample tables: bf16(1 + scale) and shift as fp32, float4-packed
-// [table][V/4][nvec] so a lane's reads for vector v are contiguous across
-// the wave.  Built cooperatively by the nthreads threads of a block.
-template <int V>
-__device__ __forceinline__ void build_tables(float4* tab, const uint16_t* sc, const uint16_t* sh,
-                                             int nvec, int tid, int nthreads) {
-  const int shift_off = (V / 4) * nvec;
-  for (int v = tid; v < nvec; v += nthreads) {
-    const Vec<V> sv = load_vec<V>(sc + v * V);
-    const Vec<V> hv = load_vec<V>(sh + v * V);
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
-      float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
-      round_pair(o0, o1);  // bf16(1 + scale)
-      round_pair(o2, o3);
-      tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
-      tab[shift_off + q * nvec + v] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
-                                                  lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
-    }
-  }
-}
-
-// One row, held by one wave as NV packed vectors per lane (lane l owns
-// vectors l, l + 64, ...): Welford, merge tree, statistics, then
-// normalize, modulate with the LDS tables and store (non-temporal).
-// kXf32: widen the row once and keep it in fp32 for both passes; otherwise
-// widen it for the reduction and again (opaque to the compiler, so no fp32
-// copy stays live) when normalizing.
-template <int V, int NV, bool UNIF, bool kXf32>
-__device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* tab, int nvec, int lane,
-                                              float Df, float eps, uint16_t* orow, float* mean_out,
-                                              float* rstd_out) {
-  const int shift_off = (V / 4) * nvec;
-  float xf[NV][V];
-#pragma unroll
-  for (int k = 0; k < NV; ++k)
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) {
-      xf[k][2 * i] = lo_f32(buf[k].w[i]);
-      xf[k][2 * i + 1] = hi_f32(buf[k].w[i]);
-    }
-  auto xval = [&](int k, int e) -> float {
-    if constexpr (kXf32) return xf[k][e];
-    return (e & 1) ? hi_f32_again(buf[k].w[e / 2]) : lo_f32_again(buf[k].w[e / 2]);
-  };
-  float mean = 0.0f, m2 = 0.0f;
-  welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
-  if constexpr (UNIF) {
-    const float c = (float)(NV * V);
-    merge_down_equal<1>(mean, m2, c);
-    merge_down_equal<2>(mean, m2, c);
-    merge_down_equal<4>(mean, m2, c);
-    merge_down_equal<8>(mean, m2, c);
-    merge_down_equal<16>(mean, m2, c);
-    merge_down_equal<32>(mean, m2, c);
-  } else {
-    float n = (float)((nvec / kWave + (lane < nvec % kWave ? 1 : 0)) * V);
-    merge_down<1>(mean, m2, n);
-    merge_down<2>(mean, m2, n);
-    merge_down<4>(mean, m2, n);
-    merge_down<8>(mean, m2, n);
-    merge_down<16>(mean, m2, n);
-    merge_down<32>(mean, m2, n);
-  }
-  mean = bcast_lane0(mean);
-  m2 = bcast_lane0(m2);
-  const float rstd = finalize_rstd(m2, Df, eps);
-  if (lane == 0) {
-    if (mean_out) *mean_out = mean;
-    if (rstd_out) *rstd_out = rstd;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // table values for step k are read one step ahead of their use
-  float4 ot[V / 4], ht[V / 4];
-  auto read_tab = [&](int k) {
-    const int v = k * kWave + lane;
-    const int vc = (UNIF || v < nvec) ? v : nvec - 1;
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      ot[q] = tab[q * nvec + vc];
-      ht[q] = tab[shift_off + q * nvec + vc];
-    }
-  };
-  read_tab(0);
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    float4 oc[V / 4], hc[V / 4];
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      oc[q] = ot[q];
-      hc[q] = ht[q];
-    }
-    if (k + 1 < NV) read_tab(k + 1);
-    const int v = k * kWave + lane;
-    if (UNIF || v < nvec) {
-      Vec<V> o;
-#pragma unroll
-      for (int q = 0; q < V / 4; ++q) {
-        float n0 = (xval(k, 4 * q) - mean) * rstd, n1 = (xval(k, 4 * q + 1) - mean) * rstd;
-        float n2 = (xval(k, 4 * q + 2) - mean) * rstd, n3 = (xval(k, 4 * q + 3) - mean) * rstd;
-        round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
-        round_pair(n2, n3);
-        float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
-        round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
-        round_pair(y2, y3);
-        o.w[2 * q] = pack_bf16(y0 + hc[q].x, y1 + hc[q].y);  // bf16(y + shift)
-        o.w[2 * q + 1] = pack_bf16(y2 + hc[q].z, y3 + hc[q].w);
-      }
-      store_vec_nt<V>(orow + v * V, o);
-    }
-    // keep two steps' table values live at a time (the scheduler would
-    // otherwise hoist every LDS read and halve the occupancy)
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
 
 template <int V, int NV, bool UNIF>
 __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
@@ -552,19 +406,6 @@ template <int V, bool GATHER>
 int launch_stream(const LnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((ln_modulate_stream<V, GATHER>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
-}
-
-// Compute units of the current device (cached; 0 if the query fails).
-inline int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables

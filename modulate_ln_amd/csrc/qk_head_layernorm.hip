@@ -15,7 +15,6 @@
 // side's weight and bias in fp32 VGPRs for the whole launch, and each
 // 16-lane group loads HP heads (non-temporal, unguarded) before reducing
 // them, so several heads per lane are in flight.
-#include <atomic>
 #include <utility>
 
 #include "device_common.hpp"
@@ -216,19 +215,6 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
       }
     }
   }
-}
-
-// Compute units of the current device (cached; 0 if the query fails).
-inline int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 constexpr int kHeadsBlocksPerCu = 4;

@@ -12,7 +12,6 @@
 // keeps that chunk of the current sample's gate in VGPRs, and issues all
 // 2*U residual/update loads of a row (non-temporal, unguarded) before it
 // computes.  Other layouts take a row-per-wave or element-wise kernel.
-#include <atomic>
 
 #include "device_common.hpp"
 #include "host_common.hpp"
@@ -134,19 +133,6 @@ __global__ __launch_bounds__(256) void rga_rows_scalar(RgaArgs a) {
 inline unsigned grid_for(int64_t R) {
   int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
   return (unsigned)std::min(blocks, kMaxBlocks);
-}
-
-// Compute units of the current device (cached; 0 if the query fails).
-inline int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 // grid size of the column-chunk kernel (blocks per compute unit in total),

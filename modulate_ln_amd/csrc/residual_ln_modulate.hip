@@ -1,0 +1,321 @@
+// residual_gate_add_ln_modulate: the gated residual update followed by
+// ln_modulate of the updated residual, in one pass, on gfx950.
+//
+// Operation: "Fused Kernels" page, table "Normalization"
+// (scale_residual_norm_scale_shift: the norm + scale/shift with the
+// preceding residual + gate * update folded in).  Both results are written:
+//   res_out = bf16(residual + bf16(gate * update))      (two eager ops)
+//   out     = bf16 chain of LN(res_out) * (1 + scale) + shift
+// with exactly the roundings and the Welford order of the two unfused ops,
+// so the results are bit-identical to residual_gate_add then ln_modulate.
+//
+// Design: the tabled ln_modulate kernel with a gate-add prologue.  A block
+// serves one batch sample and holds three fp32 tables in LDS: bf16(1 +
+// scale), shift and gate.  Each wave streams rows: it loads the row of
+// residual and of update (non-temporal 16-byte loads, issued before the
+// tables are built for the first row), forms the new residual in packed
+// bf16, stores it, and hands the packed row to the same per-row routine as
+// ln_modulate.  Per element: 2 reads + 2 writes of bf16 (8 bytes), against
+// 6 + 4 for the two unfused ops, one launch instead of two.
+// Other layouts (unaligned rows, rows over 8192) run the two unfused entry
+// points back to back: same bits, two launches.
+
+#include "device_common.hpp"
+#include "host_common.hpp"
+#include "ln_row.hpp"
+
+// the unfused entry points, for the layouts the fused kernel does not take
+extern "C" int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_s, const void* gate,
+                                 int64_t sg_b, const void* update, int64_t su_b, int64_t su_s,
+                                 int64_t B, int64_t S, int64_t D, int dtype, void* out, void* stream);
+extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                           int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
+                           const void* shift, int64_t sshift_b, float eps, int dtype, void* out,
+                           float* mean_out, float* rstd_out, void* stream);
+
+namespace adaln {
+namespace {
+
+struct FusedArgs {
+  const uint16_t* res;
+  int64_t sr_b, sr_s;
+  const uint16_t* gate;
+  int64_t sg_b;
+  const uint16_t* upd;
+  int64_t su_b, su_s;
+  const uint16_t* scale;
+  int64_t ssc_b;
+  const uint16_t* shift;
+  int64_t ssh_b;
+  float eps;
+  uint16_t* res_out;
+  uint16_t* out;
+  float* mean_out;
+  float* rstd_out;
+  int64_t S, D, R;
+};
+
+// Launch shape, measured on MI355X (every choice gives the same bits).
+// Rows of up to 6 vectors per lane prefetch the next row's residual and
+// update into a second pair of buffers; longer rows do not (the VGPRs would
+// cut the waves per SIMD).  Blocks per compute unit: 4, or as many as the
+// three tables (12*D bytes of LDS per block) allow.
+template <int NV>
+struct FusedShape {
+  static constexpr bool kPrefetch = NV <= 6;
+  static constexpr bool kXf32 = NV <= 4;
+  static constexpr int kBlocksPerCu = 4;
+};
+
+template <int V, int NV, bool UNIF>
+__global__ __launch_bounds__(256) void rga_ln_modulate_tab(FusedArgs a, int bpb) {
+  constexpr bool kPrefetch = FusedShape<NV>::kPrefetch;
+  constexpr bool kXf32 = FusedShape<NV>::kXf32;
+  extern __shared__ float4 tab[];  // [3][V/4][nvec] float4: bf16(1+scale), shift, gate
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int D = (int)a.D;
+  const int nvec = D / V;
+  const int S = (int)a.S;
+  const int b = blockIdx.x / bpb;
+  const int j = blockIdx.x - b * bpb;
+  const int row_step = 4 * bpb;
+  const int gate_off = 2 * (V / 4) * nvec;
+  int s = 4 * j + wave;
+
+  const uint16_t* rb = a.res + (int64_t)b * a.sr_b;
+  const uint16_t* ub = a.upd + (int64_t)b * a.su_b;
+  auto load_rows = [&](Vec<V>* rbuf, Vec<V>* ubuf, int ss) {
+    const uint16_t* rr = rb + (int64_t)ss * a.sr_s;
+    const uint16_t* ur = ub + (int64_t)ss * a.su_s;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * kWave + lane;
+      const int vc = (UNIF || v < nvec) ? v : nvec - 1;
+      rbuf[k] = load_vec_nt<V>(rr + vc * V);
+      ubuf[k] = load_vec_nt<V>(ur + vc * V);
+    }
+  };
+
+  Vec<V> rA[NV], uA[NV];
+  Vec<V> rB[kPrefetch ? NV : 1], uB[kPrefetch ? NV : 1];
+  if (s < S) load_rows(rA, uA, s);
+  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
+                  threadIdx.x, 256);
+  build_gate_table<V>(tab, a.gate + (int64_t)b * a.sg_b, nvec, threadIdx.x, 256);
+  __syncthreads();
+  if (s >= S) return;
+
+  const float Df = (float)D;
+  auto process = [&](const Vec<V>* rbuf, const Vec<V>* ubuf, int ss) {
+    const int64_t r = (int64_t)b * S + ss;
+    uint16_t* xrow = a.res_out + r * D;
+    Vec<V> xn[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * kWave + lane;
+      const int vc = (UNIF || v < nvec) ? v : nvec - 1;
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) {
+        const float4 g = tab[gate_off + q * nvec + vc];
+        const uint32_t u0 = ubuf[k].w[2 * q], u1 = ubuf[k].w[2 * q + 1];
+        const uint32_t r0 = rbuf[k].w[2 * q], r1 = rbuf[k].w[2 * q + 1];
+        float t0 = g.x * lo_f32(u0), t1 = g.y * hi_f32(u0);
+        float t2 = g.z * lo_f32(u1), t3 = g.w * hi_f32(u1);
+        round_pair(t0, t1);  // bf16(gate * update)
+        round_pair(t2, t3);
+        xn[k].w[2 * q] = pack_bf16(lo_f32(r0) + t0, hi_f32(r0) + t1);  // bf16(residual + t)
+        xn[k].w[2 * q + 1] = pack_bf16(lo_f32(r1) + t2, hi_f32(r1) + t3);
+      }
+      if (UNIF || v < nvec) store_vec_nt<V>(xrow + v * V, xn[k]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    normalize_row<V, NV, UNIF, kXf32>(xn, tab, nvec, lane, Df, a.eps, a.out + r * D,
+                                      a.mean_out ? a.mean_out + r : nullptr,
+                                      a.rstd_out ? a.rstd_out + r : nullptr);
+  };
+
+  if constexpr (kPrefetch) {
+    while (true) {
+      int s1 = s + row_step;
+      if (s1 < S) load_rows(rB, uB, s1);
+      process(rA, uA, s);
+      if (s1 >= S) break;
+      s = s1;
+      s1 = s + row_step;
+      if (s1 < S) load_rows(rA, uA, s1);
+      process(rB, uB, s);
+      if (s1 >= S) break;
+      s = s1;
+    }
+  } else {
+    while (true) {
+      process(rA, uA, s);
+      s += row_step;
+      if (s >= S) break;
+      load_rows(rA, uA, s);
+    }
+  }
+}
+
+constexpr int kFusedMaxD = 8192;  // 96 KiB of LDS tables
+constexpr int64_t kLdsPerCu = 160 * 1024;
+
+template <int V, int NV, bool UNIF>
+int launch_fused(const FusedArgs& a, hipStream_t st) {
+  const int64_t B = a.R / a.S;
+  const size_t lds = (size_t)3 * a.D * sizeof(float);
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(FusedShape<NV>::kBlocksPerCu,
+                                                                kLdsPerCu / (int64_t)lds));
+  const int cus = cu_count();
+  const int64_t target = per_cu * (cus > 0 ? cus : 256);
+  int64_t bpb = (target + B - 1) / B;
+  bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
+  hipLaunchKernelGGL((rga_ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)(B * bpb)), dim3(256), lds,
+                     st, a, (int)bpb);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <int V>
+int dispatch_fused(const FusedArgs& a, hipStream_t st) {
+  const int64_t nvec = a.D / V;
+  const int64_t nv = (nvec + kWave - 1) / kWave;
+  const bool unif = nvec % kWave == 0;
+#define ADALN_FUSED_CASE(N) \
+  if (nv == N) return unif ? launch_fused<V, N, true>(a, st) : launch_fused<V, N, false>(a, st);
+  ADALN_FUSED_CASE(1)
+  ADALN_FUSED_CASE(2)
+  ADALN_FUSED_CASE(3)
+  ADALN_FUSED_CASE(4)
+  ADALN_FUSED_CASE(5)
+  ADALN_FUSED_CASE(6)
+  ADALN_FUSED_CASE(7)
+  ADALN_FUSED_CASE(8)
+  ADALN_FUSED_CASE(9)
+  ADALN_FUSED_CASE(10)
+  ADALN_FUSED_CASE(11)
+  ADALN_FUSED_CASE(12)
+  ADALN_FUSED_CASE(13)
+  ADALN_FUSED_CASE(14)
+  ADALN_FUSED_CASE(15)
+  ADALN_FUSED_CASE(16)
+#undef ADALN_FUSED_CASE
+  return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
+}
+
+}  // namespace
+
+static int fused_check_shape(int64_t B, int64_t S, int64_t D, int64_t sr_b, int64_t sr_s,
+                             int64_t sg_b, int64_t su_b, int64_t su_s, int64_t sscale_b,
+                             int64_t sshift_b, int dtype) {
+  if (dtype != ADALN_BF16) return ADALN_ERR_DTYPE;
+  if (B < 0 || S < 0 || D < 4 || D % 4 != 0) return ADALN_ERR_SHAPE;
+  if (D > 65536) return ADALN_ERR_TOO_LARGE;
+  if (sr_b < 0 || sr_s < 0 || sg_b < 0 || su_b < 0 || su_s < 0 || sscale_b < 0 || sshift_b < 0)
+    return ADALN_ERR_STRIDE;
+  int64_t R, RD;
+  if (!mul_ok(B, S, &R) || !mul_ok(R, D, &RD)) return ADALN_ERR_TOO_LARGE;
+  if (!extent_ok({{B, sr_b}, {S, sr_s}, {D, 1}}) || !extent_ok({{B, su_b}, {S, su_s}, {D, 1}}) ||
+      !extent_ok({{B, sg_b}, {D, 1}}) || !extent_ok({{B, sscale_b}, {D, 1}}) ||
+      !extent_ok({{B, sshift_b}, {D, 1}}))
+    return ADALN_ERR_TOO_LARGE;
+  return ADALN_OK;
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int residual_gate_add_ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b,
+                                                     int64_t sr_s, int64_t sg_b, int64_t su_b,
+                                                     int64_t su_s, int64_t sscale_b,
+                                                     int64_t sshift_b, int dtype) {
+  return fused_check_shape(B, S, D, sr_b, sr_s, sg_b, su_b, su_s, sscale_b, sshift_b, dtype) ==
+         ADALN_OK;
+}
+
+extern "C" int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b, int64_t sr_s,
+                                             const void* gate, int64_t sg_b, const void* update,
+                                             int64_t su_b, int64_t su_s, int64_t B, int64_t S,
+                                             int64_t D, const void* scale, int64_t sscale_b,
+                                             const void* shift, int64_t sshift_b, float eps,
+                                             int dtype, void* residual_out, void* out,
+                                             float* mean_out, float* rstd_out, void* stream) {
+  int rc = fused_check_shape(B, S, D, sr_b, sr_s, sg_b, su_b, su_s, sscale_b, sshift_b, dtype);
+  if (rc != ADALN_OK) return rc;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return ADALN_ERR_ARG;  // also rejects NaN
+  const int64_t R = B * S;
+  if (R == 0) return ADALN_OK;
+  if (!residual || !gate || !update || !scale || !shift || !residual_out || !out)
+    return ADALN_ERR_NULL;
+  if (!aligned(residual, 2) || !aligned(gate, 2) || !aligned(update, 2) || !aligned(scale, 2) ||
+      !aligned(shift, 2) || !aligned(residual_out, 2) || !aligned(out, 2) ||
+      !aligned(mean_out, 4) || !aligned(rstd_out, 4))
+    return ADALN_ERR_ALIGN;
+
+  // overlap rules: residual_out may be exactly a contiguous residual, out
+  // exactly a contiguous update; nothing else may overlap an output
+  const Span sro = span_of(residual_out, {{R * D, 1}});
+  const Span so = span_of(out, {{R * D, 1}});
+  const Span sres = span_of(residual, {{B, sr_b}, {S, sr_s}, {D, 1}});
+  const Span supd = span_of(update, {{B, su_b}, {S, su_s}, {D, 1}});
+  const Span sg = span_of(gate, {{B, sg_b}, {D, 1}});
+  const Span ssc = span_of(scale, {{B, sscale_b}, {D, 1}});
+  const Span ssh = span_of(shift, {{B, sshift_b}, {D, 1}});
+  const Span sm = mean_out ? Span{(uintptr_t)mean_out, (uintptr_t)(mean_out + R)} : Span{};
+  const Span sr = rstd_out ? Span{(uintptr_t)rstd_out, (uintptr_t)(rstd_out + R)} : Span{};
+  auto contig = [&](int64_t sb, int64_t ss) {
+    return (S == 1 || ss == D) && (B == 1 || sb == S * D);
+  };
+  if (overlaps(sro, sres) && !(residual_out == residual && contig(sr_b, sr_s))) return ADALN_ERR_ALIAS;
+  if (overlaps(so, supd) && !(out == update && contig(su_b, su_s))) return ADALN_ERR_ALIAS;
+  for (const Span* t : {&supd, &sg, &ssc, &ssh, &so, &sm, &sr})
+    if (overlaps(sro, *t)) return ADALN_ERR_ALIAS;
+  for (const Span* t : {&sres, &sg, &ssc, &ssh, &sm, &sr})
+    if (overlaps(so, *t)) return ADALN_ERR_ALIAS;
+  for (const Span* t : {&sres, &supd, &sg, &ssc, &ssh})
+    if (overlaps(sm, *t) || overlaps(sr, *t)) return ADALN_ERR_ALIAS;
+  if (overlaps(sm, sr)) return ADALN_ERR_ALIAS;
+
+  int V = 0;
+  order_for(ADALN_OP_LN_MODULATE, D, &V, nullptr);
+  const uintptr_t vb = (uintptr_t)(2 * V);
+  auto stride_ok = [&](int64_t n, int64_t st) { return n <= 1 || ((uintptr_t)st * 2u) % vb == 0; };
+  const bool fused = D <= kFusedMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
+                     B <= INT32_MAX && aligned(residual, vb) && aligned(update, vb) &&
+                     aligned(gate, vb) && aligned(scale, vb) && aligned(shift, vb) &&
+                     aligned(residual_out, vb) && aligned(out, vb) && stride_ok(B, sr_b) &&
+                     stride_ok(S, sr_s) && stride_ok(B, su_b) && stride_ok(S, su_s) &&
+                     stride_ok(B, sg_b) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
+  hipStream_t st = (hipStream_t)stream;
+  if (!fused) {
+    rc = ::residual_gate_add(residual, sr_b, sr_s, gate, sg_b, update, su_b, su_s, B, S, D, dtype,
+                             residual_out, stream);
+    if (rc != ADALN_OK) return rc;
+    return ::ln_modulate(residual_out, B, S, D, S * D, D, 1, scale, sscale_b, shift, sshift_b, eps,
+                         dtype, out, mean_out, rstd_out, stream);
+  }
+
+  FusedArgs a;
+  a.res = (const uint16_t*)residual;
+  a.sr_b = sr_b;
+  a.sr_s = sr_s;
+  a.gate = (const uint16_t*)gate;
+  a.sg_b = sg_b;
+  a.upd = (const uint16_t*)update;
+  a.su_b = su_b;
+  a.su_s = su_s;
+  a.scale = (const uint16_t*)scale;
+  a.ssc_b = sscale_b;
+  a.shift = (const uint16_t*)shift;
+  a.ssh_b = sshift_b;
+  a.eps = eps;
+  a.res_out = (uint16_t*)residual_out;
+  a.out = (uint16_t*)out;
+  a.mean_out = mean_out;
+  a.rstd_out = rstd_out;
+  a.S = S;
+  a.D = D;
+  a.R = R;
+  return V == 8 ? dispatch_fused<8>(a, st) : dispatch_fused<4>(a, st);
+}

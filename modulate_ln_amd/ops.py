@@ -118,6 +118,51 @@ def residual_gate_add(residual: torch.Tensor, gate: torch.Tensor, update: torch.
     return call if prepare else call()
 
 
+def residual_gate_add_ln_modulate(residual: torch.Tensor, gate: torch.Tensor, update: torch.Tensor,
+                                  scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
+                                  residual_out: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                                  mean_out: torch.Tensor | None = None, rstd_out: torch.Tensor | None = None,
+                                  stream=None, prepare: bool = False):
+    """(new residual, LN(new residual) * (1 + scale) + shift) with new residual =
+    residual + gate * update, every eager bf16 rounding kept; one pass over the rows.
+
+    residual/update [B,S,D] (unit stride along D), gate/scale/shift [B,D] or [B,1,D].
+    residual_out may be residual itself and out may be update itself when contiguous."""
+    for name, t in (("residual", residual), ("gate", gate), ("update", update), ("scale", scale),
+                    ("shift", shift)):
+        _require(t, name)
+    if residual.dim() != 3 or update.shape != residual.shape:
+        raise ValueError("residual and update must both be [B,S,D]")
+    B, S, D = residual.shape
+    gate, sg = _rows_view(gate, B, D, "gate")
+    scale, ssc = _rows_view(scale, B, D, "scale")
+    shift, ssh = _rows_view(shift, B, D, "shift")
+    for name, t in (("residual", residual), ("update", update)):
+        if D > 1 and t.stride(2) != 1:
+            raise ValueError("%s must have unit stride along the hidden dim" % name)
+    if residual_out is None:
+        residual_out = torch.empty((B, S, D), dtype=torch.bfloat16, device=residual.device)
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=residual.device)
+    for name, t in (("residual_out", residual_out), ("out", out)):
+        _require(t, name)
+        if tuple(t.shape) != (B, S, D) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous [B,S,D] tensor" % name)
+    for name, t in (("mean_out", mean_out), ("rstd_out", rstd_out)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * S or not t.is_contiguous()
+                              or t.device != residual.device):
+            raise ValueError("%s must be a contiguous float32 tensor of B*S elements on residual's device" % name)
+    st = _stream_handle(residual, stream)
+    call = Prepared("residual_gate_add_ln_modulate", N.lib().residual_gate_add_ln_modulate, (
+        residual.data_ptr(), residual.stride(0), residual.stride(1), gate.data_ptr(), sg,
+        update.data_ptr(), update.stride(0), update.stride(1), B, S, D,
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16,
+        residual_out.data_ptr(), out.data_ptr(),
+        mean_out.data_ptr() if mean_out is not None else None,
+        rstd_out.data_ptr() if rstd_out is not None else None, st), (residual_out, out))
+    return call if prepare else call()
+
+
 def qk_head_layernorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None = None,
                       bq: torch.Tensor | None = None, wk: torch.Tensor | None = None,
                       bk: torch.Tensor | None = None, eps: float = 1e-6, *,

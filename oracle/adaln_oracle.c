@@ -48,6 +48,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_FP64_TWO_PASS 0
 #define ORC_FP32_FIXED 1
@@ -417,6 +420,24 @@ int orc_bias_gelu_tanh(const uint16_t* x, int64_t rows, int64_t width, const uin
     }
   }
   return ORC_OK;
+}
+
+/* OpenMP threads the row loops use (rows are independent: results do not
+   depend on the thread count). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 int orc_abi_version(void) { return 1; }

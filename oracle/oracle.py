@@ -88,6 +88,10 @@ def load_library(path: str):
                                                       ctypes.c_int, u16p, u16p, f64p, f64p]
     lib.orc_qk_head_layernorm.argtypes = [u16p, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, u16p]
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = None
+    lib.orc_get_threads.argtypes = []
+    lib.orc_get_threads.restype = ctypes.c_int
     lib.orc_gelu_tanh_f64.argtypes = [ctypes.c_double]
     lib.orc_gelu_tanh_f64.restype = ctypes.c_double
     lib.orc_bias_gelu_tanh.argtypes = [u16p, i64, i64, u16p, u16p, f64p]
@@ -259,3 +263,12 @@ def bias_gelu_tanh(x, bias):
                                     _p(out, ctypes.c_uint16), _p(val, ctypes.c_double))
     _check(rc, "bias_gelu_tanh")
     return out, val
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the row loops (results are independent of it)."""
+    _load().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().orc_get_threads())

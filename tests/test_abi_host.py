@@ -58,6 +58,7 @@ def test_version_and_status_strings(L):
 def test_order_for(D, V):
     assert N.order_for(N.OP_LN_MODULATE, D) == (V, 64)
     assert N.order_for(N.OP_QK_HEAD_LAYERNORM, D) == (V, 16)
+    assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D) == (V, 64)
 
 
 @pytest.mark.parametrize("D", [0, -4, 6, 2242])
@@ -180,3 +181,48 @@ def test_bias_gelu_rejections(L):
     assert bg(out=P1 - 2) == N.ERR_ALIAS
     assert bg(out=P0, sx=128) == N.ERR_ALIAS
     assert bg(x=None, bias=None, out=None, rows=0) == N.OK
+
+
+def test_fused_residual_can_use(L):
+    ok = lambda *a: L.residual_gate_add_ln_modulate_can_use(*a, N.BF16)  # noqa: E731
+    sq = 4096 * 4096
+    assert ok(1, 4096, 4096, sq, 4096, 4096, sq, 4096, 4096, 4096)
+    assert ok(4, 4096, 3072, 4096 * 3072, 3072, 6 * 3072, 4096 * 3072, 3072, 6 * 3072, 6 * 3072)
+    assert ok(0, 0, 4, 0, 0, 0, 0, 0, 0, 0)
+    assert ok(1, 1, 65536, 0, 65536, 0, 0, 65536, 0, 0)
+    assert not ok(1, 1, 65540, 0, 65540, 0, 0, 65540, 0, 0)
+    assert not ok(1, 1, 6, 0, 6, 0, 0, 6, 0, 0)
+    assert not ok(1, 2, 8, 16, 8, 8, 16, 8, -8, 8)
+    assert not L.residual_gate_add_ln_modulate_can_use(1, 1, 8, 8, 8, 8, 8, 8, 8, 8, 0)
+
+
+def test_fused_residual_rejections(L):
+    P5, P6, P7 = 0x60000000, 0x70000000, 0x80000000
+
+    def fz(res=P0, gate=P1, upd=P2, scale=P3, shift=P4, ro=P5, out=P6, mean=None, rstd=None, B=2, S=3, D=8,
+           eps=1e-6, dtype=N.BF16, sr=(24, 8), su=(24, 8), sg=8, ssc=8, ssh=8):
+        return L.residual_gate_add_ln_modulate(res, sr[0], sr[1], gate, sg, upd, su[0], su[1], B, S, D, scale,
+                                               ssc, shift, ssh, eps, dtype, ro, out, mean, rstd, None)
+
+    assert fz(dtype=2) == N.ERR_DTYPE
+    assert fz(D=6) == N.ERR_SHAPE
+    assert fz(D=65540) == N.ERR_TOO_LARGE
+    assert fz(su=(24, -8)) == N.ERR_STRIDE
+    assert fz(eps=float("nan")) == N.ERR_ARG
+    for k in ("res", "gate", "upd", "scale", "shift", "ro", "out"):
+        assert fz(**{k: None}) == N.ERR_NULL, k
+    assert fz(upd=P2 + 1) == N.ERR_ALIGN
+    assert fz(rstd=P7 + 2) == N.ERR_ALIGN
+    # allowed: residual_out exactly residual, out exactly update (both contiguous)
+    # rejected: any other overlap
+    assert fz(ro=P0 + 2) == N.ERR_ALIAS
+    assert fz(ro=P0, sr=(48, 16)) == N.ERR_ALIAS  # residual not contiguous
+    assert fz(out=P2, su=(48, 16)) == N.ERR_ALIAS  # update not contiguous
+    assert fz(ro=P2) == N.ERR_ALIAS  # residual_out over update
+    assert fz(out=P0) == N.ERR_ALIAS  # out over residual
+    assert fz(out=P5 + 16) == N.ERR_ALIAS  # the two outputs overlap
+    assert fz(ro=P1) == N.ERR_ALIAS  # residual_out over gate
+    assert fz(out=P3 - 16) == N.ERR_ALIAS  # out tail over scale
+    assert fz(mean=P6 + 8) == N.ERR_ALIAS  # stats over out
+    assert fz(mean=P7, rstd=P7 + 8) == N.ERR_ALIAS
+    assert fz(res=None, gate=None, upd=None, scale=None, shift=None, ro=None, out=None, S=0) == N.OK
