@@ -262,6 +262,27 @@ int orc_layernorm_stats(const uint16_t* x, int64_t R, int64_t D, float eps, int 
 }
 
 /* ------------------------------------------------------------------ */
+/* The adaLN modulate tail shared by the LayerNorm and RMSNorm chains:  */
+/* given the normalized value n (before its rounding), x_hat = bf16(n), */
+/* one_plus = bf16(1 + scale), y = bf16(x_hat * one_plus),              */
+/* out = bf16(y + shift) -- one rounding per eager op.                  */
+/* ------------------------------------------------------------------ */
+
+static uint16_t modulate_tail_f32(float n, uint16_t sc, uint16_t sh) {
+  float xhat = rb(n);
+  float one_plus = rb(1.0f + orc_f32_from_bf16(sc));
+  float y = rb(xhat * one_plus);
+  return orc_bf16_from_f32(y + orc_f32_from_bf16(sh));
+}
+
+static uint16_t modulate_tail_f64(double n, uint16_t sc, uint16_t sh) {
+  double xhat = rb64(n);
+  double one_plus = rb64(1.0 + (double)orc_f32_from_bf16(sc));
+  double y = rb64(xhat * one_plus);
+  return orc_bf16_from_f64(y + (double)orc_f32_from_bf16(sh));
+}
+
+/* ------------------------------------------------------------------ */
 /* ln_modulate: LN(x) * (1 + scale) + shift, per-sample scale/shift     */
 /* x [B*S, D] logical row-major; scale, shift [B, D]; out [B*S, D]      */
 /* ------------------------------------------------------------------ */
@@ -282,23 +303,14 @@ int orc_ln_modulate(const uint16_t* x, int64_t B, int64_t S, int64_t D, const ui
     if (mode == ORC_FP32_FIXED) {
       float mean, rstd;
       row_stats_fp32(xr, D, eps, V, L, &mean, &rstd);
-      for (int64_t j = 0; j < D; ++j) {
-        float xhat = rb((orc_f32_from_bf16(xr[j]) - mean) * rstd);
-        float one_plus = rb(1.0f + orc_f32_from_bf16(sc[j]));
-        float y = rb(xhat * one_plus);
-        o[j] = orc_bf16_from_f32(y + orc_f32_from_bf16(sh[j]));
-      }
+      for (int64_t j = 0; j < D; ++j) o[j] = modulate_tail_f32((orc_f32_from_bf16(xr[j]) - mean) * rstd, sc[j], sh[j]);
       if (mean_out) mean_out[r] = mean;
       if (rstd_out) rstd_out[r] = rstd;
     } else {
       double mean, rstd;
       row_stats_fp64(xr, D, eps, &mean, &rstd);
-      for (int64_t j = 0; j < D; ++j) {
-        double xhat = rb64(((double)orc_f32_from_bf16(xr[j]) - mean) * rstd);
-        double one_plus = rb64(1.0 + (double)orc_f32_from_bf16(sc[j]));
-        double y = rb64(xhat * one_plus);
-        o[j] = orc_bf16_from_f64(y + (double)orc_f32_from_bf16(sh[j]));
-      }
+      for (int64_t j = 0; j < D; ++j)
+        o[j] = modulate_tail_f64(((double)orc_f32_from_bf16(xr[j]) - mean) * rstd, sc[j], sh[j]);
       if (mean_out) mean_out[r] = mean;
       if (rstd_out) rstd_out[r] = rstd;
     }
@@ -327,6 +339,109 @@ int orc_residual_gate_add(const uint16_t* res, const uint16_t* gate, const uint1
       } else {
         double t = rb64((double)orc_f32_from_bf16(g[j]) * (double)orc_f32_from_bf16(upd[i]));
         out[i] = orc_bf16_from_f64((double)orc_f32_from_bf16(res[i]) + t);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* RMSNorm statistics.  The pages' RMSNorm fusions ("Fused Kernels"     */
+/* page, table "Normalization": rmsnorm_scale_shift, qk_rmsnorm_native; */
+/* the request-gated fusion table: rms_norm(x) * (1 + scale) + shift)   */
+/* normalize by the root mean square: x_hat = x / sqrt(mean(x^2) + eps) */
+/* with no mean subtraction.                                            */
+/*   fp64: ss = sum of x^2 in double (sequential), rinv =               */
+/*         1/sqrt(ss/D + eps).                                          */
+/*   fp32(V, L): lane l owns vectors l, l+L, ... of V elements and      */
+/*         accumulates ss = fma(x, x, ss) in increasing position; lanes */
+/*         are summed pairwise nearest-first (lane l takes              */
+/*         ss[l] + ss[l+off], lower first); then ms = ss/D,             */
+/*         rinv = 1/sqrt(ms + eps), IEEE fp32.                          */
+/* ------------------------------------------------------------------ */
+
+static float row_rinv_fp32(const uint16_t* x, int64_t D, float eps, int V, int L) {
+  float lane[ORC_MAX_LANES];
+  for (int l = 0; l < L; ++l) lane[l] = 0.0f;
+  int64_t nvec = D / V;
+  for (int l = 0; l < L; ++l)
+    for (int64_t v = l; v < nvec; v += L)
+      for (int e = 0; e < V; ++e) {
+        float xv = orc_f32_from_bf16(x[v * V + e]);
+        lane[l] = fmaf(xv, xv, lane[l]);
+      }
+  for (int off = 1; off < L; off *= 2)
+    for (int l = 0; l < L; l += 2 * off) lane[l] = lane[l] + lane[l + off];
+  float ms = lane[0] / (float)D;
+  float t = ms + eps;
+  float s = sqrtf(t);
+  return 1.0f / s;
+}
+
+static double row_rinv_fp64(const uint16_t* x, int64_t D, float eps) {
+  double ss = 0.0;
+  for (int64_t j = 0; j < D; ++j) {
+    double xv = (double)orc_f32_from_bf16(x[j]);
+    ss += xv * xv;
+  }
+  return 1.0 / sqrt(ss / (double)D + (double)eps);
+}
+
+/* rmsnorm_scale_shift: RMSNorm(x) * (1 + scale) + shift, the eager ops  */
+/* of that chain each rounded to bf16 (x_hat = bf16(x * rinv), then the  */
+/* modulate tail).  x [B*S, D]; scale, shift [B, D].                     */
+int orc_rmsnorm_scale_shift(const uint16_t* x, int64_t B, int64_t S, int64_t D, const uint16_t* scale,
+                            const uint16_t* shift, float eps, int mode, int V, int L, uint16_t* out,
+                            double* rinv_out) {
+  if (B < 0 || S < 0 || D <= 0) return ORC_EINVAL;
+  if (mode == ORC_FP32_FIXED && check_order(D, V, L) != ORC_OK) return ORC_EINVAL;
+  if (mode != ORC_FP32_FIXED && mode != ORC_FP64_TWO_PASS) return ORC_EINVAL;
+  int64_t R = B * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const uint16_t* xr = x + r * D;
+    const uint16_t* sc = scale + (r / S) * D;
+    const uint16_t* sh = shift + (r / S) * D;
+    uint16_t* o = out + r * D;
+    if (mode == ORC_FP32_FIXED) {
+      float rinv = row_rinv_fp32(xr, D, eps, V, L);
+      for (int64_t j = 0; j < D; ++j) o[j] = modulate_tail_f32(orc_f32_from_bf16(xr[j]) * rinv, sc[j], sh[j]);
+      if (rinv_out) rinv_out[r] = rinv;
+    } else {
+      double rinv = row_rinv_fp64(xr, D, eps);
+      for (int64_t j = 0; j < D; ++j) o[j] = modulate_tail_f64((double)orc_f32_from_bf16(xr[j]) * rinv, sc[j], sh[j]);
+      if (rinv_out) rinv_out[r] = rinv;
+    }
+  }
+  return ORC_OK;
+}
+
+/* qk_rmsnorm: RMSNorm over each head row of Dh with an optional weight, */
+/* one eager op (torch's rms_norm: x * rinv, times the weight, computed  */
+/* in fp32 and rounded once): out = bf16((x * rinv) * w).  x [R, Dh];    */
+/* w [Dh] or NULL.                                                        */
+int orc_qk_rmsnorm(const uint16_t* x, int64_t R, int64_t Dh, const uint16_t* w, float eps, int mode, int V,
+                   int L, uint16_t* out) {
+  if (R < 0 || Dh <= 0) return ORC_EINVAL;
+  if (mode == ORC_FP32_FIXED && check_order(Dh, V, L) != ORC_OK) return ORC_EINVAL;
+  if (mode != ORC_FP32_FIXED && mode != ORC_FP64_TWO_PASS) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const uint16_t* xr = x + r * Dh;
+    uint16_t* o = out + r * Dh;
+    if (mode == ORC_FP32_FIXED) {
+      float rinv = row_rinv_fp32(xr, Dh, eps, V, L);
+      for (int64_t j = 0; j < Dh; ++j) {
+        float xn = orc_f32_from_bf16(xr[j]) * rinv;
+        float y = w ? xn * orc_f32_from_bf16(w[j]) : xn;
+        o[j] = orc_bf16_from_f32(y);
+      }
+    } else {
+      double rinv = row_rinv_fp64(xr, Dh, eps);
+      for (int64_t j = 0; j < Dh; ++j) {
+        double xn = (double)orc_f32_from_bf16(xr[j]) * rinv;
+        double y = w ? xn * (double)orc_f32_from_bf16(w[j]) : xn;
+        o[j] = orc_bf16_from_f64(y);
       }
     }
   }

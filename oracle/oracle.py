@@ -88,6 +88,10 @@ def load_library(path: str):
                                                       ctypes.c_int, u16p, u16p, f64p, f64p]
     lib.orc_qk_head_layernorm.argtypes = [u16p, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, u16p]
+    lib.orc_rmsnorm_scale_shift.argtypes = [u16p, i64, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, u16p, f64p]
+    lib.orc_qk_rmsnorm.argtypes = [u16p, i64, i64, u16p, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, u16p]
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
     lib.orc_get_threads.argtypes = []
@@ -203,6 +207,41 @@ def residual_gate_add(res, gate, upd, S: int, mode: int = FP32):
     rc = _load().orc_residual_gate_add(_p(res, ctypes.c_uint16), _p(gate, ctypes.c_uint16),
                                        _p(upd, ctypes.c_uint16), B, S, D, mode, _p(out, ctypes.c_uint16))
     _check(rc, "residual_gate_add")
+    return out
+
+
+def rmsnorm_scale_shift(x, scale, shift, S: int, eps: float, mode: int, V: int = 8, L: int = 64):
+    """out = bf16 chain of RMSNorm(x)*(1+scale)+shift.
+
+    x [B*S, D], scale/shift [B, D] (bf16 bits).  Returns (out bits [B*S, D],
+    rinv [B*S] float64: 1/sqrt(mean(x^2)+eps)).
+    """
+    x, scale, shift = _u16(x), _u16(scale), _u16(shift)
+    R, D = x.shape
+    B = scale.shape[0]
+    if R != B * S or scale.shape != (B, D) or shift.shape != (B, D):
+        raise ValueError("shape mismatch")
+    out = np.empty((R, D), dtype=np.uint16)
+    rinv = np.empty(R, dtype=np.float64)
+    rc = _load().orc_rmsnorm_scale_shift(_p(x, ctypes.c_uint16), B, S, D, _p(scale, ctypes.c_uint16),
+                                         _p(shift, ctypes.c_uint16), eps, mode, V, L, _p(out, ctypes.c_uint16),
+                                         _p(rinv, ctypes.c_double))
+    _check(rc, "rmsnorm_scale_shift")
+    return out, rinv
+
+
+def qk_rmsnorm(x, w, eps: float, mode: int, V: int = 8, L: int = 16):
+    """RMSNorm of each head row with an optional weight.  x [R, Dh]; w [Dh] or None."""
+    x = _u16(x)
+    R, Dh = x.shape
+    if w is not None:
+        w = _u16(w)
+        if w.shape != (Dh,):
+            raise ValueError("shape mismatch")
+    out = np.empty((R, Dh), dtype=np.uint16)
+    rc = _load().orc_qk_rmsnorm(_p(x, ctypes.c_uint16), R, Dh, _p(w, ctypes.c_uint16) if w is not None else None,
+                                eps, mode, V, L, _p(out, ctypes.c_uint16))
+    _check(rc, "qk_rmsnorm")
     return out
 
 

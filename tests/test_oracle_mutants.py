@@ -25,8 +25,8 @@ MUTANTS = {
     "unbiased_variance_fp32": ("float var = lane[0].m2 / (float)D;", "float var = lane[0].m2 / (float)(D - 1);"),
     "eps_dropped_fp32": ("float t = var + eps;", "float t = var;"),
     "fp64_no_mean_subtraction": ("double c = (double)orc_f32_from_bf16(x[j]) - mean;", "double c = (double)orc_f32_from_bf16(x[j]);"),
-    "xhat_not_rounded": ("float xhat = rb((orc_f32_from_bf16(xr[j]) - mean) * rstd);", "float xhat = (orc_f32_from_bf16(xr[j]) - mean) * rstd;"),
-    "one_plus_scale_not_rounded": ("float one_plus = rb(1.0f + orc_f32_from_bf16(sc[j]));", "float one_plus = 1.0f + orc_f32_from_bf16(sc[j]);"),
+    "xhat_not_rounded": ("float xhat = rb(n);", "float xhat = n;"),
+    "one_plus_scale_not_rounded": ("float one_plus = rb(1.0f + orc_f32_from_bf16(sc));", "float one_plus = 1.0f + orc_f32_from_bf16(sc);"),
     "shift_and_scale_swapped": ("const uint16_t* sc = scale + (r / S) * D;", "const uint16_t* sc = shift + (r / S) * D;"),
     "gate_product_not_rounded": ("float t = rb(orc_f32_from_bf16(g[j]) * orc_f32_from_bf16(upd[i]));", "float t = orc_f32_from_bf16(g[j]) * orc_f32_from_bf16(upd[i]);"),
     "qk_affine_swapped": ("float y = w ? fmaf(orc_f32_from_bf16(w[j]), xn, orc_f32_from_bf16(b[j])) : xn;", "float y = w ? fmaf(orc_f32_from_bf16(b[j]), xn, orc_f32_from_bf16(w[j])) : xn;"),
@@ -35,8 +35,15 @@ MUTANTS = {
     "rne_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", "if (dropped >= 0x8000u) kept += 1u;"),
     "fused_norms_old_residual": ("return orc_ln_modulate(res_out, B, S, D, scale, shift", "return orc_ln_modulate(res, B, S, D, scale, shift"),
     "fused_skips_residual_update": ("int rc = orc_residual_gate_add(res, gate, upd, B, S, D, mode, res_out);", "int rc = orc_residual_gate_add(res, gate, upd, B, S, D, mode, res_out); memcpy(res_out, res, (size_t)(B * S * D) * 2);"),
+    "rms_eps_dropped": ("  float t = ms + eps;\n  float s = sqrtf(t);\n  return 1.0f / s;", "  float t = ms;\n  float s = sqrtf(t);\n  return 1.0f / s;"),
+    "rms_sum_not_divided": ("return 1.0 / sqrt(ss / (double)D + (double)eps);", "return 1.0 / sqrt(ss + (double)eps);"),
+    "rms_lane_sum_drops_partner": ("lane[l] = lane[l] + lane[l + off];", "lane[l] = lane[l];"),
+    "fp64_tail_product_not_rounded": ("double y = rb64(xhat * one_plus);", "double y = xhat * one_plus;"),
+    "qk_rms_rounds_before_weight": ("float y = w ? xn * orc_f32_from_bf16(w[j]) : xn;", "float y = w ? rb(xn) * orc_f32_from_bf16(w[j]) : xn;"),
     "bias_not_rounded": ("double z = rb64((double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]));", "double z = (double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]);"),
 }
+
+ANCHOR_COUNT = {"shift_and_scale_swapped": 2}
 
 FAST_PINS = [
     lambda o: P.test_worked_d4(o, P.FP32),
@@ -57,6 +64,14 @@ FAST_PINS = [
     lambda o: P.test_qk_fp32_within_one_ulp_of_fp64(o),
     lambda o: P.test_fused_residual_worked_d4(o, P.FP32),
     lambda o: P.test_fused_residual_equals_torch_eager_chain(o),
+    lambda o: P.test_rms_worked_d4(o, P.FP32),
+    lambda o: P.test_rms_fp64_mode_equals_torch_rms_norm(o),
+    lambda o: P.test_rms_constant_rows(o, P.FP32, 2240),
+    lambda o: P.test_rms_tail_equals_torch_eager(o),
+    lambda o: P.test_qk_rms_fp64_equals_torch_rms_norm(o),
+    lambda o: P.test_qk_rms_fp32_equals_torch_fp32_tail(o),
+    lambda o: P.test_elementwise_tail_fp64_mode_equals_torch_eager(o, "layer"),
+    lambda o: P.test_elementwise_tail_fp64_mode_equals_torch_eager(o, "rms"),
     lambda o: P.test_gelu_f64_vs_torch(o),
     lambda o: P.test_bias_gelu_rounds_after_bias(o),
 ]
@@ -66,7 +81,10 @@ FAST_PINS = [
 def test_mutant_is_caught(orc, tmp_path, name):
     src = open(os.path.join(os.path.dirname(orc.__file__), "adaln_oracle.c")).read()
     old, new = MUTANTS[name]
-    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    # the mistake is planted at every occurrence of its anchor (the LayerNorm and RMSNorm
+    # chains share some source lines); the anchor must exist
+    want = ANCHOR_COUNT.get(name, 1)
+    assert src.count(old) == want, "mutation anchor found %d times, expected %d: %r" % (src.count(old), want, old)
     path = tmp_path / "mutant.c"
     path.write_text(src.replace(old, new))
     lib = orc.compile_source(str(path), str(tmp_path / "libmutant.so"))

@@ -500,3 +500,154 @@ def test_fused_residual_equals_torch_eager_chain(orc):
     xhat = ((xf - m) * r).to(torch.bfloat16).reshape(B, S, D)
     eager = xhat * (1 + sc[:, None, :]) + sh[:, None, :]
     assert np.array_equal(out, flat(eager))
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + scale/shift and per-head q/k RMSNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_rms_worked_d4(orc, mode):
+    """x = [-3,-1,1,3] has mean 0, so RMSNorm equals LayerNorm there; x = [3,4,3,4]:
+    rinv = 1/sqrt(12.5 + eps) -> bf16 0.84765625, 1.1328125 (tests/golden/closed_forms.txt)."""
+    zero = bf([[0.0] * 4])
+    out, rinv = orc.rmsnorm_scale_shift(bf([[-3.0, -1.0, 1.0, 3.0]]), zero, zero, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[-1.34375, -0.447265625, 0.447265625, 1.34375]]
+    assert abs(rinv[0] - 1 / math.sqrt(5 + 1e-6)) < 1e-7
+    out, rinv = orc.rmsnorm_scale_shift(bf([[3.0, 4.0, 3.0, 4.0]]), zero, zero, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[0.84765625, 1.1328125, 0.84765625, 1.1328125]]
+    assert abs(rinv[0] - 1 / math.sqrt(12.5 + 1e-6)) < 1e-7
+    # scale = 1 doubles it exactly; scale = -1 leaves the shift
+    out, _ = orc.rmsnorm_scale_shift(bf([[3.0, 4.0, 3.0, 4.0]]), bf([[1.0] * 4]), zero, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[1.6953125, 2.265625, 1.6953125, 2.265625]]
+    sh = bf([[0.5, -0.25, 2.0, -8.0]])
+    out, _ = orc.rmsnorm_scale_shift(bf([[3.0, 4.0, 3.0, 4.0]]), bf([[-1.0] * 4]), sh, 1, 1e-6, mode, V=4, L=64)
+    assert np.array_equal(out, sh)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+@pytest.mark.parametrize("D", [8, 2240, 4096])
+def test_rms_constant_rows(orc, mode, D):
+    """x = c: x_hat = c/sqrt(c^2 + eps) rounds to +-1 for |c| >= 1; c = 0 gives +0."""
+    x = bf([[1.0] * D, [-3.5] * D, [1000.0] * D, [0.0] * D])
+    z = bf([[0.0] * D])
+    V = 8 if D % 8 == 0 else 4
+    out, rinv = orc.rmsnorm_scale_shift(x, z, z, 4, 1e-6, mode, V=V, L=64)
+    assert f32(out)[:3].tolist() == [[1.0] * D, [-1.0] * D, [1.0] * D]
+    assert np.all(out[3] == 0)
+
+
+def test_rms_fp64_mode_equals_torch_rms_norm(orc):
+    """scale = shift = 0: the chain is bf16(RMSNorm(x)); torch's float64 rms_norm rounded to bf16
+    must agree except where the double value sits within 1e-12 of a bf16 midpoint."""
+    g = torch.Generator().manual_seed(30)
+    x = (torch.randn(128, 2240, generator=g) * 3 + 0.5).to(torch.bfloat16)
+    z = torch.zeros(1, 2240, dtype=torch.bfloat16)
+    out, _ = orc.rmsnorm_scale_shift(bits_of(x), bits_of(z), bits_of(z), 128, 1e-6, FP64)
+    ref64 = torch.nn.functional.rms_norm(x.double(), (2240,), eps=float(np.float32(1e-6))).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+    assert diff.mean() < 1e-4
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_rms_power_of_two_scale_invariance(orc, mode):
+    """eps = 0: RMSNorm(2^k x) == RMSNorm(x) bit for bit (every step scales exactly)."""
+    g = torch.Generator().manual_seed(31)
+    x = (torch.randn(16, 1024, generator=g)).to(torch.bfloat16)
+    z = torch.zeros(1, 1024, dtype=torch.bfloat16)
+    base, r0 = orc.rmsnorm_scale_shift(bits_of(x), bits_of(z), bits_of(z), 16, 0.0, mode)
+    for k in (-3, 5):
+        xs = x * (2.0 ** k)
+        out, r = orc.rmsnorm_scale_shift(bits_of(xs), bits_of(z), bits_of(z), 16, 0.0, mode)
+        assert np.array_equal(out, base)
+        assert np.array_equal(r * (2.0 ** k), r0)
+
+
+def test_rms_stats_vs_fractions(orc):
+    """Small-integer rows: the sum of squares is exact in both modes, so rinv is the correctly
+    rounded (fp64) or within two fp32 roundings (fp32) of 1/sqrt(ss/D + eps), eps = 0."""
+    rng = np.random.default_rng(32)
+    for D in (4, 8, 12, 64, 200):
+        xi = rng.integers(-20, 21, size=(3, D)).astype(np.float32)
+        xi[:, 0] = 7  # no all-zero row
+        x = bf(xi.tolist())
+        z = bf([[0.0] * D])
+        V = 8 if D % 8 == 0 else 4
+        _, r32 = orc.rmsnorm_scale_shift(x, z, z, 3, 0.0, FP32, V=V, L=64)
+        _, r64 = orc.rmsnorm_scale_shift(x, z, z, 3, 0.0, FP64)
+        for i in range(3):
+            ss = Fraction(int(np.sum(xi[i].astype(np.int64) ** 2)))
+            exact = 1.0 / math.sqrt(float(ss / D))
+            assert abs(r64[i] - exact) <= 2 * np.finfo(np.float64).eps * exact
+            assert abs(r32[i] - exact) <= 4 * np.finfo(np.float32).eps * exact
+
+
+def test_rms_tail_equals_torch_eager(orc):
+    """Given the oracle's own fp32 rinv, the rest is torch's eager bf16 chain:
+    bf16(x * rinv), then (1 + scale), *, + shift as bf16 tensor ops."""
+    wl = W.glm_square(seed=33, S=64, D=4096)
+    x, sc, sh = wl.tensors["x"], wl.tensors["scale"], wl.tensors["shift"]
+    out, rinv = orc.rmsnorm_scale_shift(bits_of(x.reshape(64, 4096)), bits_of(sc), bits_of(sh), 64, 1e-5, FP32)
+    xf = x.reshape(64, 4096).float()
+    r = torch.from_numpy(rinv.astype(np.float32))[:, None]
+    xhat = (xf * r).to(torch.bfloat16)
+    eager = xhat * (1 + sc) + sh
+    assert np.array_equal(out, bits_of(eager))
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_qk_rms_unit_weight_equals_no_weight(orc, mode):
+    g = torch.Generator().manual_seed(34)
+    x = torch.randn(96, 128, generator=g).to(torch.bfloat16)
+    one = torch.ones(128, dtype=torch.bfloat16)
+    a = orc.qk_rmsnorm(bits_of(x), bits_of(one), 1e-6, mode)
+    b = orc.qk_rmsnorm(bits_of(x), None, 1e-6, mode)
+    assert np.array_equal(a, b)
+
+
+def test_qk_rms_fp64_equals_torch_rms_norm(orc):
+    """torch's float64 rms_norm with a weight, rounded once, against the fp64 mode."""
+    g = torch.Generator().manual_seed(35)
+    x = (torch.randn(512, 128, generator=g) * 2).to(torch.bfloat16)
+    w = (1 + 0.05 * torch.randn(128, generator=g)).to(torch.bfloat16)
+    out = orc.qk_rmsnorm(bits_of(x), bits_of(w), 1e-6, FP64)
+    ref64 = torch.nn.functional.rms_norm(x.double(), (128,), weight=w.double(), eps=float(np.float32(1e-6))).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+    assert diff.mean() < 1e-3
+
+
+def test_qk_rms_fp32_equals_torch_fp32_tail(orc):
+    """The fp32 mode's weight step is torch's fp32 arithmetic: (x * rinv) * w, rounded once."""
+    g = torch.Generator().manual_seed(36)
+    x = (torch.randn(256, 128, generator=g) * 2).to(torch.bfloat16)
+    w = (1 + 0.05 * torch.randn(128, generator=g)).to(torch.bfloat16)
+    z = torch.zeros(1, 128, dtype=torch.bfloat16)
+    _, rinv = orc.rmsnorm_scale_shift(bits_of(x), bits_of(z), bits_of(z), 256, 1e-6, FP32, V=8, L=16)
+    r = torch.from_numpy(rinv.astype(np.float32))[:, None]
+    want = ((x.float() * r) * w.float()).to(torch.bfloat16)
+    out = orc.qk_rmsnorm(bits_of(x), bits_of(w), 1e-6, FP32, V=8, L=16)
+    assert np.array_equal(out, bits_of(want))
+
+
+@pytest.mark.parametrize("norm", ["layer", "rms"])
+def test_elementwise_tail_fp64_mode_equals_torch_eager(orc, norm):
+    """The two-pass mode's tail: with x_hat = bf16(n) for the double-precision normalized value n
+    (bf16_from_f64 is pinned on its own), the rest is torch's eager bf16 ops: (1 + scale), *,
+    + shift -- each product and sum of two bf16 values is exact in double before its one rounding."""
+    wl = W.glm_square(seed=37, S=64, D=4096)
+    x, sc, sh = wl.tensors["x"], wl.tensors["scale"], wl.tensors["shift"]
+    xb = bits_of(x.reshape(64, 4096))
+    xd = x.reshape(64, 4096).double()
+    if norm == "layer":
+        out, mean, rstd = orc.ln_modulate(xb, bits_of(sc), bits_of(sh), 64, 1e-5, FP64)
+        n = (xd - torch.from_numpy(mean)[:, None]) * torch.from_numpy(rstd)[:, None]
+    else:
+        out, rinv = orc.rmsnorm_scale_shift(xb, bits_of(sc), bits_of(sh), 64, 1e-5, FP64)
+        n = xd * torch.from_numpy(rinv)[:, None]
+    xhat = W.from_bits(orc.bf16_from_f64(n.numpy()))
+    eager = xhat * (1 + sc) + sh
+    assert np.array_equal(out, bits_of(eager))
