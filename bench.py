@@ -323,6 +323,29 @@ def other_workloads(m, W, dev, stream, log):
     res["bias_gelu_tanh_16384x12288"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
     del xs2, outs, x
 
+    # RMSNorm variants on the same shapes: (1,4096,4096) rows, (1,4360,32,128) q/k heads
+    wl = W.glm_square()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    nb = rot(lnm_bytes(4096, 4096, 1))
+    xs_ = [t["x"].clone() for _ in range(nb)]
+    outs = [torch.empty_like(t["x"]) for _ in range(nb)]
+    calls = [m.rmsnorm_scale_shift(xs_[i], t["scale"], t["shift"], 1e-5, out=outs[i], prepare=True)
+             for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["rmsnorm_scale_shift_1x4096x4096"] = {"us": round(us, 3),
+                                              "GBps": round(lnm_bytes(4096, 4096, 1) / us / 1e3, 1)}
+    del xs_, outs, calls
+    wl = W.glm_qk()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    nb = rot(4 * t["q"].numel() * 2)
+    qs = [t["q"].clone() for _ in range(nb)]
+    ks = [t["k"].clone() for _ in range(nb)]
+    calls = [m.qk_rmsnorm(qs[i], ks[i], t["wq"], t["wk"], 1e-6, prepare=True) for i in range(nb)]
+    us = time_loop(calls, 200, stream)
+    b = 4 * t["q"].numel() * 2 + 2 * 128 * 2
+    res["qk_rmsnorm_1x4360x32x128"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del qs, ks, calls
+
     # the gated residual update fused with ln_modulate, (1,4096,4096)
     wl = W.glm_square()
     t = {k: v.to(dev) for k, v in wl.tensors.items()}

@@ -68,6 +68,8 @@ extern "C" {
 #define ADALN_OP_LN_MODULATE 1
 #define ADALN_OP_QK_HEAD_LAYERNORM 2
 #define ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE 3
+#define ADALN_OP_RMSNORM_SCALE_SHIFT 4
+#define ADALN_OP_QK_RMSNORM 5
 
 /*
  * ln_modulate -- out = LN(x) * (1 + scale) + shift, bf16 at every eager op.
@@ -122,6 +124,32 @@ int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_s, const vo
 
 int residual_gate_add_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b, int64_t sr_s,
                               int64_t sg_b, int64_t su_b, int64_t su_s, int dtype);
+
+/*
+ * rmsnorm_scale_shift -- out = RMSNorm(x) * (1 + scale) + shift, bf16 at
+ * every eager op: x_hat = bf16(x * rinv), then the ln_modulate tail
+ * (bf16(1+scale), bf16(x_hat*one_plus), bf16(y+shift)).
+ *
+ * Source: "Fused Kernels" page, table "Normalization" (rmsnorm_scale_shift:
+ * RMSNorm + * (1 + scale) + shift, bit-exact, replaces four eager kernels)
+ * and the request-gated fusion table (rms_norm(x) * (1 + scale) + shift in
+ * one launch).  RMSNorm without affine: rinv = 1/sqrt(mean(x^2) + eps), no
+ * mean subtraction.  Statistics order: lane l of a row accumulates
+ * ss = fma(x, x, ss) over the elements of vectors l, l+64, ... in increasing
+ * position (V as adaln_order_for reports for ADALN_OP_RMSNORM_SCALE_SHIFT);
+ * lane sums are added pairwise at offsets 1, 2, 4, ..., 32; rinv =
+ * 1/sqrt(ss/D + eps) with IEEE division and square root.
+ *
+ * Arguments, layouts, fast paths and aliasing as ln_modulate, except:
+ *  rinv_out optional [B*S] fp32 per-row 1/sqrt(mean(x^2) + eps); NULL = skip.
+ */
+int rmsnorm_scale_shift(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                        int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                        int64_t sshift_b, float eps, int dtype, void* out, float* rinv_out,
+                        void* stream);
+
+int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                int64_t sx_d, int64_t sscale_b, int64_t sshift_b, int dtype);
 
 /*
  * residual_gate_add_ln_modulate -- the gated residual update, then
@@ -193,6 +221,31 @@ int qk_head_layernorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64
                               int64_t sk_h, int dtype);
 
 /*
+ * qk_rmsnorm -- per-head RMSNorm of q and k in one launch, with an optional
+ * weight per side: out = bf16((x * rinv) * w), rinv = 1/sqrt(mean(x^2) +
+ * eps), each product rounded to fp32 and the result rounded to bf16 once
+ * (torch's rms_norm is one eager op computed in fp32).  Without weights:
+ * out = bf16(x * rinv).
+ *
+ * Source: "Fused Kernels" page, table "Normalization" (qk_rmsnorm_native:
+ * Z-Image per-head QK RMSNorm, bit-exact) and the request-gated fusion table
+ * (HunyuanVideo strided QK RMSNorm over the packed QKV layout).  Statistics:
+ * 16 lanes per head, lane l accumulates ss = fma(x, x, ss) over vectors
+ * l, l+16, ... in increasing position; lane sums added pairwise at offsets
+ * 1, 2, 4, 8; rinv with IEEE division and square root.
+ *
+ *  q, k, strides, B, S, H, Dh, q_out, k_out, aliasing: as qk_head_layernorm.
+ *  wq, wk   [Dh] each, or both NULL.
+ */
+int qk_rmsnorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h, const void* k, int64_t sk_b,
+               int64_t sk_s, int64_t sk_h, int64_t B, int64_t S, int64_t H, int64_t Dh,
+               const void* wq, const void* wk, float eps, int dtype, void* q_out, void* k_out,
+               void* stream);
+
+int qk_rmsnorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b, int64_t sq_s,
+                       int64_t sq_h, int64_t sk_b, int64_t sk_s, int64_t sk_h, int dtype);
+
+/*
  * bias_gelu_tanh -- z = bf16(x + bias); out = bf16(gelu_tanh(z)).
  *
  * Source: PR #37075 report (Wan2.2 NVFP4 bias + GELU), 实现拆解 §1 and
@@ -216,8 +269,9 @@ int bias_gelu_tanh_can_use(int64_t rows, int64_t width, int64_t sx_row, int dtyp
 /*
  * adaln_order_for -- the fixed fp32 reduction order the kernels use for a
  * row of D elements of op ADALN_OP_*: *V = elements per vector (8 when
- * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate and the
- * residual-fused ln_modulate, 16 for a q/k head).  Pure host function.  Returns ADALN_OK or an error code.
+ * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate, the
+ * residual-fused ln_modulate and rmsnorm_scale_shift, 16 for a q/k head of
+ * qk_head_layernorm or qk_rmsnorm).  Pure host function.  Returns ADALN_OK or an error code.
  */
 int adaln_order_for(int op, int64_t D, int* V, int* L);
 

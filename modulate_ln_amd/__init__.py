@@ -2,7 +2,7 @@
 kernels (``libadaln.so``) and this thin torch binding.
 
     from modulate_ln_amd import ln_modulate, residual_gate_add, qk_head_layernorm, bias_gelu_tanh
-    from modulate_ln_amd import residual_gate_add_ln_modulate
+    from modulate_ln_amd import residual_gate_add_ln_modulate, rmsnorm_scale_shift, qk_rmsnorm
 
 The binding only marshals arguments; torch provides device memory and
 streams.  Importing the package does not load the library; the first call
@@ -14,14 +14,18 @@ from .ops import (  # noqa: F401
     bias_gelu_tanh,
     ln_modulate,
     qk_head_layernorm,
+    qk_rmsnorm,
     residual_gate_add,
     residual_gate_add_ln_modulate,
+    rmsnorm_scale_shift,
 )
 
 __all__ = [
     "ln_modulate",
     "residual_gate_add",
     "residual_gate_add_ln_modulate",
+    "rmsnorm_scale_shift",
+    "qk_rmsnorm",
     "qk_head_layernorm",
     "bias_gelu_tanh",
     "order_for",

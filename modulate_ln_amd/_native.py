@@ -27,6 +27,8 @@ BF16 = 1
 OP_LN_MODULATE = 1
 OP_QK_HEAD_LAYERNORM = 2
 OP_RESIDUAL_GATE_ADD_LN_MODULATE = 3
+OP_RMSNORM_SCALE_SHIFT = 4
+OP_QK_RMSNORM = 5
 ABI_VERSION = 1
 
 # every symbol include/adaln.h declares
@@ -41,6 +43,10 @@ EXPORTS = (
     "bias_gelu_tanh_can_use",
     "residual_gate_add_ln_modulate",
     "residual_gate_add_ln_modulate_can_use",
+    "rmsnorm_scale_shift",
+    "rmsnorm_scale_shift_can_use",
+    "qk_rmsnorm",
+    "qk_rmsnorm_can_use",
     "adaln_order_for",
     "adaln_status_str",
     "adaln_abi_version",
@@ -82,6 +88,11 @@ def lib():
                                                 vp, i64, vp, i64, f32, ci, vp, vp, vp, vp, vp]
     L.residual_gate_add_ln_modulate_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                                         i64, ci]
+    L.rmsnorm_scale_shift.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp]
+    L.rmsnorm_scale_shift_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
+    L.qk_rmsnorm.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, vp, vp, f32, ci, vp, vp,
+                             vp]
+    L.qk_rmsnorm_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.adaln_order_for.argtypes = [ci, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.adaln_status_str.argtypes = [ci]
     L.adaln_status_str.restype = ctypes.c_char_p

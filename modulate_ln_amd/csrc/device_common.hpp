@@ -226,11 +226,43 @@ __device__ __forceinline__ void merge_down_equal(float& m, float& m2, float cnt)
   m = mm;
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm statistics: per-lane sums of squares (ss = fma(x, x, ss) in
+// increasing position) summed pairwise, nearest first.  fp32 addition is
+// commutative bit for bit, so the butterfly (every lane of a 2*OFF group
+// computes lower + upper) and the tree toward lane 0 give the same sums as
+// lane l taking ss[l] + ss[l + OFF].  Lanes without elements hold +0.
+// ---------------------------------------------------------------------------
+template <int OFF>
+__device__ __forceinline__ void sum_level(float& s) {
+  s = s + lane_xor<OFF>(s);
+}
+
+template <int L>
+__device__ __forceinline__ void sum_lanes(float& s) {
+  sum_level<1>(s);
+  sum_level<2>(s);
+  sum_level<4>(s);
+  sum_level<8>(s);
+  if constexpr (L == 64) {
+    sum_level<16>(s);
+    sum_level<32>(s);
+  } else {
+    static_assert(L == 16, "sum_lanes: L must be 16 or 64");
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ void sum_down(float& s) {
+  s = s + lane_down<OFF>(s);
+}
+
 __device__ __forceinline__ float bcast_lane0(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
 // var = m2/D, rstd = 1/sqrt(var + eps): IEEE division and square root.
+// (With m2 the sum of squares this is RMSNorm's 1/sqrt(mean(x^2) + eps).)
 __device__ __forceinline__ float finalize_rstd(float m2, float D, float eps) {
   float var = m2 / D;
   float t = var + eps;

@@ -77,9 +77,10 @@ inline int order_for(int op, int64_t D, int* V, int* L) {
   if (D <= 0 || D % 4 != 0) return ADALN_ERR_SHAPE;
   int v = (D % 8 == 0) ? 8 : 4;
   int l;
-  if (op == ADALN_OP_LN_MODULATE || op == ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE)
+  if (op == ADALN_OP_LN_MODULATE || op == ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE ||
+      op == ADALN_OP_RMSNORM_SCALE_SHIFT)
     l = 64;
-  else if (op == ADALN_OP_QK_HEAD_LAYERNORM)
+  else if (op == ADALN_OP_QK_HEAD_LAYERNORM || op == ADALN_OP_QK_RMSNORM)
     l = 16;
   else
     return ADALN_ERR_ARG;

@@ -20,6 +20,13 @@
 // Rows whose storage is not vector-aligned or not contiguous take the same
 // code with element-wise gathers; the order of arithmetic is identical, so
 // the result depends only on the logical values.
+//
+// rmsnorm_scale_shift ("Fused Kernels" page, table "Normalization":
+// RMSNorm + * (1 + scale) + shift; the request-gated fusion table's
+// rms_norm(x) * (1 + scale) + shift) is the same kernel family with RMSNorm
+// statistics: each lane accumulates fma(x, x, ss) in the same element order,
+// the lanes' sums are added pairwise nearest-first, rinv = 1/sqrt(ss/D +
+// eps), and x_hat = bf16(x * rinv) enters the same modulate tail.
 #include <utility>
 
 #include "device_common.hpp"
@@ -66,16 +73,32 @@ __device__ __forceinline__ void welford_lane(const Vec<V>* buf, int64_t nvec, in
       ...);
 }
 
-// the per-element tail of the chain for one vector
-template <int V>
+// RMSNorm: the lane's sum of squares, same element order as welford_lane
+template <int V, int K, int... E>
+__device__ __forceinline__ void sumsq_vec(const Vec<V>& v, float& ss, std::integer_sequence<int, E...>) {
+  ((ss = __builtin_fmaf(elem<V, E>(v), elem<V, E>(v), ss)), ...);
+}
+
+template <int V, int... K>
+__device__ __forceinline__ void sumsq_lane(const Vec<V>* buf, int64_t nvec, int lane, float& ss,
+                                           std::integer_sequence<int, K...>) {
+  (
+      [&] {
+        if ((int64_t)K * kWave + lane < nvec) sumsq_vec<V, K>(buf[K], ss, std::make_integer_sequence<int, V>{});
+      }(),
+      ...);
+}
+
+// the per-element tail of the chain for one vector (RMS: x * rinv, no mean)
+template <int V, bool RMS>
 __device__ __forceinline__ Vec<V> modulate_vec(const Vec<V>& xv, const Vec<V>& sv, const Vec<V>& hv,
                                                float mean, float rstd) {
   Vec<V> o;
 #pragma unroll
   for (int i = 0; i < V / 2; ++i) {
-    float n0 = (lo_f32(xv.w[i]) - mean) * rstd;
-    float n1 = (hi_f32(xv.w[i]) - mean) * rstd;
-    round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
+    float n0 = RMS ? lo_f32(xv.w[i]) * rstd : (lo_f32(xv.w[i]) - mean) * rstd;
+    float n1 = RMS ? hi_f32(xv.w[i]) * rstd : (hi_f32(xv.w[i]) - mean) * rstd;
+    round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean)), or bf16(x * rinv)
     float p0 = 1.0f + lo_f32(sv.w[i]);
     float p1 = 1.0f + hi_f32(sv.w[i]);
     round_pair(p0, p1);  // bf16(1 + scale)
@@ -89,7 +112,7 @@ __device__ __forceinline__ Vec<V> modulate_vec(const Vec<V>& xv, const Vec<V>& s
 
 // NV = the largest number of vectors any lane owns for the rows this
 // instantiation serves (the launcher guarantees D/V <= 64*NV).
-template <int V, int NV, bool GATHER>
+template <int V, int NV, bool GATHER, bool RMS>
 __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nvec = a.D / V;
@@ -115,12 +138,17 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
     }
 
     float mean = 0.0f, m2 = 0.0f;
-    welford_lane<V>(buf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
-    float n = (float)(nv_lane * V);
-    merge_lanes<64>(mean, m2, n, lane);
+    if constexpr (RMS) {
+      sumsq_lane<V>(buf, nvec, lane, m2, std::make_integer_sequence<int, NV>{});
+      sum_lanes<64>(m2);
+    } else {
+      welford_lane<V>(buf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
+      float n = (float)(nv_lane * V);
+      merge_lanes<64>(mean, m2, n, lane);
+    }
     const float rstd = finalize_rstd(m2, Df, a.eps);
     if (lane == 0) {
-      if (a.mean_out) a.mean_out[r] = mean;
+      if (!RMS && a.mean_out) a.mean_out[r] = mean;
       if (a.rstd_out) a.rstd_out[r] = rstd;
     }
 
@@ -140,9 +168,9 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
       const int64_t v = (int64_t)k * kWave + lane;
       if (v < nvec) {
         if constexpr (GATHER)
-          scatter_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv[k], hv[k], mean, rstd));
+          scatter_vec<V>(orow + v * V, modulate_vec<V, RMS>(buf[k], sv[k], hv[k], mean, rstd));
         else
-          store_vec<V>(orow + v * V, modulate_vec<V>(buf[k], sv[k], hv[k], mean, rstd));
+          store_vec<V>(orow + v * V, modulate_vec<V, RMS>(buf[k], sv[k], hv[k], mean, rstd));
       }
     }
   }
@@ -176,7 +204,7 @@ struct TabShape {
 };
 
 
-template <int V, int NV, bool UNIF>
+template <int V, int NV, bool UNIF, bool RMS>
 __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   constexpr bool kPrefetch = TabShape<NV>::kPrefetch;
   constexpr bool kXf32 = TabShape<NV>::kXf32;
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   const float Df = (float)D;
   auto process = [&](const Vec<V>* buf, int ss) {
     const int64_t r = (int64_t)b * S + ss;
-    normalize_row<V, NV, UNIF, kXf32>(buf, tab, nvec, lane, Df, a.eps, a.out + r * D,
+    normalize_row<V, NV, UNIF, kXf32, RMS>(buf, tab, nvec, lane, Df, a.eps, a.out + r * D,
                                       a.mean_out ? a.mean_out + r : nullptr,
                                       a.rstd_out ? a.rstd_out + r : nullptr);
   };
@@ -264,7 +292,7 @@ __device__ __forceinline__ uint32_t join_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-template <int NV, bool UNIF>
+template <int NV, bool UNIF, bool RMS>
 __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sample) {
   constexpr int V = 8;
   extern __shared__ float4 smem[];  // tables [2][2][nvec], then the x tile [8][nvec] (uint4)
@@ -317,7 +345,7 @@ __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sa
     buf[k].w[3] = t.w;
   }
   const int64_t r = (int64_t)b * S + t0 + w;
-  normalize_row<V, NV, UNIF, true>(buf, tab, nvec, lane, (float)D, a.eps, a.out + r * D,
+  normalize_row<V, NV, UNIF, true, RMS>(buf, tab, nvec, lane, (float)D, a.eps, a.out + r * D,
                                    a.mean_out ? a.mean_out + r : nullptr,
                                    a.rstd_out ? a.rstd_out + r : nullptr);
 }
@@ -337,7 +365,7 @@ constexpr RcpTable make_rcp_table() {
 }
 __constant__ RcpTable kRcp = make_rcp_table();
 
-template <int V, bool GATHER>
+template <int V, bool GATHER, bool RMS>
 __global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nvec = a.D / V;
@@ -355,17 +383,25 @@ __global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float x = (e & 1) ? hi_f32(xv.w[e / 2]) : lo_f32(xv.w[e / 2]);
-        const float rc = kRcp.v[k * V + e + 1];
-        float delta = x - mean;
-        mean = __builtin_fmaf(delta, rc, mean);
-        m2 = __builtin_fmaf(delta, x - mean, m2);
+        if constexpr (RMS) {
+          m2 = __builtin_fmaf(x, x, m2);
+        } else {
+          const float rc = kRcp.v[k * V + e + 1];
+          float delta = x - mean;
+          mean = __builtin_fmaf(delta, rc, mean);
+          m2 = __builtin_fmaf(delta, x - mean, m2);
+        }
       }
     }
-    float n = (float)(nv_lane * V);
-    merge_lanes<64>(mean, m2, n, lane);
+    if constexpr (RMS) {
+      sum_lanes<64>(m2);
+    } else {
+      float n = (float)(nv_lane * V);
+      merge_lanes<64>(mean, m2, n, lane);
+    }
     const float rstd = finalize_rstd(m2, Df, a.eps);
     if (lane == 0) {
-      if (a.mean_out) a.mean_out[r] = mean;
+      if (!RMS && a.mean_out) a.mean_out[r] = mean;
       if (a.rstd_out) a.rstd_out[r] = rstd;
     }
     const uint16_t* sc = a.scale + b * a.ssc_b;
@@ -377,12 +413,12 @@ __global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
         Vec<V> xv = gather_vec<V>(xr + v * V * a.sx_d, a.sx_d);
         Vec<V> sv = gather_vec<V>(sc + v * V, 1);
         Vec<V> hv = gather_vec<V>(sh + v * V, 1);
-        scatter_vec<V>(orow + v * V, modulate_vec<V>(xv, sv, hv, mean, rstd));
+        scatter_vec<V>(orow + v * V, modulate_vec<V, RMS>(xv, sv, hv, mean, rstd));
       } else {
         Vec<V> xv = load_vec<V>(xr + v * V);
         Vec<V> sv = load_vec<V>(sc + v * V);
         Vec<V> hv = load_vec<V>(sh + v * V);
-        store_vec<V>(orow + v * V, modulate_vec<V>(xv, sv, hv, mean, rstd));
+        store_vec<V>(orow + v * V, modulate_vec<V, RMS>(xv, sv, hv, mean, rstd));
       }
     }
   }
@@ -396,21 +432,21 @@ inline unsigned grid_for(int64_t R) {
   return (unsigned)std::min(blocks, kMaxBlocks);
 }
 
-template <int V, int NV, bool GATHER>
+template <int V, int NV, bool GATHER, bool RMS>
 int launch_rows(const LnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ln_modulate_rows<V, NV, GATHER>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ln_modulate_rows<V, NV, GATHER, RMS>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int V, bool GATHER>
+template <int V, bool GATHER, bool RMS>
 int launch_stream(const LnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ln_modulate_stream<V, GATHER>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ln_modulate_stream<V, GATHER, RMS>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
 
-template <int V, int NV, bool UNIF>
+template <int V, int NV, bool UNIF, bool RMS>
 int launch_tab(const LnArgs& a, hipStream_t st) {
   // TabShape<NV>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
   const int64_t B = a.R / a.S;
@@ -420,30 +456,31 @@ int launch_tab(const LnArgs& a, hipStream_t st) {
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
   const int64_t blocks = B * bpb;
   const size_t lds = (size_t)2 * a.D * sizeof(float);
-  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)blocks), dim3(256), lds, st, a,
+  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS>), dim3((unsigned)blocks), dim3(256), lds, st, a,
                      (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int NV, bool UNIF>
+template <int NV, bool UNIF, bool RMS>
 int launch_tr(const LnArgs& a, hipStream_t st) {
   const int64_t B = a.R / a.S;
   const int64_t tiles_per_sample = a.S / kTrTokens;
   const int64_t nvec = a.D / 8;
   const size_t lds = (size_t)nvec * (4 * sizeof(float4) + kTrTokens * sizeof(uint4));
-  hipLaunchKernelGGL((ln_modulate_tr<NV, UNIF>), dim3((unsigned)(B * tiles_per_sample)), dim3(512),
+  hipLaunchKernelGGL((ln_modulate_tr<NV, UNIF, RMS>), dim3((unsigned)(B * tiles_per_sample)), dim3(512),
                      lds, st, a, (int)tiles_per_sample);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 constexpr int kTrMaxD = 4096;  // 96 KiB of LDS (tables + tile)
 
+template <bool RMS>
 int dispatch_tr(const LnArgs& a, hipStream_t st) {
   const int64_t nvec = a.D / 8;
   const int64_t nv = (nvec + kWave - 1) / kWave;
   const bool unif = nvec % kWave == 0;
 #define ADALN_TR_CASE(N) \
-  if (nv == N) return unif ? launch_tr<N, true>(a, st) : launch_tr<N, false>(a, st);
+  if (nv == N) return unif ? launch_tr<N, true, RMS>(a, st) : launch_tr<N, false, RMS>(a, st);
   ADALN_TR_CASE(1)
   ADALN_TR_CASE(2)
   ADALN_TR_CASE(3)
@@ -456,13 +493,13 @@ int dispatch_tr(const LnArgs& a, hipStream_t st) {
   return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
 }
 
-template <int V>
+template <int V, bool RMS>
 int dispatch_tab(const LnArgs& a, hipStream_t st) {
   const int64_t nvec = a.D / V;
   const int64_t nv = (nvec + kWave - 1) / kWave;
   const bool unif = nvec % kWave == 0;
 #define ADALN_TAB_CASE(N)                                                           \
-  if (nv == N) return unif ? launch_tab<V, N, true>(a, st) : launch_tab<V, N, false>(a, st);
+  if (nv == N) return unif ? launch_tab<V, N, true, RMS>(a, st) : launch_tab<V, N, false, RMS>(a, st);
   ADALN_TAB_CASE(1)
   ADALN_TAB_CASE(2)
   ADALN_TAB_CASE(3)
@@ -484,11 +521,11 @@ int dispatch_tab(const LnArgs& a, hipStream_t st) {
 }
 
 // vectors per lane -> the register-resident instantiation that covers it
-template <int V, bool GATHER>
+template <int V, bool GATHER, bool RMS>
 int dispatch(const LnArgs& a, hipStream_t st) {
   const int64_t nv = (a.D / V + kWave - 1) / kWave;
 #define ADALN_NV_CASE(N) \
-  if (nv <= N) return launch_rows<V, N, GATHER>(a, st);
+  if (nv <= N) return launch_rows<V, N, GATHER, RMS>(a, st);
   ADALN_NV_CASE(1)
   ADALN_NV_CASE(2)
   ADALN_NV_CASE(3)
@@ -500,7 +537,7 @@ int dispatch(const LnArgs& a, hipStream_t st) {
   ADALN_NV_CASE(12)
   ADALN_NV_CASE(16)
 #undef ADALN_NV_CASE
-  return launch_stream<V, GATHER>(a, st);
+  return launch_stream<V, GATHER, RMS>(a, st);
 }
 
 }  // namespace
@@ -522,19 +559,13 @@ static int ln_modulate_check_shape(int64_t B, int64_t S, int64_t D, int64_t sx_b
   return ADALN_OK;
 }
 
-}  // namespace adaln
-
-using namespace adaln;
-
-extern "C" int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
-                                   int64_t sx_d, int64_t sscale_b, int64_t sshift_b, int dtype) {
-  return ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype) == ADALN_OK;
-}
-
-extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
-                           int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
-                           const void* shift, int64_t sshift_b, float eps, int dtype, void* out,
-                           float* mean_out, float* rstd_out, void* stream) {
+// The entry point of both norms: validation, aliasing rules, then the
+// kernel family the layout selects (RMS: RMSNorm statistics, no mean).
+template <bool RMS>
+static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                         int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                         int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                         float* rstd_out, void* stream) {
   int rc = ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype);
   if (rc != ADALN_OK) return rc;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return ADALN_ERR_ARG;  // also rejects NaN
@@ -577,7 +608,7 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
   a.R = R;
 
   int V = 0;
-  order_for(ADALN_OP_LN_MODULATE, D, &V, nullptr);
+  order_for(RMS ? ADALN_OP_RMSNORM_SCALE_SHIFT : ADALN_OP_LN_MODULATE, D, &V, nullptr);
   // vector loads need every row start of x, scale, shift and out on a 2V-byte boundary
   const uintptr_t vb = (uintptr_t)(2 * V);
   auto stride_ok = [&](int64_t n, int64_t st) { return n <= 1 || ((uintptr_t)st * 2u) % vb == 0; };
@@ -588,13 +619,44 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
   // the tabled fast path indexes rows, samples and offsets in 32 bits
   const bool tab = vec && D <= kTabMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
                    B <= INT32_MAX;
-  if (tab) return V == 8 ? dispatch_tab<8>(a, st) : dispatch_tab<4>(a, st);
+  if (tab) return V == 8 ? dispatch_tab<8, RMS>(a, st) : dispatch_tab<4, RMS>(a, st);
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
                   B * (S / kTrTokens) < INT32_MAX && aligned(x, 16) && sx_d % 8 == 0 &&
                   (B == 1 || sx_b % 8 == 0) && aligned(scale, 16) && aligned(shift, 16) &&
                   aligned(out, 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
-  if (tr) return dispatch_tr(a, st);
-  if (V == 8) return vec ? dispatch<8, false>(a, st) : dispatch<8, true>(a, st);
-  return vec ? dispatch<4, false>(a, st) : dispatch<4, true>(a, st);
+  if (tr) return dispatch_tr<RMS>(a, st);
+  if (V == 8) return vec ? dispatch<8, false, RMS>(a, st) : dispatch<8, true, RMS>(a, st);
+  return vec ? dispatch<4, false, RMS>(a, st) : dispatch<4, true, RMS>(a, st);
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                   int64_t sx_d, int64_t sscale_b, int64_t sshift_b, int dtype) {
+  return ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype) == ADALN_OK;
+}
+
+extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                           int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
+                           const void* shift, int64_t sshift_b, float eps, int dtype, void* out,
+                           float* mean_out, float* rstd_out, void* stream) {
+  return norm_modulate<false>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b, eps,
+                              dtype, out, mean_out, rstd_out, stream);
+}
+
+extern "C" int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                                           int64_t sx_s, int64_t sx_d, int64_t sscale_b,
+                                           int64_t sshift_b, int dtype) {
+  return ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype) == ADALN_OK;
+}
+
+extern "C" int rmsnorm_scale_shift(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                                   int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
+                                   const void* shift, int64_t sshift_b, float eps, int dtype,
+                                   void* out, float* rinv_out, void* stream) {
+  return norm_modulate<true>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b, eps,
+                             dtype, out, nullptr, rinv_out, stream);
 }

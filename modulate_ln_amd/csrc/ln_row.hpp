@@ -21,6 +21,22 @@ __device__ __forceinline__ void push_f32(const float* xk, float& mean, float& m2
   (welford_push<K * V + E + 1>(mean, m2, xk[E]), ...);
 }
 
+template <int V, int... E>
+__device__ __forceinline__ void sumsq_f32(const float* xk, float& ss, std::integer_sequence<int, E...>) {
+  ((ss = __builtin_fmaf(xk[E], xk[E], ss)), ...);
+}
+
+// RMSNorm's per-lane sum of squares, same element order as the Welford pass
+template <int V, bool UNIF, int... K>
+__device__ __forceinline__ void sumsq_lane_f32(const float (*xf)[V], int nvec, int lane, float& ss,
+                                               std::integer_sequence<int, K...>) {
+  (
+      [&] {
+        if (UNIF || K * kWave + lane < nvec) sumsq_f32<V>(xf[K], ss, std::make_integer_sequence<int, V>{});
+      }(),
+      ...);
+}
+
 template <int V, bool UNIF, int... K>
 __device__ __forceinline__ void welford_f32(const float (*xf)[V], int nvec, int lane, float& mean,
                                             float& m2, std::integer_sequence<int, K...>) {
@@ -85,12 +101,15 @@ __device__ __forceinline__ void build_gate_table(float4* tab, const uint16_t* gt
 }
 
 // One row, held by one wave as NV packed vectors per lane (lane l owns
-// vectors l, l + 64, ...): Welford, merge tree, statistics, then
-// normalize, modulate with the LDS tables and store (non-temporal).
+// vectors l, l + 64, ...): statistics (Welford for LayerNorm, the sum of
+// squares for RMSNorm), merge tree, then normalize, modulate with the LDS
+// tables and store (non-temporal).  LayerNorm normalizes (x - mean) * rstd,
+// RMSNorm x * rinv with rinv = 1/sqrt(mean(x^2) + eps) (written to
+// rstd_out; mean_out is unused).
 // kXf32: widen the row once and keep it in fp32 for both passes; otherwise
 // widen it for the reduction and again (opaque to the compiler, so no fp32
 // copy stays live) when normalizing.
-template <int V, int NV, bool UNIF, bool kXf32>
+template <int V, int NV, bool UNIF, bool kXf32, bool RMS = false>
 __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* tab, int nvec, int lane,
                                               float Df, float eps, uint16_t* orow, float* mean_out,
                                               float* rstd_out) {
@@ -108,8 +127,16 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     return (e & 1) ? hi_f32_again(buf[k].w[e / 2]) : lo_f32_again(buf[k].w[e / 2]);
   };
   float mean = 0.0f, m2 = 0.0f;
-  welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
-  if constexpr (UNIF) {
+  if constexpr (RMS) {
+    sumsq_lane_f32<V, UNIF>(xf, nvec, lane, m2, std::make_integer_sequence<int, NV>{});
+    sum_down<1>(m2);
+    sum_down<2>(m2);
+    sum_down<4>(m2);
+    sum_down<8>(m2);
+    sum_down<16>(m2);
+    sum_down<32>(m2);
+  } else if constexpr (UNIF) {
+    welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
     const float c = (float)(NV * V);
     merge_down_equal<1>(mean, m2, c);
     merge_down_equal<2>(mean, m2, c);
@@ -118,6 +145,7 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     merge_down_equal<16>(mean, m2, c);
     merge_down_equal<32>(mean, m2, c);
   } else {
+    welford_f32<V, UNIF>(xf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
     float n = (float)((nvec / kWave + (lane < nvec % kWave ? 1 : 0)) * V);
     merge_down<1>(mean, m2, n);
     merge_down<2>(mean, m2, n);
@@ -126,11 +154,11 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     merge_down<16>(mean, m2, n);
     merge_down<32>(mean, m2, n);
   }
-  mean = bcast_lane0(mean);
+  if constexpr (!RMS) mean = bcast_lane0(mean);
   m2 = bcast_lane0(m2);
   const float rstd = finalize_rstd(m2, Df, eps);
   if (lane == 0) {
-    if (mean_out) *mean_out = mean;
+    if (!RMS && mean_out) *mean_out = mean;
     if (rstd_out) *rstd_out = rstd;
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -160,9 +188,19 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
       Vec<V> o;
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) {
-        float n0 = (xval(k, 4 * q) - mean) * rstd, n1 = (xval(k, 4 * q + 1) - mean) * rstd;
-        float n2 = (xval(k, 4 * q + 2) - mean) * rstd, n3 = (xval(k, 4 * q + 3) - mean) * rstd;
-        round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean))
+        float n0, n1, n2, n3;
+        if constexpr (RMS) {
+          n0 = xval(k, 4 * q) * rstd;
+          n1 = xval(k, 4 * q + 1) * rstd;
+          n2 = xval(k, 4 * q + 2) * rstd;
+          n3 = xval(k, 4 * q + 3) * rstd;
+        } else {
+          n0 = (xval(k, 4 * q) - mean) * rstd;
+          n1 = (xval(k, 4 * q + 1) - mean) * rstd;
+          n2 = (xval(k, 4 * q + 2) - mean) * rstd;
+          n3 = (xval(k, 4 * q + 3) - mean) * rstd;
+        }
+        round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean)), or bf16(x * rinv)
         round_pair(n2, n3);
         float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
         round_pair(y0, y1);  // bf16(x_hat * (1 + scale))

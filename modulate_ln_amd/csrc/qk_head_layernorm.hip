@@ -6,6 +6,11 @@
 // both q and k).  The affine LayerNorm is one eager op, so the output is
 // rounded to bf16 once: out = bf16(fma(w, (x - mean) * rstd, b)).
 //
+// qk_rmsnorm ("Fused Kernels" page, table "Normalization": qk_rmsnorm_native,
+// per-head QK RMSNorm, bit-exact) is the same kernel family with RMSNorm
+// statistics: out = bf16((x * rinv) * w), each product rounded to fp32 --
+// torch's rms_norm is one op, computed in fp32 and rounded once.
+//
 // Design: a head row (Dh <= 256) is small, so 16 lanes -- one DPP row --
 // own a head and a wave normalizes four heads at once.  Lane l of the group
 // owns vectors l, l+16, ... (16-byte loads for V = 8); the merge tree is the
@@ -64,9 +69,26 @@ __device__ __forceinline__ void welford_lane(const Vec<V>* buf, int64_t nvec, in
       ...);
 }
 
+// RMSNorm: the lane's sum of squares, same element order as welford_lane
+template <int V, int K, int... E>
+__device__ __forceinline__ void sumsq_vec(const Vec<V>& v, float& ss, std::integer_sequence<int, E...>) {
+  ((ss = __builtin_fmaf(elem<V, E>(v), elem<V, E>(v), ss)), ...);
+}
+
+template <int V, int... K>
+__device__ __forceinline__ void sumsq_lane(const Vec<V>* buf, int64_t nvec, int l16, float& ss,
+                                           std::integer_sequence<int, K...>) {
+  (
+      [&] {
+        if ((int64_t)K * kGroup + l16 < nvec) sumsq_vec<V, K>(buf[K], ss, std::make_integer_sequence<int, V>{});
+      }(),
+      ...);
+}
+
 // UNIFORM: head rows of a side sit at a constant stride s_h (q viewed as
 // [B*S*H, Dh]); otherwise the row index is decomposed into (b, s, h).
-template <int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
+// RMS: RMSNorm statistics (sum of squares), x * rinv, weight only.
+template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
 __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int l16 = lane & (kGroup - 1);
@@ -98,9 +120,14 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
     }
 
     float mean = 0.0f, m2 = 0.0f;
-    welford_lane<V>(buf, nvec, l16, mean, m2, std::make_integer_sequence<int, NV>{});
-    float n = (float)(nv_lane * V);
-    merge_lanes<kGroup>(mean, m2, n, lane);
+    if constexpr (RMS) {
+      sumsq_lane<V>(buf, nvec, l16, m2, std::make_integer_sequence<int, NV>{});
+      sum_lanes<kGroup>(m2);
+    } else {
+      welford_lane<V>(buf, nvec, l16, mean, m2, std::make_integer_sequence<int, NV>{});
+      float n = (float)(nv_lane * V);
+      merge_lanes<kGroup>(mean, m2, n, lane);
+    }
     const float rstd = finalize_rstd(m2, Df, a.eps);
 
     uint16_t* orow = sd.out + rr * a.Dh;
@@ -112,13 +139,17 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
         Vec<V> wv, bv;
         if constexpr (AFFINE) {
           wv = GATHER ? gather_vec<V>(sd.w + v * V, 1) : load_vec<V>(sd.w + v * V);
-          bv = GATHER ? gather_vec<V>(sd.bias + v * V, 1) : load_vec<V>(sd.bias + v * V);
+          if constexpr (!RMS)
+            bv = GATHER ? gather_vec<V>(sd.bias + v * V, 1) : load_vec<V>(sd.bias + v * V);
         }
 #pragma unroll
         for (int i = 0; i < V / 2; ++i) {
-          float y0 = (lo_f32(buf[k].w[i]) - mean) * rstd;
-          float y1 = (hi_f32(buf[k].w[i]) - mean) * rstd;
-          if constexpr (AFFINE) {
+          float y0 = RMS ? lo_f32(buf[k].w[i]) * rstd : (lo_f32(buf[k].w[i]) - mean) * rstd;
+          float y1 = RMS ? hi_f32(buf[k].w[i]) * rstd : (hi_f32(buf[k].w[i]) - mean) * rstd;
+          if constexpr (AFFINE && RMS) {
+            y0 = y0 * lo_f32(wv.w[i]);
+            y1 = y1 * hi_f32(wv.w[i]);
+          } else if constexpr (AFFINE) {
             y0 = __builtin_fmaf(lo_f32(wv.w[i]), y0, lo_f32(bv.w[i]));
             y1 = __builtin_fmaf(hi_f32(wv.w[i]), y1, hi_f32(bv.w[i]));
           }
@@ -134,7 +165,7 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
 }
 
 // Fast path: vector-aligned q/k.  HP heads per group per iteration.
-template <int V, int NV, int HP, bool UNIFORM, bool AFFINE, bool EQ>
+template <bool RMS, int V, int NV, int HP, bool UNIFORM, bool AFFINE, bool EQ>
 __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
   const QkSide& sd = a.side[blockIdx.y];
   const int lane = threadIdx.x & (kWave - 1);
@@ -154,13 +185,18 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const Vec<V> wv = load_vec<V>(sd.w + off[k]);
-      const Vec<V> bv = load_vec<V>(sd.bias + off[k]);
 #pragma unroll
       for (int i = 0; i < V / 2; ++i) {
         wf[k][2 * i] = lo_f32(wv.w[i]);
         wf[k][2 * i + 1] = hi_f32(wv.w[i]);
-        bf[k][2 * i] = lo_f32(bv.w[i]);
-        bf[k][2 * i + 1] = hi_f32(bv.w[i]);
+      }
+      if constexpr (!RMS) {
+        const Vec<V> bv = load_vec<V>(sd.bias + off[k]);
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) {
+          bf[k][2 * i] = lo_f32(bv.w[i]);
+          bf[k][2 * i + 1] = hi_f32(bv.w[i]);
+        }
       }
     }
   }
@@ -184,11 +220,15 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
       float mean = 0.0f, m2 = 0.0f;
-      welford_lane<V>(buf[i], EQ ? (int64_t)NV * kGroup : (int64_t)nvec, l16, mean, m2,
+      if constexpr (RMS) {
+        sumsq_lane<V>(buf[i], EQ ? (int64_t)NV * kGroup : (int64_t)nvec, l16, m2,
                       std::make_integer_sequence<int, NV>{});
-      if constexpr (EQ) {
+        sum_lanes<kGroup>(m2);
+      } else if constexpr (EQ) {
+        welford_lane<V>(buf[i], (int64_t)NV * kGroup, l16, mean, m2, std::make_integer_sequence<int, NV>{});
         merge_lanes16_equal(mean, m2, (float)(NV * V), lane);
       } else {
+        welford_lane<V>(buf[i], (int64_t)nvec, l16, mean, m2, std::make_integer_sequence<int, NV>{});
         float n = (float)(nv_lane * V);
         merge_lanes<kGroup>(mean, m2, n, lane);
       }
@@ -201,9 +241,12 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
             Vec<V> o;
 #pragma unroll
             for (int j = 0; j < V / 2; ++j) {
-              float y0 = (lo_f32(buf[i][k].w[j]) - mean) * rstd;
-              float y1 = (hi_f32(buf[i][k].w[j]) - mean) * rstd;
-              if constexpr (AFFINE) {
+              float y0 = RMS ? lo_f32(buf[i][k].w[j]) * rstd : (lo_f32(buf[i][k].w[j]) - mean) * rstd;
+              float y1 = RMS ? hi_f32(buf[i][k].w[j]) * rstd : (hi_f32(buf[i][k].w[j]) - mean) * rstd;
+              if constexpr (AFFINE && RMS) {
+                y0 = y0 * wf[k][2 * j];
+                y1 = y1 * wf[k][2 * j + 1];
+              } else if constexpr (AFFINE) {
                 y0 = __builtin_fmaf(wf[k][2 * j], y0, bf[k][2 * j]);
                 y1 = __builtin_fmaf(wf[k][2 * j + 1], y1, bf[k][2 * j + 1]);
               }
@@ -219,29 +262,30 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
 
 constexpr int kHeadsBlocksPerCu = 4;
 
-template <int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
+template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
 int launch_heads(const QkArgs& a, hipStream_t st) {
   constexpr int HP = NV == 1 ? 4 : (NV == 2 ? 2 : 1);
   const int64_t need = (a.Rq + (int64_t)kGroupsPerBlock * HP - 1) / ((int64_t)kGroupsPerBlock * HP);
   const int cus = cu_count();
   const int64_t target = (int64_t)kHeadsBlocksPerCu * (cus > 0 ? cus : 256) / 2;  // per side
   const int64_t gx = std::max<int64_t>(1, std::min(need, target));
-  hipLaunchKernelGGL((qk_heads<V, NV, HP, UNIFORM, AFFINE, EQ>), dim3((unsigned)gx, 2), dim3(256), 0,
+  hipLaunchKernelGGL((qk_heads<RMS, V, NV, HP, UNIFORM, AFFINE, EQ>), dim3((unsigned)gx, 2), dim3(256), 0,
                      st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int V, int NV, bool UNIFORM, bool AFFINE>
+template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE>
 int pick_eq(const QkArgs& a, hipStream_t st) {
   const bool eq = (a.Dh / V) == (int64_t)NV * kGroup;
-  return eq ? launch_heads<V, NV, UNIFORM, AFFINE, true>(a, st)
-            : launch_heads<V, NV, UNIFORM, AFFINE, false>(a, st);
+  return eq ? launch_heads<RMS, V, NV, UNIFORM, AFFINE, true>(a, st)
+            : launch_heads<RMS, V, NV, UNIFORM, AFFINE, false>(a, st);
 }
 
-template <int V, int NV>
+template <bool RMS, int V, int NV>
 int dispatch_heads(const QkArgs& a, bool uniform, bool affine, hipStream_t st) {
-  if (uniform) return affine ? pick_eq<V, NV, true, true>(a, st) : pick_eq<V, NV, true, false>(a, st);
-  return affine ? pick_eq<V, NV, false, true>(a, st) : pick_eq<V, NV, false, false>(a, st);
+  if (uniform)
+    return affine ? pick_eq<RMS, V, NV, true, true>(a, st) : pick_eq<RMS, V, NV, true, false>(a, st);
+  return affine ? pick_eq<RMS, V, NV, false, true>(a, st) : pick_eq<RMS, V, NV, false, false>(a, st);
 }
 
 inline unsigned grid_for(int64_t heads) {
@@ -249,29 +293,29 @@ inline unsigned grid_for(int64_t heads) {
   return (unsigned)std::min(blocks, kMaxBlocks);
 }
 
-template <int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
+template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool GATHER>
 int launch(const QkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((qk_rows<V, NV, UNIFORM, AFFINE, GATHER>), dim3(grid_for(2 * a.Rq)), dim3(256),
+  hipLaunchKernelGGL((qk_rows<RMS, V, NV, UNIFORM, AFFINE, GATHER>), dim3(grid_for(2 * a.Rq)), dim3(256),
                      0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int V, int NV, bool UNIFORM, bool AFFINE>
+template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE>
 int pick_gather(const QkArgs& a, bool gather, hipStream_t st) {
-  return gather ? launch<V, NV, UNIFORM, AFFINE, true>(a, st)
-                : launch<V, NV, UNIFORM, AFFINE, false>(a, st);
+  return gather ? launch<RMS, V, NV, UNIFORM, AFFINE, true>(a, st)
+                : launch<RMS, V, NV, UNIFORM, AFFINE, false>(a, st);
 }
 
-template <int V, int NV, bool UNIFORM>
+template <bool RMS, int V, int NV, bool UNIFORM>
 int pick_affine(const QkArgs& a, bool affine, bool gather, hipStream_t st) {
-  return affine ? pick_gather<V, NV, UNIFORM, true>(a, gather, st)
-                : pick_gather<V, NV, UNIFORM, false>(a, gather, st);
+  return affine ? pick_gather<RMS, V, NV, UNIFORM, true>(a, gather, st)
+                : pick_gather<RMS, V, NV, UNIFORM, false>(a, gather, st);
 }
 
-template <int V, int NV>
+template <bool RMS, int V, int NV>
 int pick_uniform(const QkArgs& a, bool uniform, bool affine, bool gather, hipStream_t st) {
-  return uniform ? pick_affine<V, NV, true>(a, affine, gather, st)
-                 : pick_affine<V, NV, false>(a, affine, gather, st);
+  return uniform ? pick_affine<RMS, V, NV, true>(a, affine, gather, st)
+                 : pick_affine<RMS, V, NV, false>(a, affine, gather, st);
 }
 
 }  // namespace
@@ -291,28 +335,21 @@ static int qk_check_shape(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t s
   return ADALN_OK;
 }
 
-}  // namespace adaln
-
-using namespace adaln;
-
-extern "C" int qk_head_layernorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b,
-                                         int64_t sq_s, int64_t sq_h, int64_t sk_b, int64_t sk_s,
-                                         int64_t sk_h, int dtype) {
-  return qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype) == ADALN_OK;
-}
-
-extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h,
-                                 const void* k, int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B,
-                                 int64_t S, int64_t H, int64_t Dh, const void* wq, const void* bq,
-                                 const void* wk, const void* bk, float eps, int dtype, void* q_out,
-                                 void* k_out, void* stream) {
+// The entry point of both per-head norms (RMS: RMSNorm with an optional
+// weight and no bias; bq and bk are then NULL).
+template <bool RMS>
+static int qk_norm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h, const void* k,
+                   int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B, int64_t S, int64_t H,
+                   int64_t Dh, const void* wq, const void* bq, const void* wk, const void* bk,
+                   float eps, int dtype, void* q_out, void* k_out, void* stream) {
   int rc = qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype);
   if (rc != ADALN_OK) return rc;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return ADALN_ERR_ARG;
   const int64_t R = B * S * H;
   if (R == 0) return ADALN_OK;
   if (!q || !k || !q_out || !k_out) return ADALN_ERR_NULL;
-  if ((wq == nullptr) != (bq == nullptr) || (wk == nullptr) != (bk == nullptr)) return ADALN_ERR_NULL;
+  if (!RMS && ((wq == nullptr) != (bq == nullptr) || (wk == nullptr) != (bk == nullptr)))
+    return ADALN_ERR_NULL;
   if ((wq == nullptr) != (wk == nullptr)) return ADALN_ERR_NULL;  // affine on both sides or neither
   const bool affine = wq != nullptr;
   for (const void* p : {q, k, (const void*)q_out, (const void*)k_out, wq, bq, wk, bk})
@@ -331,6 +368,7 @@ extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int6
   if (overlaps(sqo, sk) || overlaps(sko, sq)) return ADALN_ERR_ALIAS;
   if (affine) {
     for (const void* p : {wq, bq, wk, bk}) {
+      if (!p) continue;
       const Span sw = span_of(p, {{Dh, 1}});
       if (overlaps(sw, sqo) || overlaps(sw, sko)) return ADALN_ERR_ALIAS;
     }
@@ -348,7 +386,7 @@ extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int6
   a.eps = eps;
 
   int V = 0;
-  order_for(ADALN_OP_QK_HEAD_LAYERNORM, Dh, &V, nullptr);
+  order_for(RMS ? ADALN_OP_QK_RMSNORM : ADALN_OP_QK_HEAD_LAYERNORM, Dh, &V, nullptr);
   const uintptr_t vb = (uintptr_t)(2 * V);
   auto st_ok = [&](int64_t n, int64_t s) { return n <= 1 || ((uintptr_t)s * 2u) % vb == 0; };
   bool vec = true;
@@ -372,17 +410,50 @@ extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int6
   const bool gather = !vec;
   const int64_t nv = (Dh / V + kGroup - 1) / kGroup;
   if (vec) {
-    if (V == 8) return nv <= 1 ? dispatch_heads<8, 1>(a, uniform, affine, st)
-                               : dispatch_heads<8, 2>(a, uniform, affine, st);
-    if (nv <= 1) return dispatch_heads<4, 1>(a, uniform, affine, st);
-    if (nv <= 2) return dispatch_heads<4, 2>(a, uniform, affine, st);
-    return dispatch_heads<4, 4>(a, uniform, affine, st);
+    if (V == 8) return nv <= 1 ? dispatch_heads<RMS, 8, 1>(a, uniform, affine, st)
+                               : dispatch_heads<RMS, 8, 2>(a, uniform, affine, st);
+    if (nv <= 1) return dispatch_heads<RMS, 4, 1>(a, uniform, affine, st);
+    if (nv <= 2) return dispatch_heads<RMS, 4, 2>(a, uniform, affine, st);
+    return dispatch_heads<RMS, 4, 4>(a, uniform, affine, st);
   }
   if (V == 8) {
-    if (nv <= 1) return pick_uniform<8, 1>(a, uniform, affine, gather, st);
-    return pick_uniform<8, 2>(a, uniform, affine, gather, st);
+    if (nv <= 1) return pick_uniform<RMS, 8, 1>(a, uniform, affine, gather, st);
+    return pick_uniform<RMS, 8, 2>(a, uniform, affine, gather, st);
   }
-  if (nv <= 1) return pick_uniform<4, 1>(a, uniform, affine, gather, st);
-  if (nv <= 2) return pick_uniform<4, 2>(a, uniform, affine, gather, st);
-  return pick_uniform<4, 4>(a, uniform, affine, gather, st);
+  if (nv <= 1) return pick_uniform<RMS, 4, 1>(a, uniform, affine, gather, st);
+  if (nv <= 2) return pick_uniform<RMS, 4, 2>(a, uniform, affine, gather, st);
+  return pick_uniform<RMS, 4, 4>(a, uniform, affine, gather, st);
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int qk_head_layernorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b,
+                                         int64_t sq_s, int64_t sq_h, int64_t sk_b, int64_t sk_s,
+                                         int64_t sk_h, int dtype) {
+  return qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype) == ADALN_OK;
+}
+
+extern "C" int qk_head_layernorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h,
+                                 const void* k, int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B,
+                                 int64_t S, int64_t H, int64_t Dh, const void* wq, const void* bq,
+                                 const void* wk, const void* bk, float eps, int dtype, void* q_out,
+                                 void* k_out, void* stream) {
+  return qk_norm<false>(q, sq_b, sq_s, sq_h, k, sk_b, sk_s, sk_h, B, S, H, Dh, wq, bq, wk, bk, eps,
+                        dtype, q_out, k_out, stream);
+}
+
+extern "C" int qk_rmsnorm_can_use(int64_t B, int64_t S, int64_t H, int64_t Dh, int64_t sq_b,
+                                  int64_t sq_s, int64_t sq_h, int64_t sk_b, int64_t sk_s,
+                                  int64_t sk_h, int dtype) {
+  return qk_check_shape(B, S, H, Dh, sq_b, sq_s, sq_h, sk_b, sk_s, sk_h, dtype) == ADALN_OK;
+}
+
+extern "C" int qk_rmsnorm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h, const void* k,
+                          int64_t sk_b, int64_t sk_s, int64_t sk_h, int64_t B, int64_t S, int64_t H,
+                          int64_t Dh, const void* wq, const void* wk, float eps, int dtype,
+                          void* q_out, void* k_out, void* stream) {
+  return qk_norm<true>(q, sq_b, sq_s, sq_h, k, sk_b, sk_s, sk_h, B, S, H, Dh, wq, nullptr, wk,
+                       nullptr, eps, dtype, q_out, k_out, stream);
 }

@@ -92,6 +92,35 @@ def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: 
     return call if prepare else call()
 
 
+def rmsnorm_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
+                        out: torch.Tensor | None = None, rinv_out: torch.Tensor | None = None, stream=None,
+                        prepare: bool = False):
+    """RMSNorm(x) * (1 + scale) + shift with every eager bf16 rounding (x: [B,S,D], any strides)."""
+    _require(x, "x")
+    _require(scale, "scale")
+    _require(shift, "shift")
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D], got %s" % (tuple(x.shape),))
+    B, S, D = x.shape
+    scale, ssc = _rows_view(scale, B, D, "scale")
+    shift, ssh = _rows_view(shift, B, D, "shift")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, "out")
+        if tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B,S,D] tensor")
+    if rinv_out is not None and (rinv_out.dtype != torch.float32 or rinv_out.numel() != B * S
+                                 or not rinv_out.is_contiguous() or rinv_out.device != x.device):
+        raise ValueError("rinv_out must be a contiguous float32 tensor of B*S elements on x's device")
+    st = _stream_handle(x, stream)
+    call = Prepared("rmsnorm_scale_shift", N.lib().rmsnorm_scale_shift, (
+        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
+        rinv_out.data_ptr() if rinv_out is not None else None, st), out)
+    return call if prepare else call()
+
+
 def residual_gate_add(residual: torch.Tensor, gate: torch.Tensor, update: torch.Tensor, *,
                       out: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """residual + gate * update with the eager roundings (residual/update [B,S,D], gate [B,D])."""
@@ -200,6 +229,42 @@ def qk_head_layernorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None 
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         B, S, H, Dh, ptr(wq), ptr(bq), ptr(wk), ptr(bk), float(eps), N.BF16,
         q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out))
+    return call if prepare else call()
+
+
+def qk_rmsnorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None = None, wk: torch.Tensor | None = None,
+               eps: float = 1e-6, *, q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None,
+               stream=None, prepare: bool = False):
+    """Per-head RMSNorm of q and k ([B,S,H,Dh] each) with optional weights, one launch."""
+    _require(q, "q")
+    _require(k, "k")
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must both be [B,S,H,Dh]")
+    B, S, H, Dh = q.shape
+    for name, t in (("q", q), ("k", k)):
+        if Dh > 1 and t.stride(3) != 1:
+            raise ValueError("%s must have unit stride along head_dim" % name)
+    if (wq is None) != (wk is None):
+        raise ValueError("wq and wk go together (both or none)")
+    for name, w in (("wq", wq), ("wk", wk)):
+        if w is not None:
+            _require(w, name)
+            if w.numel() != Dh or not w.is_contiguous():
+                raise ValueError("%s must be a contiguous [Dh] tensor" % name)
+    if q_out is None:
+        q_out = torch.empty((B, S, H, Dh), dtype=torch.bfloat16, device=q.device)
+    if k_out is None:
+        k_out = torch.empty((B, S, H, Dh), dtype=torch.bfloat16, device=q.device)
+    for name, t in (("q_out", q_out), ("k_out", k_out)):
+        _require(t, name)
+        if tuple(t.shape) != (B, S, H, Dh) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous [B,S,H,Dh] tensor" % name)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    st = _stream_handle(q, stream)
+    call = Prepared("qk_rmsnorm", N.lib().qk_rmsnorm, (
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        B, S, H, Dh, ptr(wq), ptr(wk), float(eps), N.BF16, q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out))
     return call if prepare else call()
 
 

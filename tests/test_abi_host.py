@@ -59,6 +59,8 @@ def test_order_for(D, V):
     assert N.order_for(N.OP_LN_MODULATE, D) == (V, 64)
     assert N.order_for(N.OP_QK_HEAD_LAYERNORM, D) == (V, 16)
     assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D) == (V, 64)
+    assert N.order_for(N.OP_RMSNORM_SCALE_SHIFT, D) == (V, 64)
+    assert N.order_for(N.OP_QK_RMSNORM, D) == (V, 16)
 
 
 @pytest.mark.parametrize("D", [0, -4, 6, 2242])
@@ -226,3 +228,45 @@ def test_fused_residual_rejections(L):
     assert fz(mean=P6 + 8) == N.ERR_ALIAS  # stats over out
     assert fz(mean=P7, rstd=P7 + 8) == N.ERR_ALIAS
     assert fz(res=None, gate=None, upd=None, scale=None, shift=None, ro=None, out=None, S=0) == N.OK
+
+
+def test_rms_can_use(L):
+    ok = lambda *a: L.rmsnorm_scale_shift_can_use(*a, N.BF16)  # noqa: E731
+    assert ok(1, 4096, 4096, 4096 * 4096, 4096, 1, 4096, 4096)
+    assert ok(2, 1024, 2240, 2240 * 1024, 1, 1024, 13440, 13440)
+    assert not ok(1, 1, 6, 0, 6, 1, 0, 0)
+    assert not ok(1, 1, 65540, 0, 65540, 1, 0, 0)
+    assert L.qk_rmsnorm_can_use(1, 4360, 32, 128, 4360 * 4096, 4096, 128, 4360 * 4096, 4096, 128, N.BF16)
+    assert not L.qk_rmsnorm_can_use(1, 2, 3, 260, 1560, 780, 260, 1560, 780, 260, N.BF16)
+    assert not L.qk_rmsnorm_can_use(1, 2, 3, 128, 768, 384, 128, 768, 384, 128, 0)
+
+
+def test_rms_rejections(L):
+    def rms(x=P0, B=1, S=4, D=8, sx=None, scale=P1, ssc=8, shift=P2, ssh=8, eps=1e-6, dtype=N.BF16, out=P3,
+            rinv=None):
+        sx_b, sx_s, sx_d = sx if sx is not None else (S * D, D, 1)
+        return L.rmsnorm_scale_shift(x, B, S, D, sx_b, sx_s, sx_d, scale, ssc, shift, ssh, eps, dtype, out, rinv,
+                                     None)
+
+    assert rms(dtype=0) == N.ERR_DTYPE
+    assert rms(D=10) == N.ERR_SHAPE
+    assert rms(eps=-1.0) == N.ERR_ARG
+    assert rms(shift=None) == N.ERR_NULL
+    assert rms(out=P3 + 1) == N.ERR_ALIGN
+    assert rms(out=P0 + 16) == N.ERR_ALIAS
+    assert rms(rinv=P3 + 8) == N.ERR_ALIAS
+    assert rms(x=None, scale=None, shift=None, out=None, B=0) == N.OK
+
+    def qk(q=P0, k=P1, wq=P2, wk=P2 + 1024, qo=P3, ko=P4, B=1, S=2, H=3, Dh=128, eps=1e-6, dtype=N.BF16):
+        sb, ss, sh = S * H * Dh, H * Dh, Dh
+        return L.qk_rmsnorm(q, sb, ss, sh, k, sb, ss, sh, B, S, H, Dh, wq, wk, eps, dtype, qo, ko, None)
+
+    assert qk(dtype=3) == N.ERR_DTYPE
+    assert qk(Dh=126) == N.ERR_SHAPE
+    assert qk(eps=float("nan")) == N.ERR_ARG
+    assert qk(k=None) == N.ERR_NULL
+    assert qk(wk=None) == N.ERR_NULL  # weight on one side only
+    assert qk(qo=P1) == N.ERR_ALIAS
+    assert qk(ko=P2 + 16) == N.ERR_ALIAS  # k_out over the weights
+    assert qk(wq=None, wk=None, qo=P3 + 1) == N.ERR_ALIGN
+    assert qk(q=None, k=None, qo=None, ko=None, B=0) == N.OK
