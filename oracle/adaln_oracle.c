@@ -469,6 +469,60 @@ int orc_residual_gate_add_ln_modulate(const uint16_t* res, const uint16_t* gate,
 }
 
 /* ------------------------------------------------------------------ */
+/* modulate_scale_shift: x * (1 + scale) + shift as eager bf16 ops      */
+/* ("Fused Kernels" page, table "adaLN modulation and gating";          */
+/* one affine row per token for LingBot World's camera conditioning):   */
+/* the modulate tail with x itself in place of the normalized value     */
+/* (rounding a bf16 value to bf16 changes nothing).  x [B*S, D]; scale  */
+/* and shift element (b,s,d) at base + b*s_b + s*s_s + d (s_s = 0: one  */
+/* row per sample).                                                      */
+/* ------------------------------------------------------------------ */
+
+int orc_modulate_scale_shift(const uint16_t* x, int64_t B, int64_t S, int64_t D, const uint16_t* scale,
+                             int64_t ssc_b, int64_t ssc_s, const uint16_t* shift, int64_t ssh_b, int64_t ssh_s,
+                             int mode, uint16_t* out) {
+  if (B < 0 || S < 0 || D < 0) return ORC_EINVAL;
+  if (mode != ORC_FP32_FIXED && mode != ORC_FP64_TWO_PASS) return ORC_EINVAL;
+  int64_t R = B * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t b = r / S, s = r % S;
+    const uint16_t* sc = scale + b * ssc_b + s * ssc_s;
+    const uint16_t* sh = shift + b * ssh_b + s * ssh_s;
+    for (int64_t j = 0; j < D; ++j) {
+      const uint16_t xv = x[r * D + j];
+      out[r * D + j] = mode == ORC_FP32_FIXED ? modulate_tail_f32(orc_f32_from_bf16(xv), sc[j], sh[j])
+                                              : modulate_tail_f64((double)orc_f32_from_bf16(xv), sc[j], sh[j]);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* temb_table_slices: the eager (table + temb.float()).chunk(nmod, dim=2)*/
+/* with every slice made contiguous ("Fused Kernels" page, table "adaLN  */
+/* modulation and gating", temb_table_slices and the note under it):    */
+/* out[m][b, l, d] = table[m, d] + float(temb[b, l, m, d]), one fp32    */
+/* addition.  table fp32 [nmod, D]; temb [B, L, nmod, D] contiguous,    */
+/* bf16 (temb_f32 = 0) or fp32; out fp32 [nmod, B, L, D].               */
+/* ------------------------------------------------------------------ */
+
+int orc_temb_table_slices(const float* table, const void* temb, int temb_f32, int64_t B, int64_t L, int64_t nmod,
+                          int64_t D, float* out) {
+  if (B < 0 || L < 0 || nmod < 0 || D < 0) return ORC_EINVAL;
+  int64_t R = B * L;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t m = 0; m < nmod; ++m)
+      for (int64_t d = 0; d < D; ++d) {
+        const int64_t i = (r * nmod + m) * D + d;
+        const float t = temb_f32 ? ((const float*)temb)[i] : orc_f32_from_bf16(((const uint16_t*)temb)[i]);
+        out[(m * R + r) * D + d] = table[m * D + d] + t;
+      }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* qk_head_layernorm: affine LayerNorm over each head row of Dh         */
 /* x [R, Dh]; w, b [Dh] or both NULL (no affine); out [R, Dh]           */
 /* One eager LayerNorm op, so one bf16 rounding at its output.          */

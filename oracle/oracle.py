@@ -92,6 +92,9 @@ def load_library(path: str):
                                             ctypes.c_int, ctypes.c_int, u16p, f64p]
     lib.orc_qk_rmsnorm.argtypes = [u16p, i64, i64, u16p, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, u16p]
+    lib.orc_modulate_scale_shift.argtypes = [u16p, i64, i64, i64, u16p, i64, i64, u16p, i64, i64, ctypes.c_int,
+                                             u16p]
+    lib.orc_temb_table_slices.argtypes = [f32p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64, f32p]
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
     lib.orc_get_threads.argtypes = []
@@ -242,6 +245,48 @@ def qk_rmsnorm(x, w, eps: float, mode: int, V: int = 8, L: int = 16):
     rc = _load().orc_qk_rmsnorm(_p(x, ctypes.c_uint16), R, Dh, _p(w, ctypes.c_uint16) if w is not None else None,
                                 eps, mode, V, L, _p(out, ctypes.c_uint16))
     _check(rc, "qk_rmsnorm")
+    return out
+
+
+def modulate_scale_shift(x, scale, shift, S: int, mode: int = FP32):
+    """out = bf16 chain of x*(1+scale)+shift.  x [B*S, D]; scale/shift [B, D] (one row per
+    sample) or [B*S, D] (one row per token), bf16 bits."""
+    x, scale, shift = _u16(x), _u16(scale), _u16(shift)
+    R, D = x.shape
+    B = R // S if S else 0
+
+    def strides(t):
+        if t.shape == (R, D):
+            return S * D, D
+        if t.shape[1] == D and t.shape[0] == B:
+            return D, 0
+        raise ValueError("scale/shift must be [B, D] or [B*S, D]")
+
+    ssc, ssh = strides(scale), strides(shift)
+    out = np.empty((R, D), dtype=np.uint16)
+    rc = _load().orc_modulate_scale_shift(_p(x, ctypes.c_uint16), B, S, D, _p(scale, ctypes.c_uint16), ssc[0],
+                                          ssc[1], _p(shift, ctypes.c_uint16), ssh[0], ssh[1], mode,
+                                          _p(out, ctypes.c_uint16))
+    _check(rc, "modulate_scale_shift")
+    return out
+
+
+def temb_table_slices(table, temb, temb_is_f32: bool = False):
+    """table fp32 [nmod, D]; temb [B, L, nmod, D] (bf16 bits as uint16, or float32) ->
+    out fp32 [nmod, B, L, D] with out[m] = table[m] + temb[:, :, m] in fp32."""
+    table = np.ascontiguousarray(table, dtype=np.float32)
+    nmod, D = table.shape
+    if temb_is_f32:
+        temb = np.ascontiguousarray(temb, dtype=np.float32)
+    else:
+        temb = _u16(temb)
+    B, L, m2, D2 = temb.shape
+    if (m2, D2) != (nmod, D):
+        raise ValueError("shape mismatch")
+    out = np.empty((nmod, B, L, D), dtype=np.float32)
+    rc = _load().orc_temb_table_slices(_p(table, ctypes.c_float), temb.ctypes.data_as(ctypes.c_void_p),
+                                       1 if temb_is_f32 else 0, B, L, nmod, D, _p(out, ctypes.c_float))
+    _check(rc, "temb_table_slices")
     return out
 
 

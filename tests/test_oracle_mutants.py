@@ -40,6 +40,9 @@ MUTANTS = {
     "rms_lane_sum_drops_partner": ("lane[l] = lane[l] + lane[l + off];", "lane[l] = lane[l];"),
     "fp64_tail_product_not_rounded": ("double y = rb64(xhat * one_plus);", "double y = xhat * one_plus;"),
     "qk_rms_rounds_before_weight": ("float y = w ? xn * orc_f32_from_bf16(w[j]) : xn;", "float y = w ? rb(xn) * orc_f32_from_bf16(w[j]) : xn;"),
+    "modulate_scale_row_per_sample": ("const uint16_t* sc = scale + b * ssc_b + s * ssc_s;", "const uint16_t* sc = scale + b * ssc_b;"),
+    "temb_slice_order_swapped": ("out[(m * R + r) * D + d] = table[m * D + d] + t;", "out[(r * nmod + m) * D + d] = table[m * D + d] + t;"),
+    "temb_table_row_wrong": ("out[(m * R + r) * D + d] = table[m * D + d] + t;", "out[(m * R + r) * D + d] = table[d] + t;"),
     "bias_not_rounded": ("double z = rb64((double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]));", "double z = (double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]);"),
 }
 
@@ -72,6 +75,9 @@ FAST_PINS = [
     lambda o: P.test_qk_rms_fp32_equals_torch_fp32_tail(o),
     lambda o: P.test_elementwise_tail_fp64_mode_equals_torch_eager(o, "layer"),
     lambda o: P.test_elementwise_tail_fp64_mode_equals_torch_eager(o, "rms"),
+    lambda o: P.test_modulate_worked(o, P.FP32),
+    lambda o: P.test_modulate_equals_torch_eager(o, P.FP32, True),
+    lambda o: P.test_temb_slices_equal_torch_chunks(o, False),
     lambda o: P.test_gelu_f64_vs_torch(o),
     lambda o: P.test_bias_gelu_rounds_after_bias(o),
 ]

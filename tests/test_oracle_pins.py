@@ -651,3 +651,61 @@ def test_elementwise_tail_fp64_mode_equals_torch_eager(orc, norm):
     xhat = W.from_bits(orc.bf16_from_f64(n.numpy()))
     eager = xhat * (1 + sc) + sh
     assert np.array_equal(out, bits_of(eager))
+
+
+# ---------------------------------------------------------------------------
+# modulate_scale_shift and temb_table_slices
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_modulate_worked(orc, mode):
+    """x = [1,2,3,4]: scale 1 doubles exactly and shift 0.5 is exact: [2.5, 4.5, 6.5, 8.5];
+    scale -1 leaves the shift; scale 0, shift 0 returns x (every step exact)."""
+    x = bf([[1.0, 2.0, 3.0, 4.0]])
+    out = orc.modulate_scale_shift(x, bf([[1.0] * 4]), bf([[0.5] * 4]), 1, mode)
+    assert f32(out).tolist() == [[2.5, 4.5, 6.5, 8.5]]
+    sh = bf([[0.5, -0.25, 2.0, -8.0]])
+    assert np.array_equal(orc.modulate_scale_shift(x, bf([[-1.0] * 4]), sh, 1, mode), sh)
+    assert np.array_equal(orc.modulate_scale_shift(x, bf([[0.0] * 4]), bf([[0.0] * 4]), 1, mode), x)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+@pytest.mark.parametrize("per_token", [False, True])
+def test_modulate_equals_torch_eager(orc, mode, per_token):
+    """x * (1 + scale) + shift as bf16 tensor ops on the CPU, adaLN rows per sample or per token."""
+    g = torch.Generator().manual_seed(40)
+    B, S, D = 3, 17, 520
+    x = (torch.randn(B, S, D, generator=g) * 3).to(torch.bfloat16)
+    shape = (B, S, D) if per_token else (B, 1, D)
+    sc = (torch.randn(*shape, generator=g) * 0.5).to(torch.bfloat16)
+    sh = (torch.randn(*shape, generator=g) * 0.5).to(torch.bfloat16)
+    eager = x * (1 + sc) + sh
+    rows = (lambda t: bits_of(t.reshape(B * S, D))) if per_token else (lambda t: bits_of(t[:, 0]))  # noqa: E731
+    out = orc.modulate_scale_shift(bits_of(x.reshape(B * S, D)), rows(sc), rows(sh), S, mode)
+    assert np.array_equal(out, bits_of(eager.reshape(B * S, D)))
+
+
+@pytest.mark.parametrize("temb_f32", [False, True])
+def test_temb_slices_equal_torch_chunks(orc, temb_f32):
+    """(table + temb.float()).chunk(6, dim=2), each slice .contiguous(), on the CPU."""
+    g = torch.Generator().manual_seed(41)
+    B, L, M, D = 2, 9, 6, 520
+    table = torch.randn(1, 1, M, D, generator=g) * 0.1
+    temb = torch.randn(B, L, M, D, generator=g)
+    if not temb_f32:
+        temb = temb.to(torch.bfloat16)
+    chunks = (table + temb.float()).chunk(M, dim=2)
+    want = np.stack([c.contiguous().reshape(B, L, D).numpy() for c in chunks])
+    t_in = temb.numpy() if temb_f32 else bits_of(temb)
+    out = orc.temb_table_slices(table.reshape(M, D).numpy(), t_in, temb_is_f32=temb_f32)
+    assert out.shape == (M, B, L, D)
+    assert np.array_equal(out.view(np.uint32), want.view(np.uint32))
+
+
+def test_temb_slices_zero_table_is_the_widening(orc):
+    """A zero table returns float(temb) exactly, slice m holding temb[:, :, m]."""
+    g = torch.Generator().manual_seed(42)
+    temb = torch.randn(1, 5, 9, 64, generator=g).to(torch.bfloat16)
+    out = orc.temb_table_slices(np.zeros((9, 64), np.float32), bits_of(temb))
+    for m in range(9):
+        assert np.array_equal(out[m, 0], temb[0, :, m].float().numpy())
