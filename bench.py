@@ -346,6 +346,53 @@ def other_workloads(m, W, dev, stream, log):
     res["qk_rmsnorm_1x4360x32x128"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
     del qs, ks, calls
 
+    # modulate_scale_shift (1,4096,4096): one adaLN row per sample, then one per token
+    wl = W.glm_square()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    nb = rot(lnm_bytes(4096, 4096, 1))
+    xs_ = [t["x"].clone() for _ in range(nb)]
+    outs = [torch.empty_like(t["x"]) for _ in range(nb)]
+    calls = [m.modulate_scale_shift(xs_[i], t["scale"], t["shift"], out=outs[i], prepare=True) for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["modulate_scale_shift_1x4096x4096"] = {"us": round(us, 3),
+                                               "GBps": round(lnm_bytes(4096, 4096, 1) / us / 1e3, 1)}
+    g = torch.Generator().manual_seed(1)
+    sc_tok = W.normal((1, 4096, 4096), g, std=0.1).to(dev)
+    sh_tok = W.normal((1, 4096, 4096), g, std=0.1).to(dev)
+    nb2 = rot(4 * 4096 * 4096 * 2)
+    calls = [m.modulate_scale_shift(xs_[i % nb], sc_tok, sh_tok, out=outs[i % nb], prepare=True) for i in range(nb2)]
+    us = time_loop(calls, 300, stream)
+    b = 4 * 4096 * 4096 * 2
+    res["modulate_scale_shift_1x4096x4096_per_token_rows"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del xs_, outs, calls, sc_tok, sh_tok
+
+    # temb_table_slices at the Wan 704x1280, 121-frame size: (1,109120,6,3072) -> 8 GB of fp32
+    wl = W.wan_temb()
+    table = wl.tensors["table"].to(dev)
+    temb = W.tile(wl.tensors["temb_frame"].to(dev), wl.meta["frames"])
+    Bt, Lt, Mt, Dt = temb.shape
+    out_t = torch.empty((Mt, Bt, Lt, Dt), dtype=torch.float32, device=dev)
+    call = m.temb_table_slices(table, temb, out=out_t, prepare=True)
+    us = time_loop([call], 10, stream)
+    b = Bt * Lt * Mt * Dt * (2 + 4) + Mt * Dt * 4
+    entry = {"ms": round(us / 1e3, 4), "GBps": round(b / us / 1e3, 1)}
+    del out_t
+
+    def eager():
+        return [c.contiguous() for c in (table[None, None] + temb.float()).chunk(Mt, dim=2)]
+
+    eager()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        eager()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    entry["torch_eager_chunks_contiguous_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+    res["temb_table_slices_1x109120x6x3072"] = entry
+    del temb, table
+
     # the gated residual update fused with ln_modulate, (1,4096,4096)
     wl = W.glm_square()
     t = {k: v.to(dev) for k, v in wl.tensors.items()}

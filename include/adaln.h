@@ -8,7 +8,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Tensors are bf16 (dtype argument must be ADALN_BF16).  Every tensor
+ *  - Tensors are bf16 (dtype argument must be ADALN_BF16), except where an
+ *    entry point names fp32 tensors.  Every tensor
  *    pointer is a DEVICE pointer, at least 2-byte aligned.  Strides are in
  *    elements, non-negative.  Outputs are written contiguously (row-major).
  *  - Ownership: the caller owns every buffer.  The library never allocates,
@@ -63,6 +64,7 @@ extern "C" {
 
 /* dtypes */
 #define ADALN_BF16 1
+#define ADALN_F32 2 /* only where an entry point says so (temb_table_slices' temb) */
 
 /* ops, for adaln_order_for */
 #define ADALN_OP_LN_MODULATE 1
@@ -265,6 +267,56 @@ int bias_gelu_tanh(const void* x, int64_t rows, int64_t width, int64_t sx_row, c
                    int dtype, void* out, void* stream);
 
 int bias_gelu_tanh_can_use(int64_t rows, int64_t width, int64_t sx_row, int dtype);
+
+/*
+ * modulate_scale_shift -- out = x * (1 + scale) + shift as three eager bf16
+ * ops: one_plus = bf16(1 + scale), y = bf16(x * one_plus),
+ * out = bf16(y + shift) (the ln_modulate tail applied to x itself).
+ *
+ * Source: "Fused Kernels" page, table "adaLN modulation and gating"
+ * (modulate_scale_shift replaces x * (1 + scale) + shift, bit-exact) and the
+ * note under it (LingBot World's camera conditioning uses one affine row per
+ * token).
+ *
+ *  x        [B,S,D], element (b,s,d) at x + b*sx_b + s*sx_s + d.
+ *  scale    element (b,s,d) at scale + b*ssc_b + s*ssc_s + d: ssc_s = 0 for
+ *           one adaLN row per sample, ssc_s = D (or any) for one per token.
+ *  shift    likewise with ssh_b, ssh_s.
+ *  out      [B,S,D] contiguous; may be exactly x when x is contiguous.
+ *  D        >= 0, any value (16-byte-aligned rows with D % 8 == 0 take the
+ *           vector kernel).
+ */
+int modulate_scale_shift(const void* x, int64_t sx_b, int64_t sx_s, const void* scale, int64_t ssc_b,
+                         int64_t ssc_s, const void* shift, int64_t ssh_b, int64_t ssh_s, int64_t B,
+                         int64_t S, int64_t D, int dtype, void* out, void* stream);
+
+int modulate_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                 int64_t ssc_b, int64_t ssc_s, int64_t ssh_b, int64_t ssh_s, int dtype);
+
+/*
+ * temb_table_slices -- the nmod adaLN slices of table + temb, each written
+ * contiguously in one pass: out[m][b,l,d] = table[m,d] + float(temb[b,l,m,d]),
+ * one fp32 addition (round-to-nearest-even).
+ *
+ * Source: "Fused Kernels" page, table "adaLN modulation and gating"
+ * (temb_table_slices, bit-exact) and the note under it: it replaces the
+ * eager (scale_shift_table + temb.float()).chunk(6, dim=2), whose strided
+ * slices the model then copies with .contiguous().
+ *
+ *  table    fp32 [nmod, D], row m at table + m*st_m (the model's
+ *           scale_shift_table, any leading singleton dims dropped).
+ *  temb     [B, L, nmod, D], element (b,l,m,d) at temb + b*se_b + l*se_l +
+ *           m*se_m + d; dtype ADALN_BF16 or ADALN_F32 (the temb dtype).
+ *  out      fp32 [nmod][B*L][D]: slice m is the contiguous block starting at
+ *           out + m*B*L*D.  Must not overlap table or temb.
+ *  nmod, D  >= 0 (6 slices for the Wan-style table; any count).
+ */
+int temb_table_slices(const float* table, int64_t st_m, const void* temb, int64_t se_b, int64_t se_l,
+                      int64_t se_m, int64_t B, int64_t L, int64_t nmod, int64_t D, int dtype, float* out,
+                      void* stream);
+
+int temb_table_slices_can_use(int64_t B, int64_t L, int64_t nmod, int64_t D, int64_t st_m, int64_t se_b,
+                              int64_t se_l, int64_t se_m, int dtype);
 
 /*
  * adaln_order_for -- the fixed fp32 reduction order the kernels use for a

@@ -24,6 +24,7 @@ ERR_STRIDE = -7
 ERR_HIP = -8
 ERR_ARG = -9
 BF16 = 1
+F32 = 2
 OP_LN_MODULATE = 1
 OP_QK_HEAD_LAYERNORM = 2
 OP_RESIDUAL_GATE_ADD_LN_MODULATE = 3
@@ -47,6 +48,10 @@ EXPORTS = (
     "rmsnorm_scale_shift_can_use",
     "qk_rmsnorm",
     "qk_rmsnorm_can_use",
+    "modulate_scale_shift",
+    "modulate_scale_shift_can_use",
+    "temb_table_slices",
+    "temb_table_slices_can_use",
     "adaln_order_for",
     "adaln_status_str",
     "adaln_abi_version",
@@ -93,6 +98,10 @@ def lib():
     L.qk_rmsnorm.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64, vp, vp, f32, ci, vp, vp,
                              vp]
     L.qk_rmsnorm_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, ci]
+    L.modulate_scale_shift.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i64, ci, vp, vp]
+    L.modulate_scale_shift_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, ci]
+    L.temb_table_slices.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, vp]
+    L.temb_table_slices_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.adaln_order_for.argtypes = [ci, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.adaln_status_str.argtypes = [ci]
     L.adaln_status_str.restype = ctypes.c_char_p

@@ -29,6 +29,8 @@ HIP_SOURCES = [
     "qk_head_layernorm.hip",
     "bias_gelu_tanh.hip",
     "residual_ln_modulate.hip",
+    "modulate_scale_shift.hip",
+    "temb_table_slices.hip",
 ]
 HOST_SOURCES = ["abi.cpp"]
 

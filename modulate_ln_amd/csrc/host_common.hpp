@@ -21,8 +21,8 @@ struct Dim {
   int64_t stride;  // elements
 };
 
-// Byte range [lo, hi) touched by a bf16 tensor with the given dims.  Empty
-// tensors touch nothing (lo == hi).
+// Byte range [lo, hi) touched by a tensor of elem-byte elements (bf16 by
+// default) with the given dims.  Empty tensors touch nothing (lo == hi).
 struct Span {
   uintptr_t lo = 0, hi = 0;
 };
@@ -33,7 +33,7 @@ inline bool dims_ok(std::initializer_list<Dim> dims) {
   return true;
 }
 
-inline Span span_of(const void* p, std::initializer_list<Dim> dims) {
+inline Span span_of(const void* p, std::initializer_list<Dim> dims, size_t elem = 2) {
   Span s;
   int64_t last = 0;
   for (const Dim& d : dims) {
@@ -41,7 +41,7 @@ inline Span span_of(const void* p, std::initializer_list<Dim> dims) {
     last += (d.size - 1) * d.stride;
   }
   s.lo = (uintptr_t)p;
-  s.hi = s.lo + (uintptr_t)(last + 1) * 2u;
+  s.hi = s.lo + (uintptr_t)(last + 1) * (uintptr_t)elem;
   return s;
 }
 

@@ -1,0 +1,293 @@
+// modulate_scale_shift: out = bf16 chain of x * (1 + scale) + shift on gfx950.
+//
+// Operation: "Fused Kernels" page, table "adaLN modulation and gating"
+// (modulate_scale_shift replaces x * (1 + scale) + shift, bit-exact; LingBot
+// World's camera conditioning uses it with one affine row per token).  Three
+// eager bf16 ops, so three roundings: one_plus = bf16(1 + scale),
+// y = bf16(x * one_plus), out = bf16(y + shift) -- the tail of ln_modulate
+// with x in place of the normalized row.
+//
+// Design: pure streaming, the column-chunk layout of residual_gate_add.  Wave
+// w of chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it
+// visits, the next row's loads in flight while the current row is computed.
+// With one adaLN row per sample, the wave keeps bf16(1 + scale) and shift of
+// its chunk in fp32 VGPRs while it stays in a sample (1 read + 1 write per
+// element); with one row per token it streams the scale and shift rows too
+// (3 reads + 1 write).  Loads and stores are non-temporal.
+#include "device_common.hpp"
+#include "host_common.hpp"
+
+namespace adaln {
+namespace {
+
+struct ModArgs {
+  const uint16_t* x;
+  int64_t sx_b, sx_s;
+  const uint16_t* scale;
+  int64_t ssc_b, ssc_s;
+  const uint16_t* shift;
+  int64_t ssh_b, ssh_s;
+  int64_t S, D, R;
+  uint16_t* out;
+};
+
+constexpr int kRowsPerBlock = 4;
+constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
+
+// x * o + h with the two roundings, o = bf16(1 + scale) and h = shift in fp32
+template <int V>
+__device__ __forceinline__ Vec<V> mod_vec(const Vec<V>& xv, const float* o, const float* h) {
+  Vec<V> r;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    float y0 = lo_f32(xv.w[i]) * o[2 * i];
+    float y1 = hi_f32(xv.w[i]) * o[2 * i + 1];
+    round_pair(y0, y1);  // bf16(x * one_plus)
+    r.w[i] = pack_bf16(y0 + h[2 * i], y1 + h[2 * i + 1]);  // bf16(y + shift)
+  }
+  return r;
+}
+
+// bf16(1 + scale) and shift of one vector, widened to fp32
+template <int V>
+__device__ __forceinline__ void mod_rows(const Vec<V>& sv, const Vec<V>& hv, float* o, float* h) {
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    o[2 * i] = 1.0f + lo_f32(sv.w[i]);
+    o[2 * i + 1] = 1.0f + hi_f32(sv.w[i]);
+    round_pair(o[2 * i], o[2 * i + 1]);  // bf16(1 + scale)
+    h[2 * i] = lo_f32(hv.w[i]);
+    h[2 * i + 1] = hi_f32(hv.w[i]);
+  }
+}
+
+// One row step of a wave: the row's x (and, per token, scale and shift)
+// vectors of the lane's chunk.
+template <int V, int U, bool PER_TOKEN>
+struct ModRow {
+  Vec<V> x[U];
+  Vec<V> sc[PER_TOKEN ? U : 1];
+  Vec<V> sh[PER_TOKEN ? U : 1];
+};
+
+// Rows r = first, first + step, ... of the chunk; the next row's loads are in
+// flight while the current row is computed and stored (two row buffers).
+template <int V, int U, bool PER_TOKEN>
+__global__ __launch_bounds__(256) void mod_chunks(ModArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nvec = a.D / V;
+  const int64_t step = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  if (r >= a.R) return;
+
+  bool ok[U];
+  int64_t off[U];  // element offset of the lane's u-th vector (clamped in-bounds)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = (int64_t)blockIdx.y * kWave * U + (int64_t)u * kWave + lane;
+    ok[u] = v < nvec;
+    off[u] = (ok[u] ? v : nvec - 1) * V;
+  }
+  auto load_row = [&](ModRow<V, U, PER_TOKEN>& row, int64_t rr) {
+    const int64_t b = rr / a.S;
+    const int64_t s = rr - b * a.S;
+    const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
+#pragma unroll
+    for (int u = 0; u < U; ++u) row.x[u] = load_vec_nt<V>(xr + off[u]);
+    if constexpr (PER_TOKEN) {
+      const uint16_t* sr = a.scale + b * a.ssc_b + s * a.ssc_s;
+      const uint16_t* hr = a.shift + b * a.ssh_b + s * a.ssh_s;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        row.sc[u] = load_vec_nt<V>(sr + off[u]);
+        row.sh[u] = load_vec_nt<V>(hr + off[u]);
+      }
+    }
+  };
+  int64_t cached_b = -1;
+  float o[U][V], h[U][V];
+  auto process = [&](const ModRow<V, U, PER_TOKEN>& row, int64_t rr) {
+    if constexpr (PER_TOKEN) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) mod_rows<V>(row.sc[u], row.sh[u], o[u], h[u]);
+    } else {
+      const int64_t b = rr / a.S;
+      if (b != cached_b) {
+        const uint16_t* sr = a.scale + b * a.ssc_b;
+        const uint16_t* hr = a.shift + b * a.ssh_b;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mod_rows<V>(load_vec<V>(sr + off[u]), load_vec<V>(hr + off[u]), o[u], h[u]);
+        cached_b = b;
+      }
+    }
+    uint16_t* orow = a.out + rr * a.D;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) store_vec_nt<V>(orow + off[u], mod_vec<V>(row.x[u], o[u], h[u]));
+  };
+
+  ModRow<V, U, PER_TOKEN> bufA, bufB;
+  load_row(bufA, r);
+  while (true) {
+    int64_t r1 = r + step;
+    if (r1 < a.R) load_row(bufB, r1);
+    process(bufA, r);
+    if (r1 >= a.R) break;
+    r = r1;
+    r1 = r + step;
+    if (r1 < a.R) load_row(bufA, r1);
+    process(bufB, r);
+    if (r1 >= a.R) break;
+    r = r1;
+  }
+}
+
+// any D, any 2-byte alignment: one element per lane step
+__global__ __launch_bounds__(256) void mod_rows_scalar(ModArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
+       r += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int64_t b = r / a.S;
+    const int64_t s = r - b * a.S;
+    const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
+    const uint16_t* sr = a.scale + b * a.ssc_b + s * a.ssc_s;
+    const uint16_t* hr = a.shift + b * a.ssh_b + s * a.ssh_s;
+    uint16_t* orow = a.out + r * a.D;
+    for (int64_t j = lane; j < a.D; j += kWave) {
+      const float o = u16_f32(to_bf16(1.0f + u16_f32(sr[j])));
+      const float y = u16_f32(to_bf16(u16_f32(xr[j]) * o));
+      orow[j] = to_bf16(y + u16_f32(hr[j]));
+    }
+  }
+}
+
+inline unsigned grid_for(int64_t R) {
+  int64_t blocks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+  return (unsigned)std::min(blocks, kMaxBlocks);
+}
+
+// grid size (blocks per compute unit in total: 4 with per-sample rows, 8
+// with per-token rows) and vectors per lane in a chunk, measured on MI355X
+// at (1,4096,4096); overridable at build time
+#ifndef ADALN_MOD_BLOCKS_PER_CU
+#define ADALN_MOD_BLOCKS_PER_CU 4
+#endif
+#ifndef ADALN_MOD_TOKEN_BLOCKS_PER_CU
+#define ADALN_MOD_TOKEN_BLOCKS_PER_CU 8
+#endif
+#ifndef ADALN_MOD_MAX_U
+#define ADALN_MOD_MAX_U 4
+#endif
+
+template <int V, int U, bool PER_TOKEN>
+int launch_mod(const ModArgs& a, hipStream_t st) {
+  const int64_t nvec = a.D / V;
+  const int64_t nchunks = (nvec + kWave * U - 1) / (kWave * U);
+  if (nchunks > 65535) {  // grid.y limit: rows of more than 2^24 vectors go element-wise
+    hipLaunchKernelGGL(mod_rows_scalar, dim3(grid_for(a.R)), dim3(256), 0, st, a);
+    return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+  }
+  const int cus = cu_count();
+  const int64_t per_cu = PER_TOKEN ? ADALN_MOD_TOKEN_BLOCKS_PER_CU : ADALN_MOD_BLOCKS_PER_CU;
+  const int64_t target = per_cu * (cus > 0 ? cus : 256);
+  int64_t gx = (target + nchunks - 1) / nchunks;
+  gx = std::max<int64_t>(1, std::min<int64_t>(gx, (a.R + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((mod_chunks<V, U, PER_TOKEN>), dim3((unsigned)gx, (unsigned)nchunks), dim3(256), 0,
+                     st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+// vectors per lane in one chunk: as many as a row needs, at most
+// ADALN_MOD_MAX_U (the per-sample rows stay in VGPRs as fp32: 2*U*V registers)
+template <int V, bool PER_TOKEN>
+int dispatch_mod(const ModArgs& a, hipStream_t st) {
+  const int64_t per_lane = (a.D / V + kWave - 1) / kWave;
+  switch (std::min<int64_t>(per_lane, ADALN_MOD_MAX_U)) {
+    case 1: return launch_mod<V, 1, PER_TOKEN>(a, st);
+    case 2: return launch_mod<V, 2, PER_TOKEN>(a, st);
+    case 3: return launch_mod<V, 3, PER_TOKEN>(a, st);
+#if ADALN_MOD_MAX_U > 4
+    case 4: return launch_mod<V, 4, PER_TOKEN>(a, st);
+    case 5: return launch_mod<V, 5, PER_TOKEN>(a, st);
+    case 6: return launch_mod<V, 6, PER_TOKEN>(a, st);
+    case 7: return launch_mod<V, 7, PER_TOKEN>(a, st);
+    default: return launch_mod<V, 8, PER_TOKEN>(a, st);
+#else
+    default: return launch_mod<V, 4, PER_TOKEN>(a, st);
+#endif
+  }
+}
+
+}  // namespace
+
+static int mod_check_shape(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s, int64_t ssc_b,
+                           int64_t ssc_s, int64_t ssh_b, int64_t ssh_s, int dtype) {
+  if (dtype != ADALN_BF16) return ADALN_ERR_DTYPE;
+  if (B < 0 || S < 0 || D < 0) return ADALN_ERR_SHAPE;
+  if (sx_b < 0 || sx_s < 0 || ssc_b < 0 || ssc_s < 0 || ssh_b < 0 || ssh_s < 0) return ADALN_ERR_STRIDE;
+  int64_t R, RD;
+  if (!mul_ok(B, S, &R) || !mul_ok(R, D, &RD)) return ADALN_ERR_TOO_LARGE;
+  if (!extent_ok({{B, sx_b}, {S, sx_s}, {D, 1}}) || !extent_ok({{B, ssc_b}, {S, ssc_s}, {D, 1}}) ||
+      !extent_ok({{B, ssh_b}, {S, ssh_s}, {D, 1}}))
+    return ADALN_ERR_TOO_LARGE;
+  return ADALN_OK;
+}
+
+}  // namespace adaln
+
+using namespace adaln;
+
+extern "C" int modulate_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                            int64_t ssc_b, int64_t ssc_s, int64_t ssh_b, int64_t ssh_s,
+                                            int dtype) {
+  return mod_check_shape(B, S, D, sx_b, sx_s, ssc_b, ssc_s, ssh_b, ssh_s, dtype) == ADALN_OK;
+}
+
+extern "C" int modulate_scale_shift(const void* x, int64_t sx_b, int64_t sx_s, const void* scale,
+                                    int64_t ssc_b, int64_t ssc_s, const void* shift, int64_t ssh_b,
+                                    int64_t ssh_s, int64_t B, int64_t S, int64_t D, int dtype, void* out,
+                                    void* stream) {
+  int rc = mod_check_shape(B, S, D, sx_b, sx_s, ssc_b, ssc_s, ssh_b, ssh_s, dtype);
+  if (rc != ADALN_OK) return rc;
+  const int64_t R = B * S;
+  if (R == 0 || D == 0) return ADALN_OK;
+  if (!x || !scale || !shift || !out) return ADALN_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(out, 2)) return ADALN_ERR_ALIGN;
+
+  const Span so = span_of(out, {{R * D, 1}});
+  const Span sx = span_of(x, {{B, sx_b}, {S, sx_s}, {D, 1}});
+  const Span ssc = span_of(scale, {{B, ssc_b}, {S, ssc_s}, {D, 1}});
+  const Span ssh = span_of(shift, {{B, ssh_b}, {S, ssh_s}, {D, 1}});
+  const bool x_contig = (S == 1 || sx_s == D) && (B == 1 || sx_b == S * D);
+  if (overlaps(so, sx) && !(x == out && x_contig)) return ADALN_ERR_ALIAS;
+  if (overlaps(so, ssc) || overlaps(so, ssh)) return ADALN_ERR_ALIAS;
+
+  ModArgs a;
+  a.x = (const uint16_t*)x;
+  a.sx_b = sx_b;
+  a.sx_s = sx_s;
+  a.scale = (const uint16_t*)scale;
+  a.ssc_b = ssc_b;
+  a.ssc_s = ssc_s;
+  a.shift = (const uint16_t*)shift;
+  a.ssh_b = ssh_b;
+  a.ssh_s = ssh_s;
+  a.S = S;
+  a.D = D;
+  a.R = R;
+  a.out = (uint16_t*)out;
+  const bool per_token = S > 1 && (ssc_s != 0 || ssh_s != 0);
+
+  hipStream_t st = (hipStream_t)stream;
+  auto vec_ok = [&](uintptr_t vb) {
+    auto so_ = [&](int64_t n, int64_t s) { return n <= 1 || ((uintptr_t)s * 2u) % vb == 0; };
+    return D % (int64_t)(vb / 2) == 0 && aligned(x, vb) && aligned(scale, vb) && aligned(shift, vb) &&
+           aligned(out, vb) && so_(B, sx_b) && so_(S, sx_s) && so_(B, ssc_b) && so_(S, ssc_s) &&
+           so_(B, ssh_b) && so_(S, ssh_s);
+  };
+  if (vec_ok(16)) return per_token ? dispatch_mod<8, true>(a, st) : dispatch_mod<8, false>(a, st);
+  if (vec_ok(8)) return per_token ? dispatch_mod<4, true>(a, st) : dispatch_mod<4, false>(a, st);
+  hipLaunchKernelGGL(mod_rows_scalar, dim3(grid_for(R)), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}

@@ -192,6 +192,80 @@ def residual_gate_add_ln_modulate(residual: torch.Tensor, gate: torch.Tensor, up
     return call if prepare else call()
 
 
+def _affine_rows(t: torch.Tensor, B: int, S: int, D: int, name: str):
+    """adaLN rows per sample ([B,D], [B,1,D], broadcast [1,D]) or per token ([B,S,D]) ->
+    (tensor, batch stride, token stride); element stride must be 1."""
+    if t.dim() == 3 and t.shape[1] == S and S != 1:
+        if t.shape[0] not in (B, 1) or t.shape[2] != D:
+            raise ValueError("%s must be [B,S,D], [B,1,D] or [B,D], got %s" % (name, tuple(t.shape)))
+        if D > 1 and t.stride(2) != 1:
+            raise ValueError("%s must have unit stride along the hidden dim" % name)
+        return t, (t.stride(0) if t.shape[0] == B else 0), t.stride(1)
+    t, sb = _rows_view(t, B, D, name)
+    return t, sb, 0
+
+
+def modulate_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, *,
+                         out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """x * (1 + scale) + shift with the eager roundings; scale/shift one row per sample
+    ([B,D] / [B,1,D]) or per token ([B,S,D]); x [B,S,D] with unit stride along D."""
+    for name, t in (("x", x), ("scale", scale), ("shift", shift)):
+        _require(t, name)
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D]")
+    B, S, D = x.shape
+    if D > 1 and x.stride(2) != 1:
+        raise ValueError("x must have unit stride along the hidden dim")
+    scale, ssc_b, ssc_s = _affine_rows(scale, B, S, D, "scale")
+    shift, ssh_b, ssh_s = _affine_rows(shift, B, S, D, "shift")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _require(out, "out")
+        if tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B,S,D] tensor")
+    st = _stream_handle(x, stream)
+    call = Prepared("modulate_scale_shift", N.lib().modulate_scale_shift, (
+        x.data_ptr(), x.stride(0), x.stride(1), scale.data_ptr(), ssc_b, ssc_s, shift.data_ptr(), ssh_b, ssh_s,
+        B, S, D, N.BF16, out.data_ptr(), st), out)
+    return call if prepare else call()
+
+
+def temb_table_slices(table: torch.Tensor, temb: torch.Tensor, *, out: torch.Tensor | None = None, stream=None,
+                      prepare: bool = False):
+    """The nmod slices of table + temb.float() in one pass: table fp32 [nmod, D] (or with leading
+    singleton dims), temb bf16/fp32 [B, L, nmod, D] (unit stride along D).  Returns an fp32
+    tensor [nmod, B, L, D]; out[m] is slice m, contiguous."""
+    if not isinstance(table, torch.Tensor) or not isinstance(temb, torch.Tensor):
+        raise TypeError("table and temb must be torch.Tensors")
+    if table.dtype != torch.float32:
+        raise TypeError("table must be float32, got %s" % table.dtype)
+    if temb.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("temb must be bfloat16 or float32, got %s" % temb.dtype)
+    for name, t in (("table", table), ("temb", temb)):
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on a HIP device" % name)
+    if temb.dim() != 4:
+        raise ValueError("temb must be [B, L, nmod, D]")
+    B, L, M, D = temb.shape
+    table = table.reshape(-1, table.shape[-1]) if table.dim() > 2 else table
+    if table.dim() != 2 or tuple(table.shape) != (M, D):
+        raise ValueError("table must be [nmod, D] = [%d, %d]" % (M, D))
+    for name, t in (("table", table), ("temb", temb)):
+        if D > 1 and t.stride(-1) != 1:
+            raise ValueError("%s must have unit stride along D" % name)
+    if out is None:
+        out = torch.empty((M, B, L, D), dtype=torch.float32, device=temb.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, B, L, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [nmod, B, L, D] tensor")
+    dt = N.F32 if temb.dtype == torch.float32 else N.BF16
+    st = _stream_handle(temb, stream)
+    call = Prepared("temb_table_slices", N.lib().temb_table_slices, (
+        table.data_ptr(), table.stride(0), temb.data_ptr(), temb.stride(0), temb.stride(1), temb.stride(2),
+        B, L, M, D, dt, out.data_ptr(), st), out)
+    return call if prepare else call()
+
+
 def qk_head_layernorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None = None,
                       bq: torch.Tensor | None = None, wk: torch.Tensor | None = None,
                       bk: torch.Tensor | None = None, eps: float = 1e-6, *,

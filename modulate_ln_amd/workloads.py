@@ -129,6 +129,27 @@ def wan_bias_gelu(seed: int = 0, rows: int = 4 * 4096, width: int = 12288) -> Wo
     return Workload("bias_gelu_tanh (%d,%d)" % (rows, width), dict(x=x, bias=bias), {})
 
 
+def wan_temb(seed: int = 0, B: int = 1, frames: int = 31, tokens_per_frame: int = 44 * 80, nmod: int = 6,
+             D: int = 3072) -> Workload:
+    """The adaLN table and per-token timestep embedding of a Wan-style DiT at 704x1280, 121
+    frames: 31 latent frames of 44x80 tokens (109,120 tokens), 6 slices, hidden 3072 -- the
+    size at which the eager (table + temb.float()) holds about 8 GB of fp32.
+
+    table fp32 [nmod, D] ~N(0, 0.1); temb_frame bf16 [B, tokens_per_frame, nmod, D] ~N(0, 1),
+    one latent frame's tokens.  Draw order: table, temb_frame.  The full temb is temb_frame
+    repeated along the token axis `frames` times (meta["frames"]): tile(temb_frame, frames)."""
+    g = _gen(seed)
+    table = torch.randn((nmod, D), generator=g, dtype=torch.float32) * 0.1
+    temb_frame = normal((B, tokens_per_frame, nmod, D), g)
+    return Workload("temb_table_slices (%d,%d,%d,%d)" % (B, frames * tokens_per_frame, nmod, D),
+                    dict(table=table, temb_frame=temb_frame), dict(frames=frames))
+
+
+def tile(t: torch.Tensor, frames: int) -> torch.Tensor:
+    """t [B, T, ...] -> [B, frames*T, ...]: the block repeated along axis 1 (works on any device)."""
+    return t.repeat(1, frames, *([1] * (t.dim() - 2)))
+
+
 def bits(t: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns in logical row-major order (a copy)."""
     import numpy as np

@@ -270,3 +270,43 @@ def test_rms_rejections(L):
     assert qk(ko=P2 + 16) == N.ERR_ALIAS  # k_out over the weights
     assert qk(wq=None, wk=None, qo=P3 + 1) == N.ERR_ALIGN
     assert qk(q=None, k=None, qo=None, ko=None, B=0) == N.OK
+
+
+def test_modulate_and_temb_can_use(L):
+    assert L.modulate_scale_shift_can_use(1, 4096, 4096, 4096 * 4096, 4096, 4096, 0, 4096, 0, N.BF16)
+    assert L.modulate_scale_shift_can_use(2, 3, 5, 15, 5, 15, 5, 15, 5, N.BF16)  # per token, any D
+    assert not L.modulate_scale_shift_can_use(2, 3, 5, 15, 5, 15, -5, 15, 5, N.BF16)
+    assert not L.modulate_scale_shift_can_use(2, 3, 5, 15, 5, 15, 5, 15, 5, N.F32)
+    assert L.temb_table_slices_can_use(1, 109120, 6, 3072, 3072, 109120 * 6 * 3072, 6 * 3072, 3072, N.BF16)
+    assert L.temb_table_slices_can_use(2, 3, 9, 7, 7, 189, 63, 7, N.F32)
+    assert not L.temb_table_slices_can_use(2, 3, 9, 7, 7, 189, 63, 7, 3)
+    assert not L.temb_table_slices_can_use(2, -3, 9, 7, 7, 189, 63, 7, N.BF16)
+
+
+def test_modulate_and_temb_rejections(L):
+    def mod(x=P0, scale=P1, shift=P2, out=P3, B=2, S=3, D=8, sx=(24, 8), ssc=(8, 0), ssh=(8, 0), dtype=N.BF16):
+        return L.modulate_scale_shift(x, sx[0], sx[1], scale, ssc[0], ssc[1], shift, ssh[0], ssh[1], B, S, D, dtype,
+                                      out, None)
+
+    assert mod(dtype=2) == N.ERR_DTYPE
+    assert mod(D=-1) == N.ERR_SHAPE
+    assert mod(ssc=(8, -1)) == N.ERR_STRIDE
+    assert mod(shift=None) == N.ERR_NULL
+    assert mod(out=P3 + 1) == N.ERR_ALIGN
+    assert mod(out=P0 + 2) == N.ERR_ALIAS
+    assert mod(out=P0, sx=(48, 16)) == N.ERR_ALIAS
+    assert mod(out=P1 - 4) == N.ERR_ALIAS
+    assert mod(x=None, scale=None, shift=None, out=None, S=0) == N.OK
+
+    def temb(table=P0, t=P1, out=P2, B=2, Lq=3, M=6, D=8, st=8, se=(144, 48, 8), dtype=N.BF16):
+        return L.temb_table_slices(table, st, t, se[0], se[1], se[2], B, Lq, M, D, dtype, out, None)
+
+    assert temb(dtype=0) == N.ERR_DTYPE
+    assert temb(M=-1) == N.ERR_SHAPE
+    assert temb(se=(144, -48, 8)) == N.ERR_STRIDE
+    assert temb(t=None) == N.ERR_NULL
+    assert temb(table=P0 + 2) == N.ERR_ALIGN
+    assert temb(t=P1 + 2, dtype=N.F32) == N.ERR_ALIGN
+    assert temb(out=P1 + 64) == N.ERR_ALIAS  # out over temb
+    assert temb(out=P0 + 4) == N.ERR_ALIAS  # out over the table
+    assert temb(table=None, t=None, out=None, M=0) == N.OK
