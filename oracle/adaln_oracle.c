@@ -47,6 +47,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -141,6 +142,49 @@ void orc_bf16_from_f64_array(const double* in, uint16_t* out, int64_t n) {
 /* round an fp32 value to bf16 and widen it back: the value eager stores */
 static float rb(float f) { return orc_f32_from_bf16(orc_bf16_from_f32(f)); }
 static double rb64(double d) { return (double)orc_f32_from_bf16(orc_bf16_from_f64(d)); }
+
+/* ------------------------------------------------------------------ */
+/* OCP FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3       */
+/* mantissa bits, no infinities, S.1111.111 is NaN, largest finite      */
+/* 448, subnormals k * 2^-9).  Value of a code, and the nearest code to */
+/* a real value with ties to the even code, written from that           */
+/* definition.  Magnitudes that round past 448 (above 464) have no      */
+/* finite code: NaN, as torch's conversion gives (no saturation).       */
+/* ------------------------------------------------------------------ */
+
+double orc_f64_from_fp8e4m3(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+static uint8_t fp8_nearest(double a, int sgn) {
+  /* a >= 0 finite.  Codes 0x00..0x7E increase in value; the slot after
+     448 (code 0x7F, which would be 480) is NaN, so a value rounding to it
+     -- anything above the midpoint 464, or at or beyond 480 -- is NaN. */
+  if (a >= 480.0) return (uint8_t)(0x7F | (sgn << 7));
+  int lo = 0;
+  while (lo < 0x7E && orc_f64_from_fp8e4m3((uint8_t)(lo + 1)) <= a) ++lo;
+  double v1 = orc_f64_from_fp8e4m3((uint8_t)lo);
+  double v2 = lo < 0x7E ? orc_f64_from_fp8e4m3((uint8_t)(lo + 1)) : 480.0;
+  double mid = 0.5 * (v1 + v2); /* exact: both values have few significant bits */
+  int code = lo;
+  if (a > mid || (a == mid && ((lo + 1) & 1) == 0)) code = lo + 1;
+  return (uint8_t)(code | (sgn << 7));
+}
+
+uint8_t orc_fp8e4m3_from_f64(double d) {
+  if (isnan(d)) return 0x7F;
+  return fp8_nearest(fabs(d), signbit(d) ? 1 : 0);
+}
+
+uint8_t orc_fp8e4m3_from_f32(float f) { return orc_fp8e4m3_from_f64((double)f); }
+
+void orc_fp8e4m3_from_f32_array(const float* in, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8e4m3_from_f32(in[i]);
+}
 
 /* ------------------------------------------------------------------ */
 /* Welford (Welford 1962) and the pairwise merge (Chan, Golub, LeVeque) */
@@ -446,6 +490,96 @@ int orc_qk_rmsnorm(const uint16_t* x, int64_t R, int64_t Dh, const uint16_t* w, 
     }
   }
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* ln_modulate_fold: the single-rounding variant the pages offer in the  */
+/* high-quality tier ("Fused Kernels" page, request-gated fusion table:  */
+/* layer_norm(x, weight=(1 + scale), bias=shift) in place of an affine- */
+/* free LayerNorm plus a separate modulate).  One eager affine LayerNorm */
+/* op with the bf16 weight tensor (1 + scale): out = bf16(fma(w, n, b)), */
+/* n = RN(RN(x - mean) * rstd) in fp32 (fp64 mode: w * n + b in double), */
+/* w = bf16(1 + scale), b = shift.  Not the eager four-op chain's bits:  */
+/* it drops the roundings of x_hat and of the product.                   */
+/* ------------------------------------------------------------------ */
+
+int orc_ln_modulate_fold(const uint16_t* x, int64_t B, int64_t S, int64_t D, const uint16_t* scale,
+                         const uint16_t* shift, float eps, int mode, int V, int L, uint16_t* out, double* mean_out,
+                         double* rstd_out) {
+  if (B < 0 || S < 0 || D <= 0) return ORC_EINVAL;
+  if (mode == ORC_FP32_FIXED && check_order(D, V, L) != ORC_OK) return ORC_EINVAL;
+  if (mode != ORC_FP32_FIXED && mode != ORC_FP64_TWO_PASS) return ORC_EINVAL;
+  int64_t R = B * S;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    const uint16_t* xr = x + r * D;
+    const uint16_t* sc = scale + (r / S) * D;
+    const uint16_t* sh = shift + (r / S) * D;
+    uint16_t* o = out + r * D;
+    if (mode == ORC_FP32_FIXED) {
+      float mean, rstd;
+      row_stats_fp32(xr, D, eps, V, L, &mean, &rstd);
+      for (int64_t j = 0; j < D; ++j) {
+        float n = (orc_f32_from_bf16(xr[j]) - mean) * rstd;
+        float w = rb(1.0f + orc_f32_from_bf16(sc[j]));
+        o[j] = orc_bf16_from_f32(fmaf(w, n, orc_f32_from_bf16(sh[j])));
+      }
+      if (mean_out) mean_out[r] = mean;
+      if (rstd_out) rstd_out[r] = rstd;
+    } else {
+      double mean, rstd;
+      row_stats_fp64(xr, D, eps, &mean, &rstd);
+      for (int64_t j = 0; j < D; ++j) {
+        double n = ((double)orc_f32_from_bf16(xr[j]) - mean) * rstd;
+        double w = rb64(1.0 + (double)orc_f32_from_bf16(sc[j]));
+        o[j] = orc_bf16_from_f64(w * n + (double)orc_f32_from_bf16(sh[j]));
+      }
+      if (mean_out) mean_out[r] = mean;
+      if (rstd_out) rstd_out[r] = rstd;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* ln_modulate_fp8: ln_modulate with its bf16 output quantized straight  */
+/* to static FP8 ("Fused Kernels" page, table "Quantized layout          */
+/* producers": flux2_layernorm_modulate_fp8_quant, LayerNorm plus adaLN  */
+/* modulation directly into static FP8 output).  With y the eager chain's */
+/* bf16 output and s the static per-tensor scale:                        */
+/*   fp32 mode: q = e4m3(RN(y * RN(1/s))) after clamping to [-448, 448]   */
+/*   fp64 mode: q = e4m3(y / s) after the same clamp (exact quotient)     */
+/* (NaN stays NaN).  out is one byte per element, [B*S, D].              */
+/* ------------------------------------------------------------------ */
+
+int orc_ln_modulate_fp8(const uint16_t* x, int64_t B, int64_t S, int64_t D, const uint16_t* scale,
+                        const uint16_t* shift, float eps, float qscale, int mode, int V, int L, uint8_t* out,
+                        double* mean_out, double* rstd_out) {
+  if (B < 0 || S < 0 || D <= 0) return ORC_EINVAL;
+  if (!(qscale > 0.0f) || isinf(qscale)) return ORC_EINVAL;
+  int64_t R = B * S;
+  uint16_t* y = (uint16_t*)malloc((size_t)(R > 0 ? R * D : 1) * sizeof(uint16_t));
+  if (!y) return ORC_EINVAL;
+  int rc = orc_ln_modulate(x, B, S, D, scale, shift, eps, mode, V, L, y, mean_out, rstd_out);
+  if (rc == ORC_OK) {
+    const float inv = 1.0f / qscale;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R * D; ++i) {
+      if (mode == ORC_FP32_FIXED) {
+        float v = orc_f32_from_bf16(y[i]) * inv;
+        if (v > 448.0f) v = 448.0f;
+        if (v < -448.0f) v = -448.0f;
+        out[i] = orc_fp8e4m3_from_f32(v);
+      } else {
+        double v = (double)orc_f32_from_bf16(y[i]) / (double)qscale;
+        if (v > 448.0) v = 448.0;
+        if (v < -448.0) v = -448.0;
+        out[i] = orc_fp8e4m3_from_f64(v);
+      }
+    }
+  }
+  free(y);
+  return rc;
 }
 
 /* ------------------------------------------------------------------ */

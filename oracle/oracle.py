@@ -95,6 +95,18 @@ def load_library(path: str):
     lib.orc_modulate_scale_shift.argtypes = [u16p, i64, i64, i64, u16p, i64, i64, u16p, i64, i64, ctypes.c_int,
                                              u16p]
     lib.orc_temb_table_slices.argtypes = [f32p, ctypes.c_void_p, ctypes.c_int, i64, i64, i64, i64, f32p]
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.orc_f64_from_fp8e4m3.argtypes = [ctypes.c_uint8]
+    lib.orc_f64_from_fp8e4m3.restype = ctypes.c_double
+    lib.orc_fp8e4m3_from_f32.argtypes = [ctypes.c_float]
+    lib.orc_fp8e4m3_from_f32.restype = ctypes.c_uint8
+    lib.orc_fp8e4m3_from_f64.argtypes = [ctypes.c_double]
+    lib.orc_fp8e4m3_from_f64.restype = ctypes.c_uint8
+    lib.orc_fp8e4m3_from_f32_array.argtypes = [f32p, u8p, i64]
+    lib.orc_ln_modulate_fold.argtypes = [u16p, i64, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, u16p, f64p, f64p]
+    lib.orc_ln_modulate_fp8.argtypes = [u16p, i64, i64, i64, u16p, u16p, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p, f64p, f64p]
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
     lib.orc_get_threads.argtypes = []
@@ -288,6 +300,57 @@ def temb_table_slices(table, temb, temb_is_f32: bool = False):
                                        1 if temb_is_f32 else 0, B, L, nmod, D, _p(out, ctypes.c_float))
     _check(rc, "temb_table_slices")
     return out
+
+
+def fp8_from_f32(a) -> np.ndarray:
+    """float32 array -> OCP e4m3 codes (uint8), nearest with ties to even."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint8)
+    _load().orc_fp8e4m3_from_f32_array(_p(a, ctypes.c_float), _p(out, ctypes.c_uint8), a.size)
+    return out
+
+
+def f64_from_fp8(codes) -> np.ndarray:
+    """OCP e4m3 codes -> their values as float64."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.array([lib.orc_f64_from_fp8e4m3(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def ln_modulate_fold(x, scale, shift, S: int, eps: float, mode: int, V: int = 8, L: int = 64):
+    """Single-rounding fold: bf16(fma(bf16(1+scale), (x-mean)*rstd, shift)).  Returns
+    (out bits, mean, rstd) like ln_modulate."""
+    x, scale, shift = _u16(x), _u16(scale), _u16(shift)
+    R, D = x.shape
+    B = scale.shape[0]
+    if R != B * S or scale.shape != (B, D) or shift.shape != (B, D):
+        raise ValueError("shape mismatch")
+    out = np.empty((R, D), dtype=np.uint16)
+    mean = np.empty(R, dtype=np.float64)
+    rstd = np.empty(R, dtype=np.float64)
+    rc = _load().orc_ln_modulate_fold(_p(x, ctypes.c_uint16), B, S, D, _p(scale, ctypes.c_uint16),
+                                      _p(shift, ctypes.c_uint16), eps, mode, V, L, _p(out, ctypes.c_uint16),
+                                      _p(mean, ctypes.c_double), _p(rstd, ctypes.c_double))
+    _check(rc, "ln_modulate_fold")
+    return out, mean, rstd
+
+
+def ln_modulate_fp8(x, scale, shift, S: int, eps: float, qscale: float, mode: int, V: int = 8, L: int = 64):
+    """ln_modulate's bf16 output quantized to static OCP e4m3 with per-tensor scale qscale.
+    Returns (codes uint8 [B*S, D], mean, rstd)."""
+    x, scale, shift = _u16(x), _u16(scale), _u16(shift)
+    R, D = x.shape
+    B = scale.shape[0]
+    if R != B * S or scale.shape != (B, D) or shift.shape != (B, D):
+        raise ValueError("shape mismatch")
+    out = np.empty((R, D), dtype=np.uint8)
+    mean = np.empty(R, dtype=np.float64)
+    rstd = np.empty(R, dtype=np.float64)
+    rc = _load().orc_ln_modulate_fp8(_p(x, ctypes.c_uint16), B, S, D, _p(scale, ctypes.c_uint16),
+                                     _p(shift, ctypes.c_uint16), eps, qscale, mode, V, L, _p(out, ctypes.c_uint8),
+                                     _p(mean, ctypes.c_double), _p(rstd, ctypes.c_double))
+    _check(rc, "ln_modulate_fp8")
+    return out, mean, rstd
 
 
 def residual_gate_add_ln_modulate(res, gate, upd, scale, shift, S: int, eps: float, mode: int,

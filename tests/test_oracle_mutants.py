@@ -43,10 +43,16 @@ MUTANTS = {
     "modulate_scale_row_per_sample": ("const uint16_t* sc = scale + b * ssc_b + s * ssc_s;", "const uint16_t* sc = scale + b * ssc_b;"),
     "temb_slice_order_swapped": ("out[(m * R + r) * D + d] = table[m * D + d] + t;", "out[(r * nmod + m) * D + d] = table[m * D + d] + t;"),
     "temb_table_row_wrong": ("out[(m * R + r) * D + d] = table[m * D + d] + t;", "out[(m * R + r) * D + d] = table[d] + t;"),
+    "fp8_ties_away": ("if (a > mid || (a == mid && ((lo + 1) & 1) == 0)) code = lo + 1;", "if (a >= mid) code = lo + 1;"),
+    "fp8_subnormal_step": ("double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);", "double v = e == 0 ? ldexp((double)m, -10) : ldexp(1.0 + m / 8.0, e - 7);"),
+    "fp8_no_clamp": ("        if (v > 448.0f) v = 448.0f;\n", ""),
+    "fp8_scale_not_inverted": ("        float v = orc_f32_from_bf16(y[i]) * inv;", "        float v = orc_f32_from_bf16(y[i]) * qscale;"),
+    "fold_rounds_xhat": ("o[j] = orc_bf16_from_f32(fmaf(w, n, orc_f32_from_bf16(sh[j])));", "o[j] = orc_bf16_from_f32(fmaf(w, rb(n), orc_f32_from_bf16(sh[j])));"),
+    "fold_weight_not_rounded": ("float w = rb(1.0f + orc_f32_from_bf16(sc[j]));", "float w = 1.0f + orc_f32_from_bf16(sc[j]);"),
     "bias_not_rounded": ("double z = rb64((double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]));", "double z = (double)orc_f32_from_bf16(x[i]) + (double)orc_f32_from_bf16(bias[j]);"),
 }
 
-ANCHOR_COUNT = {"shift_and_scale_swapped": 2}
+ANCHOR_COUNT = {"shift_and_scale_swapped": 3}
 
 FAST_PINS = [
     lambda o: P.test_worked_d4(o, P.FP32),
@@ -78,6 +84,12 @@ FAST_PINS = [
     lambda o: P.test_modulate_worked(o, P.FP32),
     lambda o: P.test_modulate_equals_torch_eager(o, P.FP32, True),
     lambda o: P.test_temb_slices_equal_torch_chunks(o, False),
+    lambda o: P.test_fp8_decode_table_vs_torch(o),
+    lambda o: P.test_fp8_encode_vs_torch(o),
+    lambda o: P.test_ln_modulate_fp8_worked(o, P.FP32),
+    lambda o: P.test_ln_modulate_fp8_tail_vs_torch(o, 0.0123),
+    lambda o: P.test_fold_worked(o, P.FP32),
+    lambda o: P.test_fold_fp32_tail_exact(o),
     lambda o: P.test_gelu_f64_vs_torch(o),
     lambda o: P.test_bias_gelu_rounds_after_bias(o),
 ]

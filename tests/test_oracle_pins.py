@@ -709,3 +709,136 @@ def test_temb_slices_zero_table_is_the_widening(orc):
     out = orc.temb_table_slices(np.zeros((9, 64), np.float32), bits_of(temb))
     for m in range(9):
         assert np.array_equal(out[m, 0], temb[0, :, m].float().numpy())
+
+
+# ---------------------------------------------------------------------------
+# OCP FP8 E4M3 conversion, the FP8 producer and the single-rounding fold
+# ---------------------------------------------------------------------------
+
+def test_fp8_decode_table_vs_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.f64_from_fp8(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[1] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_fp8_encode_vs_torch(orc):
+    """Every bf16 value as fp32, the exact midpoints between adjacent codes and one fp32 ulp
+    either side, and 2M log-uniform fp32 values: nearest-even codes equal torch's conversion."""
+    allbf = (np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)).view(np.float32)
+    vals = [allbf]
+    codes = np.arange(0x7E, dtype=np.uint8)
+    v = orc.f64_from_fp8(codes)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    mids = np.concatenate([mids, [np.float32(464.0)]])
+    vals += [mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)), v.astype(np.float32)]
+    rng = np.random.default_rng(43)
+    mag = (2.0 ** rng.uniform(-14, 9.2, 2_000_000)).astype(np.float32)
+    vals.append(mag * np.where(rng.random(mag.size) < 0.5, -1, 1).astype(np.float32))
+    a = np.concatenate(vals).astype(np.float32)
+    a = np.concatenate([a, -a])
+    mine = orc.fp8_from_f32(a)
+    ref = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nan = np.isnan(a)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.all((mine[nan] & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_ln_modulate_fp8_worked(orc, mode):
+    """tests/golden/closed_forms.txt: the worked row quantized with qscale 1 and 0.5."""
+    x = bf([[-3.0, -1.0, 1.0, 3.0]])
+    z = bf([[0.0] * 4])
+    q, mean, rstd = orc.ln_modulate_fp8(x, z, z, 1, 1e-6, 1.0, mode, V=4, L=64)
+    assert q.tolist() == [[0xBB, 0xAE, 0x2E, 0x3B]]
+    assert mean[0] == 0.0
+    q, _, _ = orc.ln_modulate_fp8(x, z, z, 1, 1e-6, 0.5, mode, V=4, L=64)
+    assert q.tolist() == [[0xC3, 0xB6, 0x36, 0x43]]
+
+
+@pytest.mark.parametrize("qscale", [0.0123, 0.25, 3.0])
+def test_ln_modulate_fp8_tail_vs_torch(orc, qscale):
+    """fp32 mode: the quantizer is torch's fp32 ops on the oracle's own bf16 output:
+    (y * float32(1/s)).clamp(-448, 448).to(float8_e4m3fn).  With s a power of two the
+    fp64 mode (exact quotient) gives the same codes."""
+    wl = W.glm_square(seed=44, S=32, D=4096)
+    x, sc, sh = wl.tensors["x"], wl.tensors["scale"], wl.tensors["shift"]
+    xb = bits_of(x.reshape(32, 4096))
+    y, _, _ = orc.ln_modulate(xb, bits_of(sc), bits_of(sh), 32, 1e-5, FP32)
+    q, _, _ = orc.ln_modulate_fp8(xb, bits_of(sc), bits_of(sh), 32, 1e-5, qscale, FP32)
+    inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(qscale, dtype=torch.float32)
+    yt = W.from_bits(y).float()
+    want = (yt * inv).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, want)
+    if qscale == 0.25:
+        q64, _, _ = orc.ln_modulate_fp8(xb, bits_of(sc), bits_of(sh), 32, 1e-5, qscale, FP64)
+        y64, _, _ = orc.ln_modulate(xb, bits_of(sc), bits_of(sh), 32, 1e-5, FP64)
+        want64 = (W.from_bits(y64).float() * 4).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(q64, want64)
+
+
+@pytest.mark.parametrize("mode", [FP64, FP32])
+def test_fold_worked(orc, mode):
+    x = bf([[-3.0, -1.0, 1.0, 3.0]])
+    z = bf([[0.0] * 4])
+    out, _, _ = orc.ln_modulate_fold(x, z, z, 1, 1e-6, mode, V=4, L=64)
+    assert f32(out).tolist() == [[-1.34375, -0.447265625, 0.447265625, 1.34375]]
+    sh = bf([[0.5, -0.25, 2.0, -8.0]])
+    out, _, _ = orc.ln_modulate_fold(x, bf([[-1.0] * 4]), sh, 1, 1e-6, mode, V=4, L=64)
+    assert np.array_equal(out, sh)
+
+
+def test_fold_fp64_mode_equals_torch_affine_layer_norm(orc):
+    """layer_norm(x, weight=bf16(1 + scale), bias=shift) in float64, rounded once."""
+    g = torch.Generator().manual_seed(45)
+    x = (torch.randn(64, 2240, generator=g) * 2).to(torch.bfloat16)
+    sc = (torch.randn(1, 2240, generator=g) * 0.3).to(torch.bfloat16)
+    sh = (torch.randn(1, 2240, generator=g) * 0.3).to(torch.bfloat16)
+    out, _, _ = orc.ln_modulate_fold(bits_of(x), bits_of(sc), bits_of(sh), 64, 1e-6, FP64)
+    w = (1 + sc).to(torch.bfloat16).double()[0]
+    ref64 = torch.nn.functional.layer_norm(x.double(), (2240,), weight=w, bias=sh.double()[0],
+                                           eps=float(np.float32(1e-6))).numpy()
+    ref = orc.bf16_from_f64(ref64)
+    diff = out != ref
+    assert np.all(_midpoint_margin(ref64[diff]) < 1e-12)
+    assert diff.mean() < 1e-4
+
+
+def _nearest_f32_exact(x: Fraction) -> float:
+    """fp32 nearest to x (any sign) by exact rational search over bit patterns, ties to even."""
+    if x < 0:
+        return -_nearest_f32_exact(-x)
+    lo, hi = 0, 0x7F800000
+    val = lambda b: Fraction(float(np.uint32(b).view(np.float32)))  # noqa: E731
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if val(mid) <= x:
+            lo = mid
+        else:
+            hi = mid
+    vlo, vup = val(lo), val(lo + 1)
+    b = lo if (x - vlo < vup - x or (x - vlo == vup - x and lo % 2 == 0)) else lo + 1
+    return float(np.uint32(b).view(np.float32))
+
+
+def test_fold_fp32_tail_exact(orc):
+    """fp32 mode: out = bf16(fma(w, n, b)) with a single rounding of w*n + b to fp32, checked
+    against exact rational arithmetic from the oracle's own fp32 mean/rstd."""
+    g = torch.Generator().manual_seed(46)
+    R, D = 4, 512
+    x = (torch.randn(R, D, generator=g) * 2).to(torch.bfloat16)
+    sc = (torch.randn(1, D, generator=g) * 0.3).to(torch.bfloat16)
+    sh = (torch.randn(1, D, generator=g) * 0.3).to(torch.bfloat16)
+    out, mean, rstd = orc.ln_modulate_fold(bits_of(x), bits_of(sc), bits_of(sh), R, 1e-6, FP32)
+    xf = x.float().numpy()
+    n = (xf - mean.astype(np.float32)[:, None]) * rstd.astype(np.float32)[:, None]  # fp32 ops, RN each
+    w = (1 + sc.float()).to(torch.bfloat16).float().numpy()[0]
+    b = sh.float().numpy()[0]
+    want = np.empty((R, D), dtype=np.float32)
+    for i in range(R):
+        for j in range(D):
+            want[i, j] = _nearest_f32_exact(Fraction(float(w[j])) * Fraction(float(n[i, j])) + Fraction(float(b[j])))
+    assert np.array_equal(out, orc.bf16_from_f32(want))
