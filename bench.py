@@ -346,6 +346,26 @@ def other_workloads(m, W, dev, stream, log):
     res["qk_rmsnorm_1x4360x32x128"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
     del qs, ks, calls
 
+    # ln_modulate into static FP8, and the single-rounding fold, (1,4096,4096)
+    wl = W.glm_square()
+    t = {k: v.to(dev) for k, v in wl.tensors.items()}
+    nb = rot(3 * 4096 * 4096)
+    xs_ = [t["x"].clone() for _ in range(nb)]
+    q8 = [torch.empty((1, 4096, 4096), dtype=torch.float8_e4m3fn, device=dev) for _ in range(nb)]
+    qscale = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    calls = [m.ln_modulate_fp8(xs_[i], t["scale"], t["shift"], qscale, 1e-5, out=q8[i], prepare=True)
+             for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    b = 3 * 4096 * 4096 + 2 * 4096 * 2
+    res["ln_modulate_fp8_1x4096x4096"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del q8, calls
+    outs = [torch.empty_like(t["x"]) for _ in range(nb)]
+    calls = [m.ln_modulate_fold(xs_[i], t["scale"], t["shift"], 1e-5, out=outs[i], prepare=True) for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["ln_modulate_fold_1x4096x4096"] = {"us": round(us, 3),
+                                           "GBps": round(lnm_bytes(4096, 4096, 1) / us / 1e3, 1)}
+    del xs_, outs, calls
+
     # modulate_scale_shift (1,4096,4096): one adaLN row per sample, then one per token
     wl = W.glm_square()
     t = {k: v.to(dev) for k, v in wl.tensors.items()}

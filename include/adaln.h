@@ -128,6 +128,51 @@ int residual_gate_add_can_use(int64_t B, int64_t S, int64_t D, int64_t sr_b, int
                               int64_t sg_b, int64_t su_b, int64_t su_s, int dtype);
 
 /*
+ * ln_modulate_fold -- the single-rounding variant of ln_modulate, one
+ * affine LayerNorm op: out = bf16(fma(bf16(1 + scale), n, shift)) with
+ * n = (x - mean) * rstd in fp32 (the statistics of ln_modulate, same order).
+ * NOT bit-identical to the eager chain ln_modulate reproduces: it skips the
+ * rounding of x_hat and of x_hat * (1 + scale).
+ *
+ * Source: "Fused Kernels" page, the request-gated fusion table ("LayerNorm +
+ * modulate": layer_norm(x, weight=(1 + scale), bias=shift) in place of the
+ * affine-free LayerNorm plus a separate modulate, mounted only in the
+ * high-quality tiers); prhub report on sglang PR #34015, 关联脉络 (the folded
+ * path measured against the bit-exact kernel).
+ *
+ * Arguments, layouts, fast paths and aliasing exactly as ln_modulate.
+ */
+int ln_modulate_fold(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                     int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                     int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                     float* rstd_out, void* stream);
+
+/*
+ * ln_modulate_fp8 -- ln_modulate with its bf16 output quantized straight to
+ * static OCP FP8 E4M3 (1-4-3, bias 7, largest finite 448, no infinities):
+ * q = e4m3(clamp(y * (1 / *qscale), -448, 448)), y the eager chain's bf16
+ * output (the bits ln_modulate writes), 1 / *qscale one IEEE fp32 division,
+ * the product rounded to fp32, the conversion round-to-nearest-even; NaN
+ * stays NaN.  One byte per element: 3 bytes of HBM traffic per element
+ * instead of the 4 + 3 of ln_modulate followed by a quantize pass.
+ *
+ * Source: "Fused Kernels" page, table "Quantized layout producers"
+ * (flux2_layernorm_modulate_fp8_quant: LayerNorm plus adaLN modulation
+ * directly into static FP8 output).
+ *
+ *  qscale   device pointer to the fp32 per-tensor scale (> 0), read by the
+ *           kernel (so the call needs no host synchronization).
+ *  out      [B,S,D] E4M3 bytes, contiguous, V-byte aligned (V as
+ *           adaln_order_for reports: 8 when D % 8 == 0, else 4); must not
+ *           overlap any input.
+ *  Other arguments as ln_modulate (mean_out / rstd_out: the row statistics).
+ */
+int ln_modulate_fp8(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                    int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                    int64_t sshift_b, float eps, const float* qscale, int dtype, void* out,
+                    float* mean_out, float* rstd_out, void* stream);
+
+/*
  * rmsnorm_scale_shift -- out = RMSNorm(x) * (1 + scale) + shift, bf16 at
  * every eager op: x_hat = bf16(x * rinv), then the ln_modulate tail
  * (bf16(1+scale), bf16(x_hat*one_plus), bf16(y+shift)).

@@ -3,7 +3,7 @@ kernels (``libadaln.so``) and this thin torch binding.
 
     from modulate_ln_amd import ln_modulate, residual_gate_add, qk_head_layernorm, bias_gelu_tanh
     from modulate_ln_amd import residual_gate_add_ln_modulate, rmsnorm_scale_shift, qk_rmsnorm
-    from modulate_ln_amd import modulate_scale_shift, temb_table_slices
+    from modulate_ln_amd import modulate_scale_shift, temb_table_slices, ln_modulate_fold, ln_modulate_fp8
 
 The binding only marshals arguments; torch provides device memory and
 streams.  Importing the package does not load the library; the first call
@@ -14,6 +14,8 @@ from ._native import AdalnError, order_for, status_str  # noqa: F401
 from .ops import (  # noqa: F401
     bias_gelu_tanh,
     ln_modulate,
+    ln_modulate_fold,
+    ln_modulate_fp8,
     modulate_scale_shift,
     qk_head_layernorm,
     qk_rmsnorm,
@@ -31,6 +33,8 @@ __all__ = [
     "qk_rmsnorm",
     "modulate_scale_shift",
     "temb_table_slices",
+    "ln_modulate_fold",
+    "ln_modulate_fp8",
     "qk_head_layernorm",
     "bias_gelu_tanh",
     "order_for",

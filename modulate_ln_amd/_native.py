@@ -52,6 +52,8 @@ EXPORTS = (
     "modulate_scale_shift_can_use",
     "temb_table_slices",
     "temb_table_slices_can_use",
+    "ln_modulate_fold",
+    "ln_modulate_fp8",
     "adaln_order_for",
     "adaln_status_str",
     "adaln_abi_version",
@@ -102,6 +104,9 @@ def lib():
     L.modulate_scale_shift_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.temb_table_slices.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, i64, ci, vp, vp]
     L.temb_table_slices_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
+    L.ln_modulate_fold.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp]
+    L.ln_modulate_fp8.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, vp, ci, vp, vp, vp,
+                                  vp]
     L.adaln_order_for.argtypes = [ci, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.adaln_status_str.argtypes = [ci]
     L.adaln_status_str.restype = ctypes.c_char_p

@@ -257,6 +257,76 @@ __device__ __forceinline__ void sum_down(float& s) {
   s = s + lane_down<OFF>(s);
 }
 
+// ---------------------------------------------------------------------------
+// The output stage of the norm + modulate kernels.
+//   kTailChain  the eager chain: x_hat, x_hat * (1 + scale) and + shift each
+//               rounded to bf16
+//   kTailFold   one affine op: bf16(fma(1 + scale, n, shift)) on the unrounded
+//               normalized value n
+//   kTailFp8    the chain's bf16 output times 1/qscale, clamped to +-448 and
+//               converted to OCP FP8 E4M3 (round to nearest even): one byte
+// ---------------------------------------------------------------------------
+constexpr int kTailChain = 0;
+constexpr int kTailFold = 1;
+constexpr int kTailFp8 = 2;
+
+// clamp to the largest finite E4M3 magnitude; NaN passes (the compares are false)
+__device__ __forceinline__ float clamp448(float v) {
+  v = v > 448.0f ? 448.0f : v;
+  return v < -448.0f ? -448.0f : v;
+}
+
+// The same clamp for values known not to be NaN: one v_med3_f32 (which would
+// turn a NaN into -448).
+__device__ __forceinline__ float clamp448_finite(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
+// four fp32 values -> four E4M3 bytes (gfx950's conversion is OCP E4M3 with
+// round-to-nearest-even; it gives NaN, not 448, past 464, hence the clamp)
+__device__ __forceinline__ uint32_t fp8_quad(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// The tail of one element pair: n0, n1 are the normalized values before any
+// rounding, o = bf16(1 + scale) and h = shift as fp32.  Returns two bf16
+// (the chain or the fold).
+template <int TAIL>
+__device__ __forceinline__ uint32_t tail_pair(float n0, float n1, float o0, float o1, float h0, float h1) {
+  if constexpr (TAIL == kTailFold) {
+    return pack_bf16(__builtin_fmaf(o0, n0, h0), __builtin_fmaf(o1, n1, h1));
+  } else {
+    round_pair(n0, n1);  // x_hat = bf16(n)
+    float y0 = n0 * o0, y1 = n1 * o1;
+    round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
+    return pack_bf16(y0 + h0, y1 + h1);  // bf16(y + shift)
+  }
+}
+
+// The FP8 stage for V/2 bf16 pairs w (the chain's output): q = e4m3(clamp(y *
+// qinv)), packed four bytes per word into q[0 .. V/4).  no_nan: the caller
+// knows no value can be NaN (finite row statistics and finite adaLN rows),
+// so the clamp is one v_med3 per element; otherwise NaN-preserving compares.
+template <int V>
+__device__ __forceinline__ void fp8_stage(const uint32_t* w, float qinv, bool no_nan, uint32_t* q) {
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    v[2 * i] = lo_f32(w[i]) * qinv;
+    v[2 * i + 1] = hi_f32(w[i]) * qinv;
+  }
+  if (no_nan) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = clamp448_finite(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = clamp448(v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) q[i] = fp8_quad(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
 __device__ __forceinline__ float bcast_lane0(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -334,6 +404,17 @@ __device__ __forceinline__ void store_vec_nt(uint16_t* p, const Vec<V>& v) {
   } else {
     u32x2 t = {v.w[0], v.w[1]};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+  }
+}
+
+// V E4M3 bytes (four per word of q); p is V-byte aligned
+template <int V>
+__device__ __forceinline__ void store_fp8_nt(uint8_t* p, const uint32_t* q) {
+  if constexpr (V == 8) {
+    u32x2 t = {q[0], q[1]};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+  } else {
+    __builtin_nontemporal_store(q[0], reinterpret_cast<uint32_t*>(p));
   }
 }
 

@@ -44,11 +44,25 @@ struct LnArgs {
   const uint16_t* shift;
   int64_t ssh_b;
   float eps;
-  uint16_t* out;
+  void* out;  // bf16 rows, or E4M3 bytes (kTailFp8)
   float* mean_out;
   float* rstd_out;
   int64_t R;
+  const float* qscale;  // kTailFp8: device pointer to the static scale
 };
+
+// start of output row r: bf16 elements, or bytes for the FP8 tail
+template <int TAIL>
+__device__ __forceinline__ void* out_row(const LnArgs& a, int64_t r) {
+  if constexpr (TAIL == kTailFp8) return static_cast<uint8_t*>(a.out) + r * a.D;
+  return static_cast<uint16_t*>(a.out) + r * a.D;
+}
+
+template <int TAIL>
+__device__ __forceinline__ float qinv_of(const LnArgs& a) {
+  if constexpr (TAIL == kTailFp8) return 1.0f / *a.qscale;
+  return 1.0f;
+}
 
 template <int V, int E>
 __device__ __forceinline__ float elem(const Vec<V>& v) {
@@ -89,31 +103,46 @@ __device__ __forceinline__ void sumsq_lane(const Vec<V>* buf, int64_t nvec, int 
       ...);
 }
 
-// the per-element tail of the chain for one vector (RMS: x * rinv, no mean)
-template <int V, bool RMS>
-__device__ __forceinline__ Vec<V> modulate_vec(const Vec<V>& xv, const Vec<V>& sv, const Vec<V>& hv,
-                                               float mean, float rstd) {
-  Vec<V> o;
+// the per-element tail for one vector (RMS: x * rinv, no mean): V/2 bf16
+// pairs (the chain's output also for the FP8 tail, quantized by put_vec)
+template <int V, bool RMS, int TAIL>
+__device__ __forceinline__ void modulate_vec(const Vec<V>& xv, const Vec<V>& sv, const Vec<V>& hv, float mean,
+                                             float rstd, uint32_t* o) {
 #pragma unroll
   for (int i = 0; i < V / 2; ++i) {
-    float n0 = RMS ? lo_f32(xv.w[i]) * rstd : (lo_f32(xv.w[i]) - mean) * rstd;
-    float n1 = RMS ? hi_f32(xv.w[i]) * rstd : (hi_f32(xv.w[i]) - mean) * rstd;
-    round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean)), or bf16(x * rinv)
+    const float n0 = RMS ? lo_f32(xv.w[i]) * rstd : (lo_f32(xv.w[i]) - mean) * rstd;
+    const float n1 = RMS ? hi_f32(xv.w[i]) * rstd : (hi_f32(xv.w[i]) - mean) * rstd;
     float p0 = 1.0f + lo_f32(sv.w[i]);
     float p1 = 1.0f + hi_f32(sv.w[i]);
     round_pair(p0, p1);  // bf16(1 + scale)
-    float y0 = n0 * p0;
-    float y1 = n1 * p1;
-    round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
-    o.w[i] = pack_bf16(y0 + lo_f32(hv.w[i]), y1 + hi_f32(hv.w[i]));  // bf16(y + shift)
+    o[i] = tail_pair<TAIL>(n0, n1, p0, p1, lo_f32(hv.w[i]), hi_f32(hv.w[i]));
   }
-  return o;
+}
+
+// store one vector's output at element v*V of row orow (bf16 rows may be
+// misaligned under GATHER; FP8 rows are V-byte aligned)
+template <int V, bool GATHER, int TAIL>
+__device__ __forceinline__ void put_vec(void* orow, int64_t v, const uint32_t* o, float qinv) {
+  if constexpr (TAIL == kTailFp8) {
+    uint32_t q8[V / 4];
+    fp8_stage<V>(o, qinv, false, q8);
+    store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
+  } else {
+    Vec<V> ov;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) ov.w[i] = o[i];
+    if constexpr (GATHER)
+      scatter_vec<V>(static_cast<uint16_t*>(orow) + v * V, ov);
+    else
+      store_vec<V>(static_cast<uint16_t*>(orow) + v * V, ov);
+  }
 }
 
 // NV = the largest number of vectors any lane owns for the rows this
 // instantiation serves (the launcher guarantees D/V <= 64*NV).
-template <int V, int NV, bool GATHER, bool RMS>
+template <int V, int NV, bool GATHER, bool RMS, int TAIL>
 __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
+  const float qinv = qinv_of<TAIL>(a);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nvec = a.D / V;
   const float Df = (float)a.D;
@@ -154,7 +183,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 
     const uint16_t* sc = a.scale + b * a.ssc_b;
     const uint16_t* sh = a.shift + b * a.ssh_b;
-    uint16_t* orow = a.out + r * a.D;
+    void* orow = out_row<TAIL>(a, r);
     Vec<V> sv[NV], hv[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -167,10 +196,9 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
     for (int k = 0; k < NV; ++k) {
       const int64_t v = (int64_t)k * kWave + lane;
       if (v < nvec) {
-        if constexpr (GATHER)
-          scatter_vec<V>(orow + v * V, modulate_vec<V, RMS>(buf[k], sv[k], hv[k], mean, rstd));
-        else
-          store_vec<V>(orow + v * V, modulate_vec<V, RMS>(buf[k], sv[k], hv[k], mean, rstd));
+        uint32_t o[V / 2];
+        modulate_vec<V, RMS, TAIL>(buf[k], sv[k], hv[k], mean, rstd, o);
+        put_vec<V, GATHER, TAIL>(orow, v, o, qinv);
       }
     }
   }
@@ -204,7 +232,7 @@ struct TabShape {
 };
 
 
-template <int V, int NV, bool UNIF, bool RMS>
+template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   constexpr bool kPrefetch = TabShape<NV>::kPrefetch;
   constexpr bool kXf32 = TabShape<NV>::kXf32;
@@ -233,17 +261,22 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   Vec<V> bufA[NV];
   Vec<V> bufB[kPrefetch ? NV : 1];
   if (s < S) load_row(bufA, s);
-  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
-                  threadIdx.x, 256);
-  __syncthreads();
+  const bool fin = build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
+                                   threadIdx.x, 256);
+  bool tab_finite = true;
+  if constexpr (TAIL == kTailFp8)
+    tab_finite = __syncthreads_and(fin);
+  else
+    __syncthreads();
   if (s >= S) return;
 
   const float Df = (float)D;
+  const float qinv = qinv_of<TAIL>(a);
   auto process = [&](const Vec<V>* buf, int ss) {
     const int64_t r = (int64_t)b * S + ss;
-    normalize_row<V, NV, UNIF, kXf32, RMS>(buf, tab, nvec, lane, Df, a.eps, a.out + r * D,
-                                      a.mean_out ? a.mean_out + r : nullptr,
-                                      a.rstd_out ? a.rstd_out + r : nullptr);
+    normalize_row<V, NV, UNIF, kXf32, RMS, TAIL>(buf, tab, nvec, lane, Df, a.eps, out_row<TAIL>(a, r),
+                                                 a.mean_out ? a.mean_out + r : nullptr,
+                                                 a.rstd_out ? a.rstd_out + r : nullptr, qinv, tab_finite);
   };
 
   if constexpr (kPrefetch) {
@@ -292,7 +325,7 @@ __device__ __forceinline__ uint32_t join_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-template <int NV, bool UNIF, bool RMS>
+template <int NV, bool UNIF, bool RMS, int TAIL>
 __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sample) {
   constexpr int V = 8;
   extern __shared__ float4 smem[];  // tables [2][2][nvec], then the x tile [8][nvec] (uint4)
@@ -328,9 +361,13 @@ __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sa
           make_uint4(join_hi(w0, w1), join_hi(w2, w3), join_hi(w4, w5), join_hi(w6, w7));
     }
   }
-  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
-                  threadIdx.x, 512);
-  __syncthreads();
+  const bool fin = build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
+                                   threadIdx.x, 512);
+  bool tab_finite = true;
+  if constexpr (TAIL == kTailFp8)
+    tab_finite = __syncthreads_and(fin);
+  else
+    __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // token within the tile
@@ -345,9 +382,9 @@ __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sa
     buf[k].w[3] = t.w;
   }
   const int64_t r = (int64_t)b * S + t0 + w;
-  normalize_row<V, NV, UNIF, true, RMS>(buf, tab, nvec, lane, (float)D, a.eps, a.out + r * D,
-                                   a.mean_out ? a.mean_out + r : nullptr,
-                                   a.rstd_out ? a.rstd_out + r : nullptr);
+  normalize_row<V, NV, UNIF, true, RMS, TAIL>(buf, tab, nvec, lane, (float)D, a.eps, out_row<TAIL>(a, r),
+                                              a.mean_out ? a.mean_out + r : nullptr,
+                                              a.rstd_out ? a.rstd_out + r : nullptr, qinv_of<TAIL>(a), tab_finite);
 }
 
 // Rows too long to hold in registers: the same order, pass 2 re-reads the
@@ -365,8 +402,9 @@ constexpr RcpTable make_rcp_table() {
 }
 __constant__ RcpTable kRcp = make_rcp_table();
 
-template <int V, bool GATHER, bool RMS>
+template <int V, bool GATHER, bool RMS, int TAIL>
 __global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
+  const float qinv = qinv_of<TAIL>(a);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nvec = a.D / V;
   const float Df = (float)a.D;
@@ -406,20 +444,22 @@ __global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
     }
     const uint16_t* sc = a.scale + b * a.ssc_b;
     const uint16_t* sh = a.shift + b * a.ssh_b;
-    uint16_t* orow = a.out + r * a.D;
+    void* orow = out_row<TAIL>(a, r);
     for (int64_t k = 0; k < nv_lane; ++k) {
       const int64_t v = k * kWave + lane;
+      uint32_t o[V / 2];
       if constexpr (GATHER) {
         Vec<V> xv = gather_vec<V>(xr + v * V * a.sx_d, a.sx_d);
         Vec<V> sv = gather_vec<V>(sc + v * V, 1);
         Vec<V> hv = gather_vec<V>(sh + v * V, 1);
-        scatter_vec<V>(orow + v * V, modulate_vec<V, RMS>(xv, sv, hv, mean, rstd));
+        modulate_vec<V, RMS, TAIL>(xv, sv, hv, mean, rstd, o);
       } else {
         Vec<V> xv = load_vec<V>(xr + v * V);
         Vec<V> sv = load_vec<V>(sc + v * V);
         Vec<V> hv = load_vec<V>(sh + v * V);
-        store_vec<V>(orow + v * V, modulate_vec<V, RMS>(xv, sv, hv, mean, rstd));
+        modulate_vec<V, RMS, TAIL>(xv, sv, hv, mean, rstd, o);
       }
+      put_vec<V, GATHER, TAIL>(orow, v, o, qinv);
     }
   }
 }
@@ -432,21 +472,21 @@ inline unsigned grid_for(int64_t R) {
   return (unsigned)std::min(blocks, kMaxBlocks);
 }
 
-template <int V, int NV, bool GATHER, bool RMS>
+template <int V, int NV, bool GATHER, bool RMS, int TAIL>
 int launch_rows(const LnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ln_modulate_rows<V, NV, GATHER, RMS>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ln_modulate_rows<V, NV, GATHER, RMS, TAIL>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int V, bool GATHER, bool RMS>
+template <int V, bool GATHER, bool RMS, int TAIL>
 int launch_stream(const LnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ln_modulate_stream<V, GATHER, RMS>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((ln_modulate_stream<V, GATHER, RMS, TAIL>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
 
-template <int V, int NV, bool UNIF, bool RMS>
+template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 int launch_tab(const LnArgs& a, hipStream_t st) {
   // TabShape<NV>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
   const int64_t B = a.R / a.S;
@@ -456,31 +496,31 @@ int launch_tab(const LnArgs& a, hipStream_t st) {
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
   const int64_t blocks = B * bpb;
   const size_t lds = (size_t)2 * a.D * sizeof(float);
-  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS>), dim3((unsigned)blocks), dim3(256), lds, st, a,
+  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS, TAIL>), dim3((unsigned)blocks), dim3(256), lds, st, a,
                      (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int NV, bool UNIF, bool RMS>
+template <int NV, bool UNIF, bool RMS, int TAIL>
 int launch_tr(const LnArgs& a, hipStream_t st) {
   const int64_t B = a.R / a.S;
   const int64_t tiles_per_sample = a.S / kTrTokens;
   const int64_t nvec = a.D / 8;
   const size_t lds = (size_t)nvec * (4 * sizeof(float4) + kTrTokens * sizeof(uint4));
-  hipLaunchKernelGGL((ln_modulate_tr<NV, UNIF, RMS>), dim3((unsigned)(B * tiles_per_sample)), dim3(512),
+  hipLaunchKernelGGL((ln_modulate_tr<NV, UNIF, RMS, TAIL>), dim3((unsigned)(B * tiles_per_sample)), dim3(512),
                      lds, st, a, (int)tiles_per_sample);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 constexpr int kTrMaxD = 4096;  // 96 KiB of LDS (tables + tile)
 
-template <bool RMS>
+template <bool RMS, int TAIL>
 int dispatch_tr(const LnArgs& a, hipStream_t st) {
   const int64_t nvec = a.D / 8;
   const int64_t nv = (nvec + kWave - 1) / kWave;
   const bool unif = nvec % kWave == 0;
 #define ADALN_TR_CASE(N) \
-  if (nv == N) return unif ? launch_tr<N, true, RMS>(a, st) : launch_tr<N, false, RMS>(a, st);
+  if (nv == N) return unif ? launch_tr<N, true, RMS, TAIL>(a, st) : launch_tr<N, false, RMS, TAIL>(a, st);
   ADALN_TR_CASE(1)
   ADALN_TR_CASE(2)
   ADALN_TR_CASE(3)
@@ -493,13 +533,14 @@ int dispatch_tr(const LnArgs& a, hipStream_t st) {
   return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
 }
 
-template <int V, bool RMS>
+template <int V, bool RMS, int TAIL>
 int dispatch_tab(const LnArgs& a, hipStream_t st) {
   const int64_t nvec = a.D / V;
   const int64_t nv = (nvec + kWave - 1) / kWave;
   const bool unif = nvec % kWave == 0;
 #define ADALN_TAB_CASE(N)                                                           \
-  if (nv == N) return unif ? launch_tab<V, N, true, RMS>(a, st) : launch_tab<V, N, false, RMS>(a, st);
+  if (nv == N)                                                                     \
+    return unif ? launch_tab<V, N, true, RMS, TAIL>(a, st) : launch_tab<V, N, false, RMS, TAIL>(a, st);
   ADALN_TAB_CASE(1)
   ADALN_TAB_CASE(2)
   ADALN_TAB_CASE(3)
@@ -521,11 +562,11 @@ int dispatch_tab(const LnArgs& a, hipStream_t st) {
 }
 
 // vectors per lane -> the register-resident instantiation that covers it
-template <int V, bool GATHER, bool RMS>
+template <int V, bool GATHER, bool RMS, int TAIL>
 int dispatch(const LnArgs& a, hipStream_t st) {
   const int64_t nv = (a.D / V + kWave - 1) / kWave;
 #define ADALN_NV_CASE(N) \
-  if (nv <= N) return launch_rows<V, N, GATHER, RMS>(a, st);
+  if (nv <= N) return launch_rows<V, N, GATHER, RMS, TAIL>(a, st);
   ADALN_NV_CASE(1)
   ADALN_NV_CASE(2)
   ADALN_NV_CASE(3)
@@ -537,7 +578,7 @@ int dispatch(const LnArgs& a, hipStream_t st) {
   ADALN_NV_CASE(12)
   ADALN_NV_CASE(16)
 #undef ADALN_NV_CASE
-  return launch_stream<V, GATHER, RMS>(a, st);
+  return launch_stream<V, GATHER, RMS, TAIL>(a, st);
 }
 
 }  // namespace
@@ -559,34 +600,39 @@ static int ln_modulate_check_shape(int64_t B, int64_t S, int64_t D, int64_t sx_b
   return ADALN_OK;
 }
 
-// The entry point of both norms: validation, aliasing rules, then the
-// kernel family the layout selects (RMS: RMSNorm statistics, no mean).
-template <bool RMS>
+// The entry point of every norm + modulate variant: validation, aliasing
+// rules, then the kernel family the layout selects (RMS: RMSNorm statistics,
+// no mean; TAIL: the output stage, see kTailChain / kTailFold / kTailFp8).
+template <bool RMS, int TAIL>
 static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
                          int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
                          int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
-                         float* rstd_out, void* stream) {
+                         float* rstd_out, const float* qscale, void* stream) {
+  constexpr bool kFp8 = TAIL == kTailFp8;
   int rc = ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype);
   if (rc != ADALN_OK) return rc;
   if (!(eps >= 0.0f) || eps > 3.0e38f) return ADALN_ERR_ARG;  // also rejects NaN
   const int64_t R = B * S;
   if (R == 0) return ADALN_OK;
-  if (!x || !scale || !shift || !out) return ADALN_ERR_NULL;
-  if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(out, 2) ||
-      !aligned(mean_out, 4) || !aligned(rstd_out, 4))
+  if (!x || !scale || !shift || !out || (kFp8 && !qscale)) return ADALN_ERR_NULL;
+  int V = 0;
+  order_for(RMS ? ADALN_OP_RMSNORM_SCALE_SHIFT : ADALN_OP_LN_MODULATE, D, &V, nullptr);
+  if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(out, kFp8 ? V : 2) ||
+      !aligned(mean_out, 4) || !aligned(rstd_out, 4) || !aligned(qscale, 4))
     return ADALN_ERR_ALIGN;
 
-  // overlap rules: out may be exactly a contiguous x; nothing else may overlap
-  const Span so = span_of(out, {{R * D, 1}});
+  // overlap rules: a bf16 out may be exactly a contiguous x; nothing else may overlap
+  const Span so = span_of(out, {{R * D, 1}}, kFp8 ? 1 : 2);
   const Span sx = span_of(x, {{B, sx_b}, {S, sx_s}, {D, sx_d}});
   const Span ssc = span_of(scale, {{B, sscale_b}, {D, 1}});
   const Span ssh = span_of(shift, {{B, sshift_b}, {D, 1}});
+  const Span sq = qscale ? Span{(uintptr_t)qscale, (uintptr_t)(qscale + 1)} : Span{};
   const bool x_contig = sx_d == 1 && (S == 1 || sx_s == D) && (B == 1 || sx_b == S * D);
-  if (overlaps(so, sx) && !(x == out && x_contig)) return ADALN_ERR_ALIAS;
-  if (overlaps(so, ssc) || overlaps(so, ssh)) return ADALN_ERR_ALIAS;
+  if (overlaps(so, sx) && (kFp8 || !(x == out && x_contig))) return ADALN_ERR_ALIAS;
+  if (overlaps(so, ssc) || overlaps(so, ssh) || overlaps(so, sq)) return ADALN_ERR_ALIAS;
   const Span sm = mean_out ? Span{(uintptr_t)mean_out, (uintptr_t)(mean_out + R)} : Span{};
   const Span sr = rstd_out ? Span{(uintptr_t)rstd_out, (uintptr_t)(rstd_out + R)} : Span{};
-  for (const Span* t : {&so, &sx, &ssc, &ssh})
+  for (const Span* t : {&so, &sx, &ssc, &ssh, &sq})
     if (overlaps(sm, *t) || overlaps(sr, *t)) return ADALN_ERR_ALIAS;
   if (overlaps(sm, sr)) return ADALN_ERR_ALIAS;
 
@@ -602,32 +648,33 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   a.shift = (const uint16_t*)shift;
   a.ssh_b = sshift_b;
   a.eps = eps;
-  a.out = (uint16_t*)out;
+  a.out = out;
   a.mean_out = mean_out;
   a.rstd_out = rstd_out;
   a.R = R;
+  a.qscale = qscale;
 
-  int V = 0;
-  order_for(RMS ? ADALN_OP_RMSNORM_SCALE_SHIFT : ADALN_OP_LN_MODULATE, D, &V, nullptr);
-  // vector loads need every row start of x, scale, shift and out on a 2V-byte boundary
+  // vector loads need every row start of x, scale, shift and out on a 2V-byte
+  // boundary (V bytes for an FP8 out)
   const uintptr_t vb = (uintptr_t)(2 * V);
+  const uintptr_t ob = kFp8 ? (uintptr_t)V : vb;
   auto stride_ok = [&](int64_t n, int64_t st) { return n <= 1 || ((uintptr_t)st * 2u) % vb == 0; };
   const bool vec = sx_d == 1 && aligned(x, vb) && aligned(scale, vb) && aligned(shift, vb) &&
-                   aligned(out, vb) && stride_ok(B, sx_b) && stride_ok(S, sx_s) &&
+                   aligned(out, ob) && stride_ok(B, sx_b) && stride_ok(S, sx_s) &&
                    stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
   hipStream_t st = (hipStream_t)stream;
   // the tabled fast path indexes rows, samples and offsets in 32 bits
   const bool tab = vec && D <= kTabMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
                    B <= INT32_MAX;
-  if (tab) return V == 8 ? dispatch_tab<8, RMS>(a, st) : dispatch_tab<4, RMS>(a, st);
+  if (tab) return V == 8 ? dispatch_tab<8, RMS, TAIL>(a, st) : dispatch_tab<4, RMS, TAIL>(a, st);
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
                   B * (S / kTrTokens) < INT32_MAX && aligned(x, 16) && sx_d % 8 == 0 &&
                   (B == 1 || sx_b % 8 == 0) && aligned(scale, 16) && aligned(shift, 16) &&
-                  aligned(out, 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
-  if (tr) return dispatch_tr<RMS>(a, st);
-  if (V == 8) return vec ? dispatch<8, false, RMS>(a, st) : dispatch<8, true, RMS>(a, st);
-  return vec ? dispatch<4, false, RMS>(a, st) : dispatch<4, true, RMS>(a, st);
+                  aligned(out, kFp8 ? 8 : 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
+  if (tr) return dispatch_tr<RMS, TAIL>(a, st);
+  if (V == 8) return vec ? dispatch<8, false, RMS, TAIL>(a, st) : dispatch<8, true, RMS, TAIL>(a, st);
+  return vec ? dispatch<4, false, RMS, TAIL>(a, st) : dispatch<4, true, RMS, TAIL>(a, st);
 }
 
 }  // namespace adaln
@@ -643,8 +690,8 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
                            int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
                            const void* shift, int64_t sshift_b, float eps, int dtype, void* out,
                            float* mean_out, float* rstd_out, void* stream) {
-  return norm_modulate<false>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b, eps,
-                              dtype, out, mean_out, rstd_out, stream);
+  return norm_modulate<false, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
+                                          eps, dtype, out, mean_out, rstd_out, nullptr, stream);
 }
 
 extern "C" int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b,
@@ -657,6 +704,22 @@ extern "C" int rmsnorm_scale_shift(const void* x, int64_t B, int64_t S, int64_t 
                                    int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
                                    const void* shift, int64_t sshift_b, float eps, int dtype,
                                    void* out, float* rinv_out, void* stream) {
-  return norm_modulate<true>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b, eps,
-                             dtype, out, nullptr, rinv_out, stream);
+  return norm_modulate<true, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b, eps,
+                                         dtype, out, nullptr, rinv_out, nullptr, stream);
+}
+
+extern "C" int ln_modulate_fold(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                                int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
+                                const void* shift, int64_t sshift_b, float eps, int dtype, void* out,
+                                float* mean_out, float* rstd_out, void* stream) {
+  return norm_modulate<false, kTailFold>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
+                                         eps, dtype, out, mean_out, rstd_out, nullptr, stream);
+}
+
+extern "C" int ln_modulate_fp8(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
+                               int64_t sx_s, int64_t sx_d, const void* scale, int64_t sscale_b,
+                               const void* shift, int64_t sshift_b, float eps, const float* qscale,
+                               int dtype, void* out, float* mean_out, float* rstd_out, void* stream) {
+  return norm_modulate<false, kTailFp8>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
+                                        eps, dtype, out, mean_out, rstd_out, qscale, stream);
 }

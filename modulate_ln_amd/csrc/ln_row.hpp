@@ -65,10 +65,12 @@ __device__ __forceinline__ float hi_f32_again(uint32_t w) {
 // The per-sample tables: bf16(1 + scale) and shift as fp32, float4-packed
 // [table][V/4][nvec] so a lane's reads for vector v are contiguous across
 // the wave.  Built cooperatively by the nthreads threads of a block.
+// Returns whether every value this thread wrote is finite.
 template <int V>
-__device__ __forceinline__ void build_tables(float4* tab, const uint16_t* sc, const uint16_t* sh,
+__device__ __forceinline__ bool build_tables(float4* tab, const uint16_t* sc, const uint16_t* sh,
                                              int nvec, int tid, int nthreads) {
   const int shift_off = (V / 4) * nvec;
+  bool finite = true;
   for (int v = tid; v < nvec; v += nthreads) {
     const Vec<V> sv = load_vec<V>(sc + v * V);
     const Vec<V> hv = load_vec<V>(sh + v * V);
@@ -79,10 +81,15 @@ __device__ __forceinline__ void build_tables(float4* tab, const uint16_t* sc, co
       round_pair(o0, o1);  // bf16(1 + scale)
       round_pair(o2, o3);
       tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
-      tab[shift_off + q * nvec + v] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
-                                                  lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
+      const float h0 = lo_f32(hv.w[2 * q]), h1 = hi_f32(hv.w[2 * q]);
+      const float h2 = lo_f32(hv.w[2 * q + 1]), h3 = hi_f32(hv.w[2 * q + 1]);
+      tab[shift_off + q * nvec + v] = make_float4(h0, h1, h2, h3);
+      finite = finite && __builtin_isfinite(o0) && __builtin_isfinite(o1) && __builtin_isfinite(o2) &&
+               __builtin_isfinite(o3) && __builtin_isfinite(h0) && __builtin_isfinite(h1) &&
+               __builtin_isfinite(h2) && __builtin_isfinite(h3);
     }
   }
+  return finite;
 }
 
 // Third table of the residual-update-fused kernel: the per-sample gate as
@@ -108,11 +115,13 @@ __device__ __forceinline__ void build_gate_table(float4* tab, const uint16_t* gt
 // rstd_out; mean_out is unused).
 // kXf32: widen the row once and keep it in fp32 for both passes; otherwise
 // widen it for the reduction and again (opaque to the compiler, so no fp32
-// copy stays live) when normalizing.
-template <int V, int NV, bool UNIF, bool kXf32, bool RMS = false>
+// copy stays live) when normalizing.  TAIL selects the output stage
+// (kTailChain, kTailFold: bf16 row at orow; kTailFp8: E4M3 bytes at orow,
+// scaled by qinv).
+template <int V, int NV, bool UNIF, bool kXf32, bool RMS = false, int TAIL = kTailChain>
 __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* tab, int nvec, int lane,
-                                              float Df, float eps, uint16_t* orow, float* mean_out,
-                                              float* rstd_out) {
+                                              float Df, float eps, void* orow, float* mean_out,
+                                              float* rstd_out, float qinv = 1.0f, bool tab_finite = false) {
   const int shift_off = (V / 4) * nvec;
   float xf[NV][V];
 #pragma unroll
@@ -161,6 +170,10 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     if (!RMS && mean_out) *mean_out = mean;
     if (rstd_out) *rstd_out = rstd;
   }
+  // FP8: with finite statistics, finite adaLN rows and a finite 1/qscale no
+  // output can be NaN (an overflow to infinity still clamps to +-448)
+  const bool no_nan = tab_finite && __builtin_isfinite(mean) && __builtin_isfinite(rstd) &&
+                      __builtin_isfinite(qinv);
   __builtin_amdgcn_sched_barrier(0);
   // table values for step k are read one step ahead of their use
   float4 ot[V / 4], ht[V / 4];
@@ -185,7 +198,7 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     if (k + 1 < NV) read_tab(k + 1);
     const int v = k * kWave + lane;
     if (UNIF || v < nvec) {
-      Vec<V> o;
+      uint32_t o[V / 2];  // bf16 pairs
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) {
         float n0, n1, n2, n3;
@@ -200,15 +213,20 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
           n2 = (xval(k, 4 * q + 2) - mean) * rstd;
           n3 = (xval(k, 4 * q + 3) - mean) * rstd;
         }
-        round_pair(n0, n1);  // x_hat = bf16(rstd * (x - mean)), or bf16(x * rinv)
-        round_pair(n2, n3);
-        float y0 = n0 * oc[q].x, y1 = n1 * oc[q].y, y2 = n2 * oc[q].z, y3 = n3 * oc[q].w;
-        round_pair(y0, y1);  // bf16(x_hat * (1 + scale))
-        round_pair(y2, y3);
-        o.w[2 * q] = pack_bf16(y0 + hc[q].x, y1 + hc[q].y);  // bf16(y + shift)
-        o.w[2 * q + 1] = pack_bf16(y2 + hc[q].z, y3 + hc[q].w);
+        // n = rstd * (x - mean), or x * rinv; then the output stage
+        o[2 * q] = tail_pair<TAIL>(n0, n1, oc[q].x, oc[q].y, hc[q].x, hc[q].y);
+        o[2 * q + 1] = tail_pair<TAIL>(n2, n3, oc[q].z, oc[q].w, hc[q].z, hc[q].w);
       }
-      store_vec_nt<V>(orow + v * V, o);
+      if constexpr (TAIL == kTailFp8) {
+        uint32_t q8[V / 4];
+        fp8_stage<V>(o, qinv, no_nan, q8);
+        store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
+      } else {
+        Vec<V> ov;
+#pragma unroll
+        for (int i = 0; i < V / 2; ++i) ov.w[i] = o[i];
+        store_vec_nt<V>(static_cast<uint16_t*>(orow) + v * V, ov);
+      }
     }
     // keep two steps' table values live at a time (the scheduler would
     // otherwise hoist every LDS read and halve the occupancy)

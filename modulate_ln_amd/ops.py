@@ -92,6 +92,60 @@ def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: 
     return call if prepare else call()
 
 
+def _ln_common(x, scale, shift, out, out_dtype, mean_out, rstd_out):
+    _require(x, "x")
+    _require(scale, "scale")
+    _require(shift, "shift")
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D], got %s" % (tuple(x.shape),))
+    B, S, D = x.shape
+    scale, ssc = _rows_view(scale, B, D, "scale")
+    shift, ssh = _rows_view(shift, B, D, "shift")
+    if out is None:
+        out = torch.empty((B, S, D), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous %s [B,S,D] tensor" % out_dtype)
+    for name, t in (("mean_out", mean_out), ("rstd_out", rstd_out)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * S or not t.is_contiguous()
+                              or t.device != x.device):
+            raise ValueError("%s must be a contiguous float32 tensor of B*S elements on x's device" % name)
+    return B, S, D, scale, ssc, shift, ssh, out
+
+
+def ln_modulate_fold(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
+                     out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
+                     rstd_out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """layer_norm(x, weight=1 + scale, bias=shift) with one rounding: the high-quality-tier fold
+    (not the eager chain's bits)."""
+    B, S, D, scale, ssc, shift, ssh, out = _ln_common(x, scale, shift, out, torch.bfloat16, mean_out, rstd_out)
+    st = _stream_handle(x, stream)
+    call = Prepared("ln_modulate_fold", N.lib().ln_modulate_fold, (
+        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
+        mean_out.data_ptr() if mean_out is not None else None,
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+    return call if prepare else call()
+
+
+def ln_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, qscale: torch.Tensor,
+                    eps: float = 1e-6, *, out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
+                    rstd_out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """ln_modulate's bf16 output quantized to static OCP FP8 E4M3 (torch.float8_e4m3fn) with the
+    per-tensor scale qscale (a 1-element float32 device tensor)."""
+    if not isinstance(qscale, torch.Tensor) or qscale.dtype != torch.float32 or qscale.numel() != 1 \
+            or qscale.device != x.device:
+        raise ValueError("qscale must be a 1-element float32 tensor on x's device")
+    B, S, D, scale, ssc, shift, ssh, out = _ln_common(x, scale, shift, out, torch.float8_e4m3fn, mean_out,
+                                                      rstd_out)
+    st = _stream_handle(x, stream)
+    call = Prepared("ln_modulate_fp8", N.lib().ln_modulate_fp8, (
+        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), qscale.data_ptr(), N.BF16, out.data_ptr(),
+        mean_out.data_ptr() if mean_out is not None else None,
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+    return call if prepare else call()
+
+
 def rmsnorm_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
                         out: torch.Tensor | None = None, rinv_out: torch.Tensor | None = None, stream=None,
                         prepare: bool = False):

@@ -310,3 +310,24 @@ def test_modulate_and_temb_rejections(L):
     assert temb(out=P1 + 64) == N.ERR_ALIAS  # out over temb
     assert temb(out=P0 + 4) == N.ERR_ALIAS  # out over the table
     assert temb(table=None, t=None, out=None, M=0) == N.OK
+
+
+def test_fold_and_fp8_rejections(L):
+    P5 = 0x60000000
+
+    assert L.ln_modulate_fold(P0, 1, 4, 6, 24, 6, 1, P1, 6, P2, 6, 1e-6, N.BF16, P3, None, None, None) == N.ERR_SHAPE
+    assert L.ln_modulate_fold(P0, 1, 4, 8, 32, 8, 1, P1, 8, P2, 8, 1e-6, N.BF16, P0 + 16, None, None, None) == N.ERR_ALIAS
+
+    def fp8(x=P0, scale=P1, shift=P2, q=P4, out=P3, D=8, S=4, dtype=N.BF16, eps=1e-6, mean=None):
+        return L.ln_modulate_fp8(x, 1, S, D, S * D, D, 1, scale, D, shift, D, eps, q, dtype, out, mean, None, None)
+
+    assert fp8(dtype=2) == N.ERR_DTYPE
+    assert fp8(D=6) == N.ERR_SHAPE
+    assert fp8(eps=float("nan")) == N.ERR_ARG
+    assert fp8(q=None) == N.ERR_NULL
+    assert fp8(q=P4 + 2) == N.ERR_ALIGN
+    assert fp8(out=P3 + 4) == N.ERR_ALIGN  # V = 8: 8-byte aligned rows of bytes
+    assert fp8(out=P0) == N.ERR_ALIAS  # an FP8 out may not alias x, not even exactly
+    assert fp8(out=P4 - 8) == N.ERR_ALIAS  # out over the scale value
+    assert fp8(mean=P5, out=P5 + 8) == N.ERR_ALIAS
+    assert fp8(x=None, scale=None, shift=None, q=None, out=None, S=0) == N.OK
