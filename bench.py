@@ -156,10 +156,11 @@ def main() -> int:
     wall = time.perf_counter() - t0
     step_ms = e_start.elapsed_time(e_end) / K
 
-    # per-kernel average duration: each kernel alone, K back-to-back launches
-    # over the same rotated buffers, bracketed by events on the same stream
-    lnm_us = time_loop(lnm_calls, K, stream)
-    rga_us = time_loop(rga_calls, K, stream)
+    # per-kernel duration: each kernel alone over the same rotated buffers, 20
+    # repetitions x 50 back-to-back launches bracketed by events on the launch
+    # stream, the median repetition
+    lnm_us = time_loop(lnm_calls, 1000, stream)
+    rga_us = time_loop(rga_calls, 1000, stream)
     lb, rb = lnm_bytes(R, D, B), rga_bytes(R, D, B)
     step_gbps = (lb + rb) / (step_ms * 1e-3) / 1e9
     lnm_gbps = lb / (lnm_us * 1e-6) / 1e9
@@ -191,7 +192,7 @@ def main() -> int:
     }
 
     # same buffers every call (67 MB fits the 256 MB MALL): reported apart, not the headline
-    hot_us = time_loop(lnm_calls[:1], K, stream)
+    hot_us = time_loop(lnm_calls[:1], 1000, stream)
     result["ln_modulate_hot_same_buffer"] = {"us": round(hot_us, 3), "GBps": round(lb / hot_us / 1e3, 1),
                                              "note": "one buffer set reused, possibly MALL-assisted"}
     # host cost of a call: a marshalled call (ctypes only) and the full binding
@@ -245,20 +246,29 @@ def main() -> int:
     return 0
 
 
-def time_loop(calls, n, stream):
-    """Average µs per launch of n back-to-back calls (rotating through calls)."""
+def time_loop(calls, n, stream, reps=20):
+    """µs per launch of back-to-back calls (rotating through calls): `reps` repetitions of
+    n // reps launches each, events on the launch stream around every repetition, the
+    median repetition reported."""
+    import statistics
+
     import torch
 
     for c in calls[: min(len(calls), 4)]:
         c()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, min(reps, n))
+    per = max(1, n // reps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(n):
-        calls[i % len(calls)]()
-    e1.record(stream)
+    k = 0
+    ev[0].record(stream)
+    for r in range(reps):
+        for _ in range(per):
+            calls[k % len(calls)]()
+            k += 1
+        ev[r + 1].record(stream)
     torch.cuda.synchronize()
-    return 1000.0 * e0.elapsed_time(e1) / n
+    return statistics.median(1000.0 * ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps))
 
 
 def other_workloads(m, W, dev, stream, log):
@@ -393,7 +403,7 @@ def other_workloads(m, W, dev, stream, log):
     Bt, Lt, Mt, Dt = temb.shape
     out_t = torch.empty((Mt, Bt, Lt, Dt), dtype=torch.float32, device=dev)
     call = m.temb_table_slices(table, temb, out=out_t, prepare=True)
-    us = time_loop([call], 10, stream)
+    us = time_loop([call], 10, stream, reps=5)
     b = Bt * Lt * Mt * Dt * (2 + 4) + Mt * Dt * 4
     entry = {"ms": round(us / 1e3, 4), "GBps": round(b / us / 1e3, 1)}
     del out_t

@@ -331,10 +331,23 @@ __device__ __forceinline__ float bcast_lane0(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
+// 2^-k when D = 2^k, else 0.  For such D, m2 * 2^-k is exactly m2 / D (both
+// are the correctly rounded value of the same real number), without the
+// division sequence.
+__device__ __forceinline__ float pow2_inverse(int64_t D) {
+  return (D > 0 && (D & (D - 1)) == 0) ? __builtin_ldexpf(1.0f, -__builtin_ctzll((uint64_t)D)) : 0.0f;
+}
+
 // var = m2/D, rstd = 1/sqrt(var + eps): IEEE division and square root.
 // (With m2 the sum of squares this is RMSNorm's 1/sqrt(mean(x^2) + eps).)
-__device__ __forceinline__ float finalize_rstd(float m2, float D, float eps) {
-  float var = m2 / D;
+// invD: pow2_inverse(D), a wave-uniform value; non-zero selects the exact
+// multiplication in place of the division.
+__device__ __forceinline__ float finalize_rstd(float m2, float D, float eps, float invD = 0.0f) {
+  float var;
+  if (invD != 0.0f)
+    var = m2 * invD;
+  else
+    var = m2 / D;
   float t = var + eps;
   float s = __builtin_sqrtf(t);
   return 1.0f / s;

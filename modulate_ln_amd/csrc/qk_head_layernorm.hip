@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
   const int l16 = lane & (kGroup - 1);
   const int64_t nvec = a.Dh / V;
   const float Df = (float)a.Dh;
+  const float invD = pow2_inverse(a.Dh);
   const int64_t nv_lane = nvec > l16 ? (nvec - l16 + kGroup - 1) / kGroup : 0;
   const int64_t total = 2 * a.Rq;
   for (int64_t h = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 4); h < total;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void qk_rows(QkArgs a) {
       float n = (float)(nv_lane * V);
       merge_lanes<kGroup>(mean, m2, n, lane);
     }
-    const float rstd = finalize_rstd(m2, Df, a.eps);
+    const float rstd = finalize_rstd(m2, Df, a.eps, invD);
 
     uint16_t* orow = sd.out + rr * a.Dh;
 #pragma unroll
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
   const int group = threadIdx.x >> 4;
   const int nvec = (int)(a.Dh / V);
   const float Df = (float)a.Dh;
+  const float invD = pow2_inverse(a.Dh);
   const int nv_lane = nvec / kGroup + (l16 < nvec % kGroup ? 1 : 0);
   int off[NV];  // element offset of the lane's k-th vector within a head (clamped)
 #pragma unroll
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
         float n = (float)(nv_lane * V);
         merge_lanes<kGroup>(mean, m2, n, lane);
       }
-      const float rstd = finalize_rstd(m2, Df, a.eps);
+      const float rstd = finalize_rstd(m2, Df, a.eps, invD);
       if (h0 + i < a.Rq) {
         uint16_t* orow = sd.out + (h0 + i) * a.Dh;
 #pragma unroll
