@@ -284,8 +284,10 @@ __device__ __forceinline__ float clamp448_finite(float v) {
 
 // four fp32 values -> four E4M3 bytes (gfx950's conversion is OCP E4M3 with
 // round-to-nearest-even; it gives NaN, not 448, past 464, hence the clamp)
+// (The first conversion fills the low half-word and keeps the high one, which
+// the second overwrites: seeding it with a's bits spares a register clear.)
 __device__ __forceinline__ uint32_t fp8_quad(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 

@@ -220,22 +220,57 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // ---------------------------------------------------------------------------
 // Launch shape of the fast path, measured on MI355X (all variants give the
 // same bits).  Rows of 7-8 vectors per lane prefetch the next row into a
-// second buffer and re-widen x from bf16 when normalizing, to stay at three
-// waves per SIMD; shorter rows keep one buffer and an fp32 copy of x;
-// longer rows (up to 16 vectors per lane, 64 KiB of tables) keep one
-// buffer and re-widen.  Grid: blocks per compute unit in total.
-template <int NV>
+// second buffer.  The bf16 stages re-widen x from bf16 when normalizing, to
+// stay at three waves per SIMD; the FP8 stage, whose extra VALU work per
+// row makes a row's compute the critical path, keeps an fp32 copy of x at
+// two waves per SIMD.  Shorter rows keep one buffer and an fp32 copy of x;
+// longer rows (up to 16 vectors per lane, 64 KiB of tables) keep one buffer
+// and re-widen.  Grid: blocks per compute unit in total.
+#ifndef ADALN_TAB_BPC_LN
+#define ADALN_TAB_BPC_LN 3
+#endif
+#ifndef ADALN_TAB_XF32_LN
+#define ADALN_TAB_XF32_LN 0
+#endif
+#ifndef ADALN_TAB_BPC_FOLD
+#define ADALN_TAB_BPC_FOLD 3
+#endif
+#ifndef ADALN_TAB_XF32_FOLD
+#define ADALN_TAB_XF32_FOLD 0
+#endif
+#ifndef ADALN_TAB_BPC_RMS
+#define ADALN_TAB_BPC_RMS 3
+#endif
+#ifndef ADALN_TAB_XF32_RMS
+#define ADALN_TAB_XF32_RMS 0
+#endif
+#ifndef ADALN_TAB_BPC_FP8
+#define ADALN_TAB_BPC_FP8 2
+#endif
+#ifndef ADALN_TAB_XF32_FP8
+#define ADALN_TAB_XF32_FP8 1
+#endif
+template <int NV, bool RMS, int TAIL>
 struct TabShape {
-  static constexpr bool kPrefetch = NV == 7 || NV == 8;
-  static constexpr bool kXf32 = NV <= 6;
-  static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (NV <= 8 ? 3 : 2);
+  static constexpr bool kLong = NV == 7 || NV == 8;
+  static constexpr int kBpcLong = TAIL == kTailFp8    ? ADALN_TAB_BPC_FP8
+                                  : TAIL == kTailFold ? ADALN_TAB_BPC_FOLD
+                                  : RMS               ? ADALN_TAB_BPC_RMS
+                                                      : ADALN_TAB_BPC_LN;
+  static constexpr bool kXf32Long = TAIL == kTailFp8    ? ADALN_TAB_XF32_FP8
+                                    : TAIL == kTailFold ? ADALN_TAB_XF32_FOLD
+                                    : RMS               ? ADALN_TAB_XF32_RMS
+                                                        : ADALN_TAB_XF32_LN;
+  static constexpr bool kPrefetch = kLong;
+  static constexpr bool kXf32 = NV <= 6 || (kLong && kXf32Long);
+  static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (kLong ? kBpcLong : 2);
 };
 
 
 template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
-  constexpr bool kPrefetch = TabShape<NV>::kPrefetch;
-  constexpr bool kXf32 = TabShape<NV>::kXf32;
+  constexpr bool kPrefetch = TabShape<NV, RMS, TAIL>::kPrefetch;
+  constexpr bool kXf32 = TabShape<NV, RMS, TAIL>::kXf32;
   extern __shared__ float4 tab[];  // [2][V/4][nvec] float4: bf16(1+scale), then shift
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -488,10 +523,10 @@ constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
 
 template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 int launch_tab(const LnArgs& a, hipStream_t st) {
-  // TabShape<NV>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
+  // TabShape<NV, RMS, TAIL>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
   const int64_t B = a.R / a.S;
   const int cus = cu_count();
-  const int64_t target = (int64_t)TabShape<NV>::kBlocksPerCu * (cus > 0 ? cus : 256);
+  const int64_t target = (int64_t)TabShape<NV, RMS, TAIL>::kBlocksPerCu * (cus > 0 ? cus : 256);
   int64_t bpb = (target + B - 1) / B;
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
   const int64_t blocks = B * bpb;

@@ -8,6 +8,7 @@
 // on sglang PR #34008, 关键源码片段 (_welford_push).
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
@@ -170,10 +171,6 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     if (!RMS && mean_out) *mean_out = mean;
     if (rstd_out) *rstd_out = rstd;
   }
-  // FP8: with finite statistics, finite adaLN rows and a finite 1/qscale no
-  // output can be NaN (an overflow to infinity still clamps to +-448)
-  const bool no_nan = tab_finite && __builtin_isfinite(mean) && __builtin_isfinite(rstd) &&
-                      __builtin_isfinite(qinv);
   __builtin_amdgcn_sched_barrier(0);
   // table values for step k are read one step ahead of their use
   float4 ot[V / 4], ht[V / 4];
@@ -186,51 +183,68 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
       ht[q] = tab[shift_off + q * nvec + vc];
     }
   };
-  read_tab(0);
+  // NO_NAN (FP8 only) is decided once per row, so the vector loop has no
+  // branch that would split its schedule
+  auto steps = [&](auto no_nan_c) {
+    constexpr bool NO_NAN = decltype(no_nan_c)::value;
+    read_tab(0);
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    float4 oc[V / 4], hc[V / 4];
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      oc[q] = ot[q];
-      hc[q] = ht[q];
-    }
-    if (k + 1 < NV) read_tab(k + 1);
-    const int v = k * kWave + lane;
-    if (UNIF || v < nvec) {
-      uint32_t o[V / 2];  // bf16 pairs
+    for (int k = 0; k < NV; ++k) {
+      float4 oc[V / 4], hc[V / 4];
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) {
-        float n0, n1, n2, n3;
-        if constexpr (RMS) {
-          n0 = xval(k, 4 * q) * rstd;
-          n1 = xval(k, 4 * q + 1) * rstd;
-          n2 = xval(k, 4 * q + 2) * rstd;
-          n3 = xval(k, 4 * q + 3) * rstd;
-        } else {
-          n0 = (xval(k, 4 * q) - mean) * rstd;
-          n1 = (xval(k, 4 * q + 1) - mean) * rstd;
-          n2 = (xval(k, 4 * q + 2) - mean) * rstd;
-          n3 = (xval(k, 4 * q + 3) - mean) * rstd;
-        }
-        // n = rstd * (x - mean), or x * rinv; then the output stage
-        o[2 * q] = tail_pair<TAIL>(n0, n1, oc[q].x, oc[q].y, hc[q].x, hc[q].y);
-        o[2 * q + 1] = tail_pair<TAIL>(n2, n3, oc[q].z, oc[q].w, hc[q].z, hc[q].w);
+        oc[q] = ot[q];
+        hc[q] = ht[q];
       }
-      if constexpr (TAIL == kTailFp8) {
-        uint32_t q8[V / 4];
-        fp8_stage<V>(o, qinv, no_nan, q8);
-        store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
-      } else {
-        Vec<V> ov;
+      if (k + 1 < NV) read_tab(k + 1);
+      const int v = k * kWave + lane;
+      if (UNIF || v < nvec) {
+        uint32_t o[V / 2];  // bf16 pairs
 #pragma unroll
-        for (int i = 0; i < V / 2; ++i) ov.w[i] = o[i];
-        store_vec_nt<V>(static_cast<uint16_t*>(orow) + v * V, ov);
+        for (int q = 0; q < V / 4; ++q) {
+          float n0, n1, n2, n3;
+          if constexpr (RMS) {
+            n0 = xval(k, 4 * q) * rstd;
+            n1 = xval(k, 4 * q + 1) * rstd;
+            n2 = xval(k, 4 * q + 2) * rstd;
+            n3 = xval(k, 4 * q + 3) * rstd;
+          } else {
+            n0 = (xval(k, 4 * q) - mean) * rstd;
+            n1 = (xval(k, 4 * q + 1) - mean) * rstd;
+            n2 = (xval(k, 4 * q + 2) - mean) * rstd;
+            n3 = (xval(k, 4 * q + 3) - mean) * rstd;
+          }
+          // n = rstd * (x - mean), or x * rinv; then the output stage
+          o[2 * q] = tail_pair<TAIL>(n0, n1, oc[q].x, oc[q].y, hc[q].x, hc[q].y);
+          o[2 * q + 1] = tail_pair<TAIL>(n2, n3, oc[q].z, oc[q].w, hc[q].z, hc[q].w);
+        }
+        if constexpr (TAIL == kTailFp8) {
+          uint32_t q8[V / 4];
+          fp8_stage<V>(o, qinv, NO_NAN, q8);
+          store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
+        } else {
+          Vec<V> ov;
+#pragma unroll
+          for (int i = 0; i < V / 2; ++i) ov.w[i] = o[i];
+          store_vec_nt<V>(static_cast<uint16_t*>(orow) + v * V, ov);
+        }
       }
+      // keep two steps' table values live at a time (the scheduler would
+      // otherwise hoist every LDS read and halve the occupancy)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // keep two steps' table values live at a time (the scheduler would
-    // otherwise hoist every LDS read and halve the occupancy)
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (TAIL == kTailFp8) {
+    // FP8: with finite statistics, finite adaLN rows and a finite 1/qscale
+    // no output can be NaN (an overflow to infinity still clamps to +-448)
+    const bool no_nan = tab_finite && __builtin_isfinite(mean) && __builtin_isfinite(rstd) &&
+                        __builtin_isfinite(qinv);
+    if (no_nan)
+      steps(std::true_type{});
+    else
+      steps(std::false_type{});
+  } else {
+    steps(std::false_type{});
   }
 }
 
