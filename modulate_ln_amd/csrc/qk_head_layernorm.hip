@@ -203,8 +203,7 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
     }
   }
   const int64_t step = (int64_t)gridDim.x * kGroupsPerBlock * HP;
-  for (int64_t h0 = ((int64_t)blockIdx.x * kGroupsPerBlock + group) * HP; h0 < a.Rq; h0 += step) {
-    Vec<V> buf[HP][NV];
+  auto load = [&](Vec<V> (*buf)[NV], int64_t h0) {
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
       const int64_t rr = h0 + i < a.Rq ? h0 + i : a.Rq - 1;
@@ -219,6 +218,8 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) buf[i][k] = load_vec_nt<V>(xr + off[k]);
     }
+  };
+  auto process = [&](const Vec<V> (*buf)[NV], int64_t h0) {
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
       float mean = 0.0f, m2 = 0.0f;
@@ -259,10 +260,24 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
         }
       }
     }
+  };
+  int64_t h0 = ((int64_t)blockIdx.x * kGroupsPerBlock + group) * HP;
+  if (h0 >= a.Rq) return;
+  // the next iteration's loads are issued as soon as this one's stores are
+  Vec<V> buf[HP][NV];
+  load(buf, h0);
+  while (true) {
+    process(buf, h0);
+    h0 += step;
+    if (h0 >= a.Rq) break;
+    load(buf, h0);
   }
 }
 
-constexpr int kHeadsBlocksPerCu = 4;
+#ifndef ADALN_QK_BLOCKS_PER_CU
+#define ADALN_QK_BLOCKS_PER_CU 4
+#endif
+constexpr int kHeadsBlocksPerCu = ADALN_QK_BLOCKS_PER_CU;
 
 template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
 int launch_heads(const QkArgs& a, hipStream_t st) {
