@@ -392,6 +392,27 @@ def test_gelu_widths(ops, orc, width):
     check_gelu(ops, orc, x, bias, "width=%d" % width)
 
 
+def test_gelu_every_bf16_value(ops, orc):
+    """All 65536 bf16 patterns as z (bias 0): finite results within one bf16 ulp of the fp64
+    oracle, and the non-finite cases as the oracle has them (NaN in, NaN out; +inf -> +inf;
+    -inf -> NaN, the eager formula's -inf * 0)."""
+    z = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = torch.from_numpy(z.view(np.int16).copy()).view(torch.bfloat16)[None].to(DEV)
+    zero = torch.zeros(x.shape[1], dtype=torch.bfloat16, device=DEV)
+    y = ops.bias_gelu_tanh(x, zero)
+    torch.cuda.synchronize()
+    want, val = orc.bias_gelu_tanh(z[None], bits(zero))
+    got = f32(bits(y)).astype(np.float64)[0]
+    ref = f32(want).astype(np.float64)[0]
+    fin = np.isfinite(ref)
+    diff = np.abs(got[fin] - ref[fin])
+    assert np.all(diff <= bf16_ulp(val[0][fin]) + 2.0 ** -133)
+    assert np.mean(got[fin] == ref[fin]) > 0.99
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    inf = np.isinf(ref)
+    assert np.array_equal(got[inf], ref[inf])
+
+
 def test_gelu_tails_and_views(ops, orc):
     z = torch.cat([torch.linspace(-15, 15, 4096), torch.tensor([0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0])])
     x = z.to(torch.bfloat16)[None].to(DEV)
