@@ -11,6 +11,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
+#include <utility>
 
 namespace adaln {
 
@@ -199,6 +201,35 @@ __device__ __forceinline__ float lane_down(float v) {
     i = (int)p[1];  // the lower half receives the upper half
   }
   return __builtin_bit_cast(float, i);
+}
+
+// Within each DPP row of 16 lanes: the value of lane (l - K), written only
+// into the lanes of the 4-lane banks set in BANKS (the others keep `old`).
+template <int K, int BANKS>
+__device__ __forceinline__ float row_shr_bank(float old, float v) {
+  static_assert(K >= 1 && K <= 15 && BANKS >= 1 && BANKS <= 15, "row_shr_bank: K in 1..15");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), 0x110 + K, 0xF,
+                                                               BANKS, false));
+}
+
+// Lane N of each DPP row of 16 lanes, broadcast to the whole row (gfx950
+// row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(N >= 0 && N <= 15, "row_bcast: N in 0..15");
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xF, 0xF, false));
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // One level of the merge tree toward lane 0: lane l merges lane l + OFF into

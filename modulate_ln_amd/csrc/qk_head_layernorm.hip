@@ -220,22 +220,49 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
     }
   };
   auto process = [&](const Vec<V> (*buf)[NV], int64_t h0) {
+    // statistics of the HP heads: after the tree toward lane 0, lane 0 of
+    // each 16-lane group holds its head's (mean, m2)
+    float mean[HP], m2[HP];
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
-      float mean = 0.0f, m2 = 0.0f;
+      mean[i] = 0.0f;
+      m2[i] = 0.0f;
       if constexpr (RMS) {
-        sumsq_lane<V>(buf[i], EQ ? (int64_t)NV * kGroup : (int64_t)nvec, l16, m2,
+        sumsq_lane<V>(buf[i], EQ ? (int64_t)NV * kGroup : (int64_t)nvec, l16, m2[i],
                       std::make_integer_sequence<int, NV>{});
-        sum_lanes<kGroup>(m2);
+        sum_down<1>(m2[i]);
+        sum_down<2>(m2[i]);
+        sum_down<4>(m2[i]);
+        sum_down<8>(m2[i]);
       } else if constexpr (EQ) {
-        welford_lane<V>(buf[i], (int64_t)NV * kGroup, l16, mean, m2, std::make_integer_sequence<int, NV>{});
-        merge_lanes16_equal(mean, m2, (float)(NV * V), lane);
+        welford_lane<V>(buf[i], (int64_t)NV * kGroup, l16, mean[i], m2[i], std::make_integer_sequence<int, NV>{});
+        const float c = (float)(NV * V);
+        merge_down_equal<1>(mean[i], m2[i], c);
+        merge_down_equal<2>(mean[i], m2[i], c);
+        merge_down_equal<4>(mean[i], m2[i], c);
+        merge_down_equal<8>(mean[i], m2[i], c);
       } else {
-        welford_lane<V>(buf[i], (int64_t)nvec, l16, mean, m2, std::make_integer_sequence<int, NV>{});
+        welford_lane<V>(buf[i], (int64_t)nvec, l16, mean[i], m2[i], std::make_integer_sequence<int, NV>{});
         float n = (float)(nv_lane * V);
-        merge_lanes<kGroup>(mean, m2, n, lane);
+        merge_down<1>(mean[i], m2[i], n);
+        merge_down<2>(mean[i], m2[i], n);
+        merge_down<4>(mean[i], m2[i], n);
+        merge_down<8>(mean[i], m2[i], n);
       }
-      const float rstd = finalize_rstd(m2, Df, a.eps, invD);
+    }
+    // one finalize for all HP heads: head i's m2 moves to lane 4i of the
+    // group (DPP row shift written to bank i only), every lane finalizes,
+    // and head i's rstd is broadcast back from lane 4i
+    float g = m2[0];
+    static_for<HP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i > 0) g = row_shr_bank<4 * i, 1 << i>(g, m2[i]);
+    });
+    const float rstd_all = finalize_rstd(g, Df, a.eps, invD);
+    static_for<HP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const float rstd = row_bcast<4 * i>(rstd_all);
+      const float mu = RMS ? 0.0f : row_bcast<0>(mean[i]);
       if (h0 + i < a.Rq) {
         uint16_t* orow = sd.out + (h0 + i) * a.Dh;
 #pragma unroll
@@ -244,8 +271,8 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
             Vec<V> o;
 #pragma unroll
             for (int j = 0; j < V / 2; ++j) {
-              float y0 = RMS ? lo_f32(buf[i][k].w[j]) * rstd : (lo_f32(buf[i][k].w[j]) - mean) * rstd;
-              float y1 = RMS ? hi_f32(buf[i][k].w[j]) * rstd : (hi_f32(buf[i][k].w[j]) - mean) * rstd;
+              float y0 = RMS ? lo_f32(buf[i][k].w[j]) * rstd : (lo_f32(buf[i][k].w[j]) - mu) * rstd;
+              float y1 = RMS ? hi_f32(buf[i][k].w[j]) * rstd : (hi_f32(buf[i][k].w[j]) - mu) * rstd;
               if constexpr (AFFINE && RMS) {
                 y0 = y0 * wf[k][2 * j];
                 y1 = y1 * wf[k][2 * j + 1];
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
           }
         }
       }
-    }
+    });
   };
   int64_t h0 = ((int64_t)blockIdx.x * kGroupsPerBlock + group) * HP;
   if (h0 >= a.Rq) return;
