@@ -233,6 +233,7 @@ def main() -> int:
     del cp_src, cp_dst
     log("copy %.1f GB/s; ln_modulate at %.1f%% of copy, %.1f%% of peak"
         % (cp_gbps, 100 * lnm_gbps / cp_gbps, 100 * lnm_gbps / PEAK_HBM_GBPS))
+    result["stream_reference"] = stream_reference(dev, stream, log)
 
     if not args.no_extra:
         result["other_workloads"] = other_workloads(m, W, dev, stream, log)
@@ -244,6 +245,41 @@ def main() -> int:
     del xs, hs, outs
     print(json.dumps(result), flush=True)
     return 0
+
+
+def stream_reference(dev, stream, log, nbytes=1 << 30):
+    """The box's streaming ceilings with torch's own kernels on 1 GiB buffers (far past the
+    MALL): write-only (fill), read-only (a float32 sum), and a copy (read + write).  Context for
+    `roofline`: HBM writes run well below the 8 TB/s peak, so a stream that writes as much as it
+    reads tops out near the copy rate."""
+    import torch
+
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+
+    def ms_per(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"bytes": nbytes}
+    for name, fn, moved in (("write_only_fill", lambda: a.fill_(2.0), nbytes),
+                            ("read_only_sum", lambda: a.sum(dtype=torch.float32), nbytes),
+                            ("copy", lambda: b.copy_(a), 2 * nbytes)):
+        ms = ms_per(fn)
+        out[name] = {"ms": round(ms, 4), "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    del a, b
+    log("stream ceilings (1 GiB, torch kernels): write-only %.0f GB/s, read-only %.0f GB/s, copy %.0f GB/s"
+        % (out["write_only_fill"]["GBps"], out["read_only_sum"]["GBps"], out["copy"]["GBps"]))
+    return out
 
 
 def time_loop(calls, n, stream, reps=20):

@@ -11,12 +11,14 @@
 // reciprocal (see gelu_tanh_f32).  Result within one bf16 ulp of the
 // correctly rounded value.
 //
-// Design: streaming.  Vector-aligned rows take a column-chunk kernel: wave w
-// of chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it
-// visits, keeps that chunk of the bias in VGPRs for the whole launch and
-// loads the next row it visits (non-temporal, unguarded) while it computes
-// the current one: the GELU costs enough ALU per byte that the loads must
-// not wait for it.
+// Design: streaming.  Vector-aligned rows take a one-shot grid: each thread
+// loads two 16-byte vectors of x (non-temporal) and the matching bias
+// vectors (cached: every row reads the same bias), computes and stores, and
+// the wave exits; the hardware dispatcher keeps the compute units full.
+// Grids too large for one launch take the column-chunk kernel: wave w of
+// chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it visits,
+// keeps that chunk of the bias in VGPRs for the whole launch and loads the
+// next row it visits while it computes the current one.
 
 #include "device_common.hpp"
 #include "host_common.hpp"
@@ -111,6 +113,34 @@ __global__ __launch_bounds__(256) void gelu_chunks(GeluArgs a) {
   }
 }
 
+// One-shot grid: block b covers vectors [c*256*U, (c+1)*256*U) of row
+// b / bpr (c = b % bpr); thread t takes vectors c*256*U + u*256 + t.  Every
+// wave reads and writes whole 1 KiB runs and exits.
+template <int V, int U>
+__global__ __launch_bounds__(256) void gelu_flat(GeluArgs a, int bpr) {
+  const int64_t row = blockIdx.x / bpr;
+  const int c = blockIdx.x - (int)row * bpr;
+  const int nvec = (int)(a.width / V);
+  const uint16_t* xr = a.x + row * a.sx_row;
+  uint16_t* orow = a.out + row * a.width;
+  Vec<V> xv[U];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    ok[u] = v < nvec;
+    if (ok[u]) xv[u] = load_vec_nt<V>(xr + v * V);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    if (ok[u]) {
+      const Vec<V> bv = load_vec<V>(a.bias + v * V);
+      store_vec_nt<V>(orow + v * V, bias_gelu_vec<V>(xv[u], bv));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void gelu_rows_scalar(GeluArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.rows;
@@ -157,8 +187,24 @@ int launch_chunks(const GeluArgs& a, hipStream_t st) {
 #define ADALN_GELU_MAX_U 4
 #endif
 
+// Vectors per thread of the one-shot grid (0: column chunks only).  The
+// one-shot grid, whose waves each read and write two 1 KiB runs and exit,
+// measured 5 % faster on MI355X than the column chunks at (16384, 12288).
+#ifndef ADALN_GELU_FLAT_U
+#define ADALN_GELU_FLAT_U 2
+#endif
+
 template <int V>
 int dispatch_chunks(const GeluArgs& a, hipStream_t st) {
+  if constexpr (ADALN_GELU_FLAT_U > 0) {
+    constexpr int U = ADALN_GELU_FLAT_U;
+    const int64_t nvec = a.width / V;
+    const int64_t bpr = (nvec + 256 * U - 1) / (256 * U);
+    if (a.rows * bpr < ((int64_t)1 << 24)) {
+      hipLaunchKernelGGL((gelu_flat<V, U>), dim3((unsigned)(a.rows * bpr)), dim3(256), 0, st, a, (int)bpr);
+      return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+    }
+  }
   const int64_t per_lane = (a.width / V + kWave - 1) / kWave;
   switch (std::min<int64_t>(per_lane, ADALN_GELU_MAX_U)) {
     case 1: return launch_chunks<V, 1>(a, st);
