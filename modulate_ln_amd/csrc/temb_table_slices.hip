@@ -9,13 +9,16 @@
 //   out[m][b, l, d] = table[m, d] + float(temb[b, l, m, d])   (one fp32 add)
 // so each slice is ready for the modulate that reads it.
 //
-// Design: streaming, column chunks.  Grid row y = (slice m, chunk c): the
-// wave keeps table[m, chunk] in fp32 VGPRs and walks the (b, l) rows.  Each
-// lane handles runs of 4 elements (8 bytes of bf16 or 16 of fp32 in, 16 bytes
-// of fp32 out), so every store instruction of a wave writes one contiguous
-// 1 KiB -- measured 1.28x faster on MI355X than 8-element runs, whose 32-byte
-// lane stores leave every instruction's lines half written.  All loads and
-// stores are non-temporal.
+// Design: streaming.  A one-shot grid whose blocks are ordered (slice, row,
+// column block), so the output -- two thirds of the traffic -- is written in
+// address order by short-lived waves (measured 12 % faster on MI355X than
+// column-chunk waves that walk the rows, which remain for grids too large
+// for one launch).  Each lane handles runs of 4 elements (8 bytes of bf16 or
+// 16 of fp32 in, 16 bytes of fp32 out), so every store instruction of a wave
+// writes one contiguous 1 KiB -- measured 1.28x faster than 8-element runs,
+// whose 32-byte lane stores leave every instruction's lines half written.
+// temb is read and the output written non-temporally; the table, which every
+// row reads, through the caches.
 #include "device_common.hpp"
 #include "host_common.hpp"
 
@@ -128,6 +131,46 @@ __global__ __launch_bounds__(256) void temb_chunks(TembArgs a, int nchunks) {
   }
 }
 
+// One-shot grid: block b covers vectors [c*256*U, (c+1)*256*U) of row r of
+// slice m, with b = (m * R + r) * bpr + c, so blocks write each slice in
+// address order; thread t takes vectors c*256*U + u*256 + t.
+template <typename T, int V, int U>
+__global__ __launch_bounds__(256) void temb_flat(TembArgs a, int bpr) {
+  const uint32_t rc = blockIdx.x;
+  const uint32_t q = rc / (uint32_t)bpr;  // m * R + r
+  const int c = (int)(rc - q * (uint32_t)bpr);
+  const int64_t m = q / (uint32_t)a.R;
+  const int64_t r = q - m * a.R;
+  const int64_t b = r / a.L;
+  const int64_t l = r - b * a.L;
+  const int nvec = (int)(a.D / V);
+  const T* er = static_cast<const T*>(a.temb) + b * a.se_b + l * a.se_l + m * a.se_m;
+  const float* tr = a.table + m * a.st_m;
+  float* orow = a.out + (m * a.R + r) * a.D;
+  float e[U][V];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    ok[u] = v < nvec;
+    if (ok[u]) loadv<V>(er + v * V, e[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    if (ok[u]) {
+      float s[V];
+#pragma unroll
+      for (int q4 = 0; q4 < V / 4; ++q4) {
+        const f32x4 t = *(reinterpret_cast<const f32x4*>(tr + v * V) + q4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * q4 + i] = t[i] + e[u][4 * q4 + i];  // table + float(temb)
+      }
+      storev<V>(orow + v * V, s);
+    }
+  }
+}
+
 // any D, any alignment: one element per lane step
 template <typename T>
 __global__ __launch_bounds__(256) void temb_scalar(TembArgs a) {
@@ -182,8 +225,29 @@ int launch_temb(const TembArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+template <typename T, int U>
+int launch_temb_flat(const TembArgs& a, hipStream_t st) {
+  constexpr int V = ADALN_TEMB_V;
+  const int64_t bpr = (a.D / V + 256 * U - 1) / (256 * U);
+  hipLaunchKernelGGL((temb_flat<T, V, U>), dim3((unsigned)(a.nmod * a.R * bpr)), dim3(256), 0, st, a, (int)bpr);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
 template <typename T>
 int dispatch_temb(const TembArgs& a, hipStream_t st) {
+  // one-shot grid (measured 12 % faster than the column chunks at (1,109120,6,3072)): a
+  // block takes a whole row of up to 1024 vectors, longer rows go in 256-vector blocks
+  const int64_t nvec = a.D / ADALN_TEMB_V;
+  const int64_t per_thread = nvec <= 1024 ? (nvec + 255) / 256 : 1;
+  const int64_t bpr = (nvec + 256 * per_thread - 1) / (256 * per_thread);
+  if (a.nmod * a.R * bpr < ((int64_t)1 << 24)) {
+    switch (per_thread) {
+      case 1: return launch_temb_flat<T, 1>(a, st);
+      case 2: return launch_temb_flat<T, 2>(a, st);
+      case 3: return launch_temb_flat<T, 3>(a, st);
+      default: return launch_temb_flat<T, 4>(a, st);
+    }
+  }
   const int64_t per_lane = (a.D / ADALN_TEMB_V + kWave - 1) / kWave;
   switch (std::min<int64_t>(per_lane, ADALN_TEMB_MAX_U)) {
     case 1: return launch_temb<T, 1>(a, st);
