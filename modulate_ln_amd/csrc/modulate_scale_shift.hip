@@ -7,13 +7,16 @@
 // y = bf16(x * one_plus), out = bf16(y + shift) -- the tail of ln_modulate
 // with x in place of the normalized row.
 //
-// Design: pure streaming, the column-chunk layout of residual_gate_add.  Wave
-// w of chunk c owns vectors c*64*U + lane + 64*u (u < U) of every row it
-// visits, the next row's loads in flight while the current row is computed.
-// With one adaLN row per sample, the wave keeps bf16(1 + scale) and shift of
-// its chunk in fp32 VGPRs while it stays in a sample (1 read + 1 write per
-// element); with one row per token it streams the scale and shift rows too
-// (3 reads + 1 write).  Loads and stores are non-temporal.
+// Design: pure streaming.  Per-token rows (3 reads + 1 write per element) and
+// large per-sample problems take a one-shot grid: each thread loads two
+// vectors of x (and of the per-token scale and shift rows), computes, stores
+// and exits, so the output is written in address order.  Smaller per-sample
+// problems take the column-chunk layout of residual_gate_add: wave w of chunk
+// c owns vectors c*64*U + lane + 64*u (u < U) of every row it visits, the
+// next row's loads in flight while the current row is computed, and keeps
+// bf16(1 + scale) and shift of its chunk in fp32 VGPRs while it stays in a
+// sample (1 read + 1 write per element).  Streams are non-temporal; the
+// per-sample rows come through the caches.
 #include "device_common.hpp"
 #include "host_common.hpp"
 
@@ -144,6 +147,48 @@ __global__ __launch_bounds__(256) void mod_chunks(ModArgs a) {
 }
 
 // any D, any 2-byte alignment: one element per lane step
+// One-shot grid: block b covers vectors [c*256*U, (c+1)*256*U) of row
+// b / bpr (c = b % bpr); thread t takes vectors c*256*U + u*256 + t.  The
+// per-sample adaLN rows come through the caches; per-token rows stream.
+template <int V, int U, bool PER_TOKEN>
+__global__ __launch_bounds__(256) void mod_flat(ModArgs a, int bpr) {
+  const int64_t r = blockIdx.x / bpr;
+  const int c = blockIdx.x - (int)r * bpr;
+  const int64_t b = r / a.S;
+  const int64_t s = r - b * a.S;
+  const int nvec = (int)(a.D / V);
+  const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
+  const uint16_t* scr = a.scale + b * a.ssc_b + (PER_TOKEN ? s * a.ssc_s : 0);
+  const uint16_t* shr = a.shift + b * a.ssh_b + (PER_TOKEN ? s * a.ssh_s : 0);
+  uint16_t* orow = a.out + r * a.D;
+  Vec<V> xv[U], sv[U], hv[U];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    ok[u] = v < nvec;
+    if (ok[u]) {
+      xv[u] = load_vec_nt<V>(xr + v * V);
+      if constexpr (PER_TOKEN) {
+        sv[u] = load_vec_nt<V>(scr + v * V);
+        hv[u] = load_vec_nt<V>(shr + v * V);
+      } else {
+        sv[u] = load_vec<V>(scr + v * V);
+        hv[u] = load_vec<V>(shr + v * V);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    if (ok[u]) {
+      float o[V], h[V];
+      mod_rows<V>(sv[u], hv[u], o, h);
+      store_vec_nt<V>(orow + v * V, mod_vec<V>(xv[u], o, h));
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void mod_rows_scalar(ModArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
@@ -200,8 +245,28 @@ int launch_mod(const ModArgs& a, hipStream_t st) {
 
 // vectors per lane in one chunk: as many as a row needs, at most
 // ADALN_MOD_MAX_U (the per-sample rows stay in VGPRs as fp32: 2*U*V registers)
+// The one-shot grid (two vectors per thread) measured faster on MI355X
+// with per-token rows -- (1,4096,4096) 25.0 -> 23.4 us -- and with per-sample
+// rows from 2^25 elements on -- (4,4096,3072) 38.4 -> 36.3 us -- but slower
+// for smaller per-sample problems ((1,4096,4096) 12.7 -> 14.8 us), where the
+// column chunks stay.
+#ifndef ADALN_MOD_FLAT_U
+#define ADALN_MOD_FLAT_U 2
+#endif
+#ifndef ADALN_MOD_FLAT_MIN_ELEMS
+#define ADALN_MOD_FLAT_MIN_ELEMS ((int64_t)1 << 25)
+#endif
+
 template <int V, bool PER_TOKEN>
 int dispatch_mod(const ModArgs& a, hipStream_t st) {
+  if constexpr (ADALN_MOD_FLAT_U > 0) {
+    constexpr int U = ADALN_MOD_FLAT_U;
+    const int64_t bpr = (a.D / V + 256 * U - 1) / (256 * U);
+    if ((PER_TOKEN || a.R * a.D >= ADALN_MOD_FLAT_MIN_ELEMS) && a.R * bpr < ((int64_t)1 << 24)) {
+      hipLaunchKernelGGL((mod_flat<V, U, PER_TOKEN>), dim3((unsigned)(a.R * bpr)), dim3(256), 0, st, a, (int)bpr);
+      return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+    }
+  }
   const int64_t per_lane = (a.D / V + kWave - 1) / kWave;
   switch (std::min<int64_t>(per_lane, ADALN_MOD_MAX_U)) {
     case 1: return launch_mod<V, 1, PER_TOKEN>(a, st);

@@ -55,6 +55,15 @@ def test_modulate_glm_square_shape(ops, orc):
     run_mod(ops, orc, t["x"], sc, sh, what="(1,4096,4096) per token")
 
 
+def test_modulate_large_per_sample(ops, orc):
+    """(2,4096,4096) = 2^25 elements: the one-shot grid with per-sample rows."""
+    g = torch.Generator().manual_seed(52)
+    x = rand_bf16((2, 4096, 4096), g).to(DEV)
+    sc = rand_bf16((2, 4096), g, std=0.1).to(DEV)
+    sh = rand_bf16((2, 4096), g, std=0.1).to(DEV)
+    run_mod(ops, orc, x, sc, sh, what="(2,4096,4096) per sample")
+
+
 @pytest.mark.parametrize("D", [1, 3, 4, 8, 520, 2240, 4096, 4100, 12288])
 @pytest.mark.parametrize("per_token", [False, True])
 def test_modulate_hidden_sizes(ops, orc, D, per_token):
