@@ -58,11 +58,20 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+// Round one fp32 value to bf16 and keep it in fp32 format: converting the
+// pair (0, v) puts bf16(v) in the high half-word over a zero low half-word,
+// which is the widened value itself (one v_cvt_pk_bf16_f32 with an inline
+// zero, where packing two values and splitting them again takes three ops).
+__device__ __forceinline__ float round_f32(float v) {
+  f32x2 f = {0.0f, v};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(float, h);
+}
+
 // Round a pair to bf16 and widen back: the values the eager chain stores.
 __device__ __forceinline__ void round_pair(float& a, float& b) {
-  uint32_t w = pack_bf16(a, b);
-  a = lo_f32(w);
-  b = hi_f32(w);
+  a = round_f32(a);
+  b = round_f32(b);
 }
 
 // ---------------------------------------------------------------------------

@@ -211,26 +211,39 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // A block serves one batch sample b.  It first turns that sample's adaLN
 // rows into two fp32 tables in LDS -- bf16(1 + scale) and shift -- laid out
 // [quarter q][vector v][4] so a lane's 16-byte LDS reads are contiguous
-// across the wave.  Each wave then streams rows s = j*4 + wave, += 4*bpb:
-// the next row's loads are in flight while the current row is reduced,
-// normalized, modulated and stored (non-temporal: every byte is touched
-// once).  The first row's loads are issued before the table is built, so
+// across the wave.  Each wave then streams rows s = j*4 + wave, += 4*bpb
+// (with the prefetch, the next row's loads are in flight while the current
+// row is reduced, normalized, modulated and stored; non-temporal: every
+// byte is touched once).  The first row's loads are issued before the table is built, so
 // the table's latency hides under them.  UNIF (D % (64*V) == 0): every lane
 // holds the same count and the merge tree needs no division.
 // ---------------------------------------------------------------------------
 // Launch shape of the fast path, measured on MI355X (all variants give the
-// same bits).  Rows of 7-8 vectors per lane prefetch the next row into a
-// second buffer.  The bf16 stages re-widen x from bf16 when normalizing, to
-// stay at three waves per SIMD; the FP8 stage, whose extra VALU work per
-// row makes a row's compute the critical path, keeps an fp32 copy of x at
-// two waves per SIMD.  Shorter rows keep one buffer and an fp32 copy of x;
-// longer rows (up to 16 vectors per lane, 64 KiB of tables) keep one buffer
-// and re-widen.  Grid: blocks per compute unit in total.
+// same bits), for rows of 7-8 vectors per lane, per output stage:
+//   PF    prefetch the next row into a second buffer (the wave walks rows);
+//         without it a wave holds one row and the grid covers every row
+//   BPC   blocks per compute unit in total
+//   XF32  keep an fp32 copy of x for the normalize pass rather than
+//         re-widening it from bf16 (one VALU op per element)
+// The LayerNorm chain and RMSNorm run best with every row in flight at
+// once, one row per wave and four waves per SIMD, with the fp32 copy (109
+// VGPRs): their VALU work per row is what the last waves to get their data
+// wait on, and a prefetched second row costs the fp32 copy (two waves per
+// SIMD would remain).  The FP8 stage keeps the prefetch at two blocks per
+// compute unit; the fold is indifferent.  Shorter rows keep one buffer and an fp32 copy of x; longer rows
+// (up to 16 vectors per lane, 64 KiB of tables) keep one buffer and
+// re-widen.
+#ifndef ADALN_TAB_PF_LN
+#define ADALN_TAB_PF_LN 0
+#endif
 #ifndef ADALN_TAB_BPC_LN
-#define ADALN_TAB_BPC_LN 3
+#define ADALN_TAB_BPC_LN 4
 #endif
 #ifndef ADALN_TAB_XF32_LN
-#define ADALN_TAB_XF32_LN 0
+#define ADALN_TAB_XF32_LN 1
+#endif
+#ifndef ADALN_TAB_PF_FOLD
+#define ADALN_TAB_PF_FOLD 1
 #endif
 #ifndef ADALN_TAB_BPC_FOLD
 #define ADALN_TAB_BPC_FOLD 3
@@ -238,11 +251,17 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #ifndef ADALN_TAB_XF32_FOLD
 #define ADALN_TAB_XF32_FOLD 0
 #endif
+#ifndef ADALN_TAB_PF_RMS
+#define ADALN_TAB_PF_RMS 0
+#endif
 #ifndef ADALN_TAB_BPC_RMS
-#define ADALN_TAB_BPC_RMS 3
+#define ADALN_TAB_BPC_RMS 4
 #endif
 #ifndef ADALN_TAB_XF32_RMS
-#define ADALN_TAB_XF32_RMS 0
+#define ADALN_TAB_XF32_RMS 1
+#endif
+#ifndef ADALN_TAB_PF_FP8
+#define ADALN_TAB_PF_FP8 1
 #endif
 #ifndef ADALN_TAB_BPC_FP8
 #define ADALN_TAB_BPC_FP8 2
@@ -261,7 +280,11 @@ struct TabShape {
                                     : TAIL == kTailFold ? ADALN_TAB_XF32_FOLD
                                     : RMS               ? ADALN_TAB_XF32_RMS
                                                         : ADALN_TAB_XF32_LN;
-  static constexpr bool kPrefetch = kLong;
+  static constexpr bool kPfLong = TAIL == kTailFp8    ? ADALN_TAB_PF_FP8
+                                  : TAIL == kTailFold ? ADALN_TAB_PF_FOLD
+                                  : RMS               ? ADALN_TAB_PF_RMS
+                                                      : ADALN_TAB_PF_LN;
+  static constexpr bool kPrefetch = kLong && kPfLong;
   static constexpr bool kXf32 = NV <= 6 || (kLong && kXf32Long);
   static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (kLong ? kBpcLong : 2);
 };
