@@ -380,6 +380,13 @@ __device__ __forceinline__ float pow2_inverse(int64_t D) {
   return (D > 0 && (D & (D - 1)) == 0) ? __builtin_ldexpf(1.0f, -__builtin_ctzll((uint64_t)D)) : 0.0f;
 }
 
+// The same for a row length given as a float (an integer below 2^24): 1/D
+// when D is a power of two, else 0.
+__device__ __forceinline__ float pow2_inverse_f(float D) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, D);
+  return (D >= 1.0f && (b & 0x7fffffu) == 0) ? __builtin_bit_cast(float, (254u - (b >> 23)) << 23) : 0.0f;
+}
+
 // var = m2/D, rstd = 1/sqrt(var + eps): IEEE division and square root.
 // (With m2 the sum of squares this is RMSNorm's 1/sqrt(mean(x^2) + eps).)
 // invD: pow2_inverse(D), a wave-uniform value; non-zero selects the exact

@@ -233,6 +233,12 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // compute unit; the fold is indifferent.  Shorter rows keep one buffer and an fp32 copy of x; longer rows
 // (up to 16 vectors per lane, 64 KiB of tables) keep one buffer and
 // re-widen.
+#ifndef ADALN_TAB_PF_SHORT
+#define ADALN_TAB_PF_SHORT 0
+#endif
+#ifndef ADALN_TAB_BPC_SHORT
+#define ADALN_TAB_BPC_SHORT 5
+#endif
 #ifndef ADALN_TAB_PF_LN
 #define ADALN_TAB_PF_LN 0
 #endif
@@ -284,9 +290,9 @@ struct TabShape {
                                   : TAIL == kTailFold ? ADALN_TAB_PF_FOLD
                                   : RMS               ? ADALN_TAB_PF_RMS
                                                       : ADALN_TAB_PF_LN;
-  static constexpr bool kPrefetch = kLong && kPfLong;
+  static constexpr bool kPrefetch = kLong ? kPfLong : (NV <= 6 && ADALN_TAB_PF_SHORT);
   static constexpr bool kXf32 = NV <= 6 || (kLong && kXf32Long);
-  static constexpr int kBlocksPerCu = NV <= 6 ? 4 : (kLong ? kBpcLong : 2);
+  static constexpr int kBlocksPerCu = NV <= 6 ? ADALN_TAB_BPC_SHORT : (kLong ? kBpcLong : 2);
 };
 
 

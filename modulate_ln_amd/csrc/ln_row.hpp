@@ -166,7 +166,7 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
   }
   if constexpr (!RMS) mean = bcast_lane0(mean);
   m2 = bcast_lane0(m2);
-  const float rstd = finalize_rstd(m2, Df, eps);
+  const float rstd = finalize_rstd(m2, Df, eps, pow2_inverse_f(Df));
   if (lane == 0) {
     if (!RMS && mean_out) *mean_out = mean;
     if (rstd_out) *rstd_out = rstd;

@@ -58,12 +58,21 @@ struct FusedArgs {
 // Launch shape, measured on MI355X (every choice gives the same bits).
 // Rows of up to 6 vectors per lane prefetch the next row's residual and
 // update into a second pair of buffers; longer rows do not (the VGPRs would
-// cut the waves per SIMD).  Blocks per compute unit: 4, or as many as the
+// cut the waves per SIMD).  Rows of up to 8 vectors per lane keep an fp32
+// copy of the updated residual for the normalize pass instead of
+// re-widening it (24.7 vs 25.0 us at (1,4096,4096); even at (4,4096,3072));
+// longer rows re-widen.  Blocks per compute unit: 4, or as many as the
 // three tables (12*D bytes of LDS per block) allow.
+#ifndef ADALN_FUSED_XF32_MAX
+#define ADALN_FUSED_XF32_MAX 8
+#endif
+#ifndef ADALN_FUSED_PF_MAX
+#define ADALN_FUSED_PF_MAX 6
+#endif
 template <int NV>
 struct FusedShape {
-  static constexpr bool kPrefetch = NV <= 6;
-  static constexpr bool kXf32 = NV <= 4;
+  static constexpr bool kPrefetch = NV <= ADALN_FUSED_PF_MAX;
+  static constexpr bool kXf32 = NV <= ADALN_FUSED_XF32_MAX;
   static constexpr int kBlocksPerCu = 4;
 };
 
