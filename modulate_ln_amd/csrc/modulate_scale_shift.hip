@@ -7,8 +7,13 @@
 // y = bf16(x * one_plus), out = bf16(y + shift) -- the tail of ln_modulate
 // with x in place of the normalized row.
 //
-// Design: pure streaming.  Per-token rows (3 reads + 1 write per element) and
-// large per-sample problems take a one-shot grid: each thread loads two
+// Design: pure streaming.  Per-sample rows of up to 4096 elements take the
+// row-per-wave layout of ln_modulate: a block serves one sample, turns its
+// bf16(1 + scale) and shift into fp32 tables in LDS behind its waves' first
+// row loads, and each wave holds one whole row (every row of the launch in
+// flight at once when the grid covers them).  Per-token rows (3 reads + 1
+// write per element) and other large per-sample problems take a one-shot
+// grid: each thread loads two
 // vectors of x (and of the per-token scale and shift rows), computes, stores
 // and exits, so the output is written in address order.  Smaller per-sample
 // problems take the column-chunk layout of residual_gate_add: wave w of chunk
@@ -19,6 +24,7 @@
 // per-sample rows come through the caches.
 #include "device_common.hpp"
 #include "host_common.hpp"
+#include "ln_row.hpp"  // build_tables: the per-sample fp32 tables of the norm kernels
 
 namespace adaln {
 namespace {
@@ -189,6 +195,65 @@ __global__ __launch_bounds__(256) void mod_flat(ModArgs a, int bpr) {
   }
 }
 
+// Per-sample rows, one row per wave: block j of sample b builds the tables
+// (bf16(1 + scale), shift; [quarter][vector] float4 in LDS) and its wave w
+// takes rows s = 4j + w, += 4*bpb, NV 16-byte vectors per lane (lane l owns
+// vectors l, l + 64, ...).  UNIF: nvec % 64 == 0.
+template <int NV, bool UNIF>
+__global__ __launch_bounds__(256) void mod_tab(ModArgs a, int bpb) {
+  constexpr int V = 8;
+  extern __shared__ float4 tab[];  // [2][V/4][nvec] float4: bf16(1+scale), then shift
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nvec = (int)(a.D / V);
+  const int S = (int)a.S;
+  const int b = blockIdx.x / bpb;
+  const int j = blockIdx.x - b * bpb;
+  const int row_step = 4 * bpb;
+  const int shift_off = (V / 4) * nvec;
+  int s = 4 * j + wave;
+  const uint16_t* xb = a.x + (int64_t)b * a.sx_b;
+  Vec<V> xv[NV];
+  auto load_row = [&](int ss) {
+    const uint16_t* xr = xb + (int64_t)ss * a.sx_s;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * kWave + lane;
+      xv[k] = load_vec_nt<V>(xr + ((UNIF || v < nvec) ? v : nvec - 1) * V);
+    }
+  };
+  if (s < S) load_row(s);
+  build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec, threadIdx.x, 256);
+  __syncthreads();
+  if (s >= S) return;
+  while (true) {
+    uint16_t* orow = a.out + ((int64_t)b * S + s) * a.D;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * kWave + lane;
+      if (UNIF || v < nvec) {
+        Vec<V> ov;
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          const float4 o = tab[q * nvec + v];
+          const float4 h = tab[shift_off + q * nvec + v];
+          const uint32_t w0 = xv[k].w[2 * q], w1 = xv[k].w[2 * q + 1];
+          float y0 = lo_f32(w0) * o.x, y1 = hi_f32(w0) * o.y;
+          float y2 = lo_f32(w1) * o.z, y3 = hi_f32(w1) * o.w;
+          round_pair(y0, y1);  // bf16(x * one_plus)
+          round_pair(y2, y3);
+          ov.w[2 * q] = pack_bf16(y0 + h.x, y1 + h.y);  // bf16(y + shift)
+          ov.w[2 * q + 1] = pack_bf16(y2 + h.z, y3 + h.w);
+        }
+        store_vec_nt<V>(orow + v * V, ov);
+      }
+    }
+    s += row_step;
+    if (s >= S) break;
+    load_row(s);
+  }
+}
+
 __global__ __launch_bounds__(256) void mod_rows_scalar(ModArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
@@ -249,7 +314,8 @@ int launch_mod(const ModArgs& a, hipStream_t st) {
 // with per-token rows -- (1,4096,4096) 25.0 -> 23.4 us -- and with per-sample
 // rows from 2^25 elements on -- (4,4096,3072) 38.4 -> 36.3 us -- but slower
 // for smaller per-sample problems ((1,4096,4096) 12.7 -> 14.8 us), where the
-// column chunks stay.
+// column chunks stay.  Per-sample rows of up to 4096 elements take the
+// row-per-wave kernel ahead of both; the others stay here.
 #ifndef ADALN_MOD_FLAT_U
 #define ADALN_MOD_FLAT_U 2
 #endif
@@ -257,8 +323,66 @@ int launch_mod(const ModArgs& a, hipStream_t st) {
 #define ADALN_MOD_FLAT_MIN_ELEMS ((int64_t)1 << 25)
 #endif
 
+// Row-per-wave layout for per-sample rows of up to kModTabMaxNv vectors per
+// lane (all sizes: ALL), blocks per compute unit in total, measured on
+// MI355X against the chunk and one-shot kernels: (1,4096,4096) 12.3 us (3
+// per CU; 14.7 at 4) vs 12.55; (4,4096,3072) 35.2 vs 36.2; (4,4096,4096)
+// 46.1 (4 per CU; 47.7 at 3) vs 49.5; (2,1024,2240) 5.1 vs 6.6.
+#ifndef ADALN_MOD_TAB
+#define ADALN_MOD_TAB 1
+#endif
+#ifndef ADALN_MOD_TAB_BPC
+#define ADALN_MOD_TAB_BPC 4
+#endif
+#ifndef ADALN_MOD_TAB_BPC_LONG
+#define ADALN_MOD_TAB_BPC_LONG 3
+#endif
+#ifndef ADALN_MOD_TAB_ALL
+#define ADALN_MOD_TAB_ALL 1
+#endif
+constexpr int kModTabMaxNv = 8;  // D <= 4096: 32 KiB of LDS tables per block
+
+template <int NV, bool UNIF>
+int launch_mod_tab(const ModArgs& a, hipStream_t st) {
+  const int64_t B = a.R / a.S;
+  const int cus = cu_count();
+  const int64_t ncu = cus > 0 ? cus : 256;
+  // Long rows: when the grid would hold every row at once (one row per
+  // wave), every store waits for the end of the read phase; one block per
+  // CU fewer leaves a third of the waves a second row
+  const bool one_row_each = a.R <= (int64_t)ADALN_MOD_TAB_BPC * 4 * ncu;
+  const int64_t target = (int64_t)(NV >= 7 && one_row_each ? ADALN_MOD_TAB_BPC_LONG : ADALN_MOD_TAB_BPC) * ncu;
+  int64_t bpb = (target + B - 1) / B;
+  bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
+  const size_t lds = (size_t)2 * a.D * sizeof(float);
+  hipLaunchKernelGGL((mod_tab<NV, UNIF>), dim3((unsigned)(B * bpb)), dim3(256), lds, st, a, (int)bpb);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+template <bool UNIF>
+int dispatch_mod_tab(const ModArgs& a, int nv, hipStream_t st) {
+  switch (nv) {
+    case 1: return launch_mod_tab<1, UNIF>(a, st);
+    case 2: return launch_mod_tab<2, UNIF>(a, st);
+    case 3: return launch_mod_tab<3, UNIF>(a, st);
+    case 4: return launch_mod_tab<4, UNIF>(a, st);
+    case 5: return launch_mod_tab<5, UNIF>(a, st);
+    case 6: return launch_mod_tab<6, UNIF>(a, st);
+    case 7: return launch_mod_tab<7, UNIF>(a, st);
+    default: return launch_mod_tab<8, UNIF>(a, st);
+  }
+}
+
 template <int V, bool PER_TOKEN>
 int dispatch_mod(const ModArgs& a, hipStream_t st) {
+  if constexpr (V == 8 && !PER_TOKEN && ADALN_MOD_TAB) {
+    const int64_t nvec = a.D / V;
+    const int64_t nv = (nvec + kWave - 1) / kWave;
+    // the grid is B * bpb blocks with bpb <= S/4: sizes that fit an int index
+    if (nv <= kModTabMaxNv && a.S < ((int64_t)1 << 30) && a.R / a.S < ((int64_t)1 << 20) &&
+        (ADALN_MOD_TAB_ALL || a.R * a.D < ADALN_MOD_FLAT_MIN_ELEMS))
+      return nvec % kWave == 0 ? dispatch_mod_tab<true>(a, (int)nv, st) : dispatch_mod_tab<false>(a, (int)nv, st);
+  }
   if constexpr (ADALN_MOD_FLAT_U > 0) {
     constexpr int U = ADALN_MOD_FLAT_U;
     const int64_t bpr = (a.D / V + 256 * U - 1) / (256 * U);
