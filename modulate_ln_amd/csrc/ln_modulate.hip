@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // A block serves one batch sample b.  It first turns that sample's adaLN
 // rows into two fp32 tables in LDS -- bf16(1 + scale) and shift -- laid out
 // [quarter q][vector v][4] so a lane's 16-byte LDS reads are contiguous
-// across the wave.  Each wave then streams rows s = j*4 + wave, += 4*bpb
+// across the wave.  Each of its W waves then streams rows s = j*W + wave, += W*bpb
 // (with the prefetch, the next row's loads are in flight while the current
 // row is reduced, normalized, modulated and stored; non-temporal: every
 // byte is touched once).  The first row's loads are issued before the table is built, so
@@ -233,6 +233,12 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // compute unit; the fold is indifferent.  Shorter rows keep one buffer and an fp32 copy of x; longer rows
 // (up to 16 vectors per lane, 64 KiB of tables) keep one buffer and
 // re-widen.
+#ifndef ADALN_TAB_WPB_LN
+#define ADALN_TAB_WPB_LN 16
+#endif
+#ifndef ADALN_TAB_WPB_RMS
+#define ADALN_TAB_WPB_RMS 4
+#endif
 #ifndef ADALN_TAB_PF_SHORT
 #define ADALN_TAB_PF_SHORT 0
 #endif
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #ifndef ADALN_TAB_XF32_FP8
 #define ADALN_TAB_XF32_FP8 1
 #endif
-template <int NV, bool RMS, int TAIL>
+template <int NV, bool UNIF, bool RMS, int TAIL>
 struct TabShape {
   static constexpr bool kLong = NV == 7 || NV == 8;
   static constexpr int kBpcLong = TAIL == kTailFp8    ? ADALN_TAB_BPC_FP8
@@ -292,14 +298,26 @@ struct TabShape {
                                                       : ADALN_TAB_PF_LN;
   static constexpr bool kPrefetch = kLong ? kPfLong : (NV <= 6 && ADALN_TAB_PF_SHORT);
   static constexpr bool kXf32 = NV <= 6 || (kLong && kXf32Long);
-  static constexpr int kBlocksPerCu = NV <= 6 ? ADALN_TAB_BPC_SHORT : (kLong ? kBpcLong : 2);
+  // waves per block: one row per wave and every row in flight lets one
+  // block per compute unit hold all its waves, so the tables are built once
+  // per compute unit rather than once per four rows.  Rows with a partial
+  // last vector step need more than the 128 VGPRs a 16-wave block allows
+  // (they would spill), so they keep 4-wave blocks.
+  // Measured: the LayerNorm chain 11.57 us at 16 waves per block, 11.79 at
+  // 8, 12.12 at 4 ((1,4096,4096)); RMSNorm, whose statistic is a quarter of
+  // the Welford work per element, 11.04 at 4, 11.45 at 16.
+  static constexpr int kWpbLong = (TAIL == kTailChain && !RMS) ? ADALN_TAB_WPB_LN : RMS ? ADALN_TAB_WPB_RMS : 4;
+  static constexpr int kWpb = (kLong && !kPrefetch && UNIF) ? kWpbLong : 4;
+  static constexpr int kBlocksPerCu =
+      NV <= 6 ? ADALN_TAB_BPC_SHORT : (kLong ? (kBpcLong * 4 + kWpb - 1) / kWpb : 2);
 };
 
 
 template <int V, int NV, bool UNIF, bool RMS, int TAIL>
-__global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
-  constexpr bool kPrefetch = TabShape<NV, RMS, TAIL>::kPrefetch;
-  constexpr bool kXf32 = TabShape<NV, RMS, TAIL>::kXf32;
+__global__ __launch_bounds__((TabShape<NV, UNIF, RMS, TAIL>::kWpb * 64)) void ln_modulate_tab(LnArgs a, int bpb) {
+  constexpr int kWpb = TabShape<NV, UNIF, RMS, TAIL>::kWpb;
+  constexpr bool kPrefetch = TabShape<NV, UNIF, RMS, TAIL>::kPrefetch;
+  constexpr bool kXf32 = TabShape<NV, UNIF, RMS, TAIL>::kXf32;
   extern __shared__ float4 tab[];  // [2][V/4][nvec] float4: bf16(1+scale), then shift
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -308,8 +326,8 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   const int S = (int)a.S;
   const int b = blockIdx.x / bpb;
   const int j = blockIdx.x - b * bpb;
-  const int row_step = 4 * bpb;
-  int s = 4 * j + wave;
+  const int row_step = kWpb * bpb;
+  int s = kWpb * j + wave;
 
   const uint16_t* xb = a.x + (int64_t)b * a.sx_b;
   auto load_row = [&](Vec<V>* buf, int ss) {
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(256) void ln_modulate_tab(LnArgs a, int bpb) {
   Vec<V> bufB[kPrefetch ? NV : 1];
   if (s < S) load_row(bufA, s);
   const bool fin = build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,
-                                   threadIdx.x, 256);
+                                   threadIdx.x, kWpb * kWave);
   bool tab_finite = true;
   if constexpr (TAIL == kTailFp8)
     tab_finite = __syncthreads_and(fin);
@@ -552,15 +570,16 @@ constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
 
 template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 int launch_tab(const LnArgs& a, hipStream_t st) {
-  // TabShape<NV, RMS, TAIL>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
+  // TabShape<NV, UNIF, RMS, TAIL>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
   const int64_t B = a.R / a.S;
   const int cus = cu_count();
-  const int64_t target = (int64_t)TabShape<NV, RMS, TAIL>::kBlocksPerCu * (cus > 0 ? cus : 256);
+  const int64_t target = (int64_t)TabShape<NV, UNIF, RMS, TAIL>::kBlocksPerCu * (cus > 0 ? cus : 256);
   int64_t bpb = (target + B - 1) / B;
-  bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
+  constexpr int kWpb = TabShape<NV, UNIF, RMS, TAIL>::kWpb;
+  bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + kWpb - 1) / kWpb));
   const int64_t blocks = B * bpb;
   const size_t lds = (size_t)2 * a.D * sizeof(float);
-  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS, TAIL>), dim3((unsigned)blocks), dim3(256), lds, st, a,
+  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS, TAIL>), dim3((unsigned)blocks), dim3(kWpb * kWave), lds, st, a,
                      (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
