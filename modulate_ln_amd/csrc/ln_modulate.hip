@@ -236,6 +236,9 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #ifndef ADALN_TAB_WPB_LN
 #define ADALN_TAB_WPB_LN 16
 #endif
+#ifndef ADALN_TAB_WPB_FOLD
+#define ADALN_TAB_WPB_FOLD 4
+#endif
 #ifndef ADALN_TAB_WPB_RMS
 #define ADALN_TAB_WPB_RMS 4
 #endif
@@ -305,8 +308,12 @@ struct TabShape {
   // (they would spill), so they keep 4-wave blocks.
   // Measured: the LayerNorm chain 11.57 us at 16 waves per block, 11.79 at
   // 8, 12.12 at 4 ((1,4096,4096)); RMSNorm, whose statistic is a quarter of
-  // the Welford work per element, 11.04 at 4, 11.45 at 16.
-  static constexpr int kWpbLong = (TAIL == kTailChain && !RMS) ? ADALN_TAB_WPB_LN : RMS ? ADALN_TAB_WPB_RMS : 4;
+  // the Welford work per element, 11.04 at 4, 11.45 at 16.  The fold keeps
+  // its prefetch (11.32 us; 11.66 with one row per wave in 16-wave blocks).
+  static constexpr int kWpbLong = TAIL == kTailFold   ? ADALN_TAB_WPB_FOLD
+                                  : TAIL == kTailFp8  ? 4
+                                  : RMS               ? ADALN_TAB_WPB_RMS
+                                                      : ADALN_TAB_WPB_LN;
   static constexpr int kWpb = (kLong && !kPrefetch && UNIF) ? kWpbLong : 4;
   static constexpr int kBlocksPerCu =
       NV <= 6 ? ADALN_TAB_BPC_SHORT : (kLong ? (kBpcLong * 4 + kWpb - 1) / kWpb : 2);

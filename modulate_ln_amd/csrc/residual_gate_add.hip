@@ -6,8 +6,9 @@
 // eager chain is two bf16 ops (a multiply, then an add), so the product is
 // rounded to bf16 before the add.
 //
-// Design: pure streaming (2 reads + 1 write per element).  Vector-aligned
-// rows take the column-chunk kernel: wave w of chunk c owns vectors
+// Design: pure streaming (2 reads + 1 write per element).  Large
+// vector-aligned problems take a one-shot grid (each thread two vectors,
+// output written in address order); smaller ones the column-chunk kernel: wave w of chunk c owns vectors
 // c*64*U + lane + 64*u (u < U) of every row it visits (rows w, w + W, ...),
 // keeps that chunk of the current sample's gate in VGPRs, and issues all
 // 2*U residual/update loads of a row (non-temporal, unguarded) before it
@@ -185,6 +186,46 @@ __global__ __launch_bounds__(256) void rga_chunks_pf(RgaArgs a) {
 }
 
 // any D, any 2-byte alignment: one element per lane step
+// One-shot grid: block b covers vectors [c*256*U, (c+1)*256*U) of row
+// r = b / bpr (c = b % bpr); thread t takes vectors c*256*U + u*256 + t,
+// loads residual and update (non-temporal) and the gate (cached), stores
+// and exits, so the output is written in address order.
+template <int V, int U>
+__global__ __launch_bounds__(256) void rga_flat(RgaArgs a, int bpr) {
+  const int64_t r = blockIdx.x / bpr;
+  const int c = blockIdx.x - (int)r * bpr;
+  const int64_t b = r / a.S;
+  const int64_t s = r - b * a.S;
+  const int nvec = (int)(a.D / V);
+  const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
+  const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
+  const uint16_t* gr = a.gate + b * a.sg_b;
+  uint16_t* orow = a.out + r * a.D;
+  Vec<V> rv[U], uv[U], gv[U];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    ok[u] = v < nvec;
+    if (ok[u]) {
+      rv[u] = load_vec_nt<V>(rr + v * V);
+      uv[u] = load_vec_nt<V>(ur + v * V);
+      gv[u] = load_vec<V>(gr + v * V);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    if (ok[u]) {
+      const Vec<V> o = gate_add_vec<V>(rv[u], gv[u], uv[u]);
+      if constexpr (ADALN_RGA_NT_STORE)
+        store_vec_nt<V>(orow + v * V, o);
+      else
+        store_vec<V>(orow + v * V, o);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void rga_rows_scalar(RgaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); r < a.R;
@@ -244,9 +285,27 @@ int launch_chunks(const RgaArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+// The one-shot grid (two vectors per thread) for problems from 2^25
+// elements on, measured on MI355X: (4,4096,3072) 50.5 -> 48.2 us; smaller
+// ones keep the column chunks ((1,4096,4096) 17.8 us vs 17.9-18.1 flat).
+#ifndef ADALN_RGA_FLAT_U
+#define ADALN_RGA_FLAT_U 2
+#endif
+#ifndef ADALN_RGA_FLAT_MIN_ELEMS
+#define ADALN_RGA_FLAT_MIN_ELEMS ((int64_t)1 << 25)
+#endif
+
 // vectors per lane in one chunk: as many as a row needs, at most 8
 template <int V>
 int dispatch_chunks(const RgaArgs& a, hipStream_t st) {
+  if constexpr (ADALN_RGA_FLAT_U > 0) {
+    constexpr int U = ADALN_RGA_FLAT_U;
+    const int64_t bpr = (a.D / V + 256 * U - 1) / (256 * U);
+    if (a.R * a.D >= ADALN_RGA_FLAT_MIN_ELEMS && a.R * bpr < ((int64_t)1 << 24)) {
+      hipLaunchKernelGGL((rga_flat<V, U>), dim3((unsigned)(a.R * bpr)), dim3(256), 0, st, a, (int)bpr);
+      return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+    }
+  }
   const int64_t per_lane = (a.D / V + kWave - 1) / kWave;
   switch (std::min<int64_t>(per_lane, ADALN_RGA_MAX_U)) {
     case 1: return launch_chunks<V, 1>(a, st);

@@ -275,6 +275,20 @@ def test_rga_hidden_sizes(ops, orc, D):
     run_rga(ops, orc, res, gate, upd, what="D=%d" % D)
 
 
+def test_rga_large_one_shot_ragged(ops, orc):
+    # 2*4100*4104 elements (>= 2^25: the one-shot grid), 513 vectors per row
+    # (a ragged last block), then the same update in place
+    g = torch.Generator().manual_seed(57)
+    B, S, D = 2, 4100, 4104
+    res = rand_bf16((B, S, D), g).to(DEV)
+    upd = rand_bf16((B, S, D), g, std=4.0).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.1).to(DEV)
+    ref = run_rga(ops, orc, res, gate, upd, what="(2,4100,4104)")
+    ops.residual_gate_add(res, gate, upd, out=res)
+    torch.cuda.synchronize()
+    assert torch.equal(res.view(torch.int16), ref.view(torch.int16))
+
+
 def test_rga_inplace_and_views(ops, orc):
     g = torch.Generator().manual_seed(11)
     B, S, D = 2, 17, 3072
