@@ -222,17 +222,18 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // same bits), for rows of 7-8 vectors per lane, per output stage:
 //   PF    prefetch the next row into a second buffer (the wave walks rows);
 //         without it a wave holds one row and the grid covers every row
-//   BPC   blocks per compute unit in total
+//   BPC   blocks of four waves per compute unit in total
 //   XF32  keep an fp32 copy of x for the normalize pass rather than
 //         re-widening it from bf16 (one VALU op per element)
+//   WPB   waves per block when a wave holds one row (see kWpb)
 // The LayerNorm chain and RMSNorm run best with every row in flight at
-// once, one row per wave and four waves per SIMD, with the fp32 copy (109
+// once, one row per wave and four waves per SIMD, with the fp32 copy (108
 // VGPRs): their VALU work per row is what the last waves to get their data
 // wait on, and a prefetched second row costs the fp32 copy (two waves per
 // SIMD would remain).  The FP8 stage keeps the prefetch at two blocks per
-// compute unit; the fold is indifferent.  Shorter rows keep one buffer and an fp32 copy of x; longer rows
-// (up to 16 vectors per lane, 64 KiB of tables) keep one buffer and
-// re-widen.
+// compute unit, the fold at three.  Shorter rows keep one buffer and an fp32
+// copy of x at five blocks per compute unit; longer rows (up to 16 vectors
+// per lane, 64 KiB of tables) keep one buffer and re-widen.
 #ifndef ADALN_TAB_WPB_LN
 #define ADALN_TAB_WPB_LN 16
 #endif
