@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 1
+#define ADALN_ABI_VERSION 2
 
 /* status codes */
 #define ADALN_OK 0
@@ -226,8 +226,9 @@ int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, i
  *  mean_out, rstd_out   optional statistics of the updated residual
  *           ([B*S] fp32 each); NULL = skip.
  *  D        % 4 == 0, 4 <= D <= 65536.  One launch for 16-byte-aligned rows
- *           (8-byte when D % 8 != 0) with D <= 8192; otherwise the two
- *           unfused kernels run back to back on the stream.
+ *           with D % 8 == 0 at any D, and for 8-byte-aligned rows with
+ *           D % 8 == 4 up to D = 4096; other rows run the two unfused
+ *           kernels back to back on the stream (same bits).
  */
 int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b, int64_t sr_s,
                                   const void* gate, int64_t sg_b, const void* update, int64_t su_b,
@@ -365,12 +366,56 @@ int temb_table_slices_can_use(int64_t B, int64_t L, int64_t nmod, int64_t D, int
 
 /*
  * adaln_order_for -- the fixed fp32 reduction order the kernels use for a
- * row of D elements of op ADALN_OP_*: *V = elements per vector (8 when
- * D % 8 == 0, else 4), *L = lanes per row (64 for ln_modulate, the
- * residual-fused ln_modulate and rmsnorm_scale_shift, 16 for a q/k head of
- * qk_head_layernorm or qk_rmsnorm).  Pure host function.  Returns ADALN_OK or an error code.
+ * row of D elements of op ADALN_OP_* (ln_modulate_fold and ln_modulate_fp8
+ * use ADALN_OP_LN_MODULATE's order), so that a reference implementation can
+ * follow the same order and compare results bit for bit ("Fused Kernels"
+ * page, section "Numerical contracts and quality tiers": the bit-exact tier
+ * rests on a fixed reduction order).
+ *
+ *  op           ADALN_OP_*.
+ *  D            elements per row (head_dim for the q/k ops); > 0, % 4 == 0.
+ *  sx_d         element stride along the row of the storage that will be
+ *               passed (1 = contiguous; any value >= 0).
+ *  align_bytes  alignment of every row start in bytes (a power of two >= 2).
+ *  out          filled on success (caller-owned):
+ *    V     elements per vector: 8 when D % 8 == 0, else 4;
+ *    W     waves per row: 1 for a q/k head (four heads share a wave); for
+ *          the row ops the smallest power of two with 64*W*64 >= D, so a
+ *          lane holds at most 64 elements of the row (W = 1 up to D = 4096,
+ *          16 at D = 65536);
+ *    L     lanes per row: 64*W for the row ops, 16 for a q/k head;
+ *    map   ADALN_MAP_INTERLEAVED: vector v (elements v*V .. v*V+V-1) belongs
+ *          to lane v mod L, which pushes its vectors in increasing v and the
+ *          elements of a vector in increasing position;
+ *    fold  ADALN_FOLD_PAIRWISE: lane states are merged at offsets 1, 2, 4,
+ *          ..., L/2 (inside a wave, then across its waves through LDS): at
+ *          offset o lane l (l % 2o == 0) takes merge(state[l],
+ *          state[l + o]), lower lane first; the row's state is lane 0's.
+ *          LayerNorm merges Welford states (Chan-Golub-LeVeque, an empty
+ *          side leaving the other unchanged), RMSNorm adds the lanes' sums
+ *          of squares.
+ *  The order depends on op and D only: every storage the entry points
+ *  accept (vector loads, transposed tiles, element-wise gathers) is reduced
+ *  in this same order, so results are a function of the logical values;
+ *  sx_d and align_bytes are checked, not used to pick a different order.
+ *  Pure host function.  Returns ADALN_OK; ADALN_ERR_SHAPE for a bad D (or a
+ *  q/k head over 256), ADALN_ERR_STRIDE for sx_d < 0, ADALN_ERR_ALIGN for an
+ *  align_bytes that is not a power of two >= 2, ADALN_ERR_ARG for an unknown
+ *  op, ADALN_ERR_NULL for a NULL out, ADALN_ERR_TOO_LARGE for a row op with
+ *  D > 65536.
  */
-int adaln_order_for(int op, int64_t D, int* V, int* L);
+#define ADALN_MAP_INTERLEAVED 1
+#define ADALN_FOLD_PAIRWISE 1
+
+typedef struct adaln_order {
+  int V;
+  int L;
+  int W;
+  int map;
+  int fold;
+} adaln_order;
+
+int adaln_order_for(int op, int64_t D, int64_t sx_d, int align_bytes, adaln_order* out);
 
 /* static string naming a status code (never NULL) */
 const char* adaln_status_str(int status);

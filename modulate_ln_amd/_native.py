@@ -30,7 +30,9 @@ OP_QK_HEAD_LAYERNORM = 2
 OP_RESIDUAL_GATE_ADD_LN_MODULATE = 3
 OP_RMSNORM_SCALE_SHIFT = 4
 OP_QK_RMSNORM = 5
-ABI_VERSION = 1
+MAP_INTERLEAVED = 1
+FOLD_PAIRWISE = 1
+ABI_VERSION = 2
 
 # every symbol include/adaln.h declares
 EXPORTS = (
@@ -107,7 +109,7 @@ def lib():
     L.ln_modulate_fold.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp]
     L.ln_modulate_fp8.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, vp, ci, vp, vp, vp,
                                   vp]
-    L.adaln_order_for.argtypes = [ci, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    L.adaln_order_for.argtypes = [ci, i64, i64, ci, ctypes.POINTER(Order)]
     L.adaln_status_str.argtypes = [ci]
     L.adaln_status_str.restype = ctypes.c_char_p
     L.adaln_abi_version.argtypes = []
@@ -129,9 +131,19 @@ def check(fn: str, status: int) -> None:
         raise AdalnError(fn, status)
 
 
-def order_for(op: int, D: int):
-    """(V, L) of the fixed fp32 reduction order for a row of D elements."""
-    V = ctypes.c_int()
-    L = ctypes.c_int()
-    check("adaln_order_for", lib().adaln_order_for(op, D, ctypes.byref(V), ctypes.byref(L)))
-    return V.value, L.value
+class Order(ctypes.Structure):
+    """adaln_order: the fixed fp32 reduction order of a row (include/adaln.h)."""
+
+    _fields_ = [("V", ctypes.c_int), ("L", ctypes.c_int), ("W", ctypes.c_int), ("map", ctypes.c_int),
+                ("fold", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+def order_for(op: int, D: int, sx_d: int = 1, align_bytes: int = 16) -> Order:
+    """The library's fixed fp32 reduction order for a row of D elements of op stored with
+    element stride sx_d and row starts aligned to align_bytes (V, L, W, map, fold)."""
+    o = Order()
+    check("adaln_order_for", lib().adaln_order_for(op, D, sx_d, align_bytes, ctypes.byref(o)))
+    return o

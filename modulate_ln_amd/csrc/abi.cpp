@@ -32,6 +32,13 @@ extern "C" const char* adaln_status_str(int status) {
 
 extern "C" int adaln_abi_version(void) { return ADALN_ABI_VERSION; }
 
-extern "C" int adaln_order_for(int op, int64_t D, int* V, int* L) {
-  return adaln::order_for(op, D, V, L);
+extern "C" int adaln_order_for(int op, int64_t D, int64_t sx_d, int align_bytes, adaln_order* out) {
+  adaln_order o{};
+  const int rc = adaln::order_of(op, D, &o);
+  if (rc != ADALN_OK) return rc;
+  if (sx_d < 0) return ADALN_ERR_STRIDE;
+  if (align_bytes < 2 || (align_bytes & (align_bytes - 1)) != 0) return ADALN_ERR_ALIGN;
+  if (!out) return ADALN_ERR_NULL;
+  *out = o;
+  return ADALN_OK;
 }

@@ -73,20 +73,39 @@ inline bool extent_ok(std::initializer_list<Dim> dims) {
   return true;
 }
 
-inline int order_for(int op, int64_t D, int* V, int* L) {
+// Lanes of one wave per q/k head: a DPP row.
+constexpr int kHeadLanes = 16;
+constexpr int kWaveLanes = 64;
+constexpr int64_t kLaneElems = 64;  // most elements of a row one lane holds
+constexpr int64_t kMaxRowD = 65536;  // longest row of the row ops
+constexpr int64_t kMaxHeadD = 256;   // longest q/k head
+
+// The fixed reduction order of op for rows of D elements (the descriptor
+// adaln_order_for reports; the kernels follow it, whatever the storage).
+inline int order_of(int op, int64_t D, adaln_order* o) {
+  const bool row_op = op == ADALN_OP_LN_MODULATE || op == ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE ||
+                      op == ADALN_OP_RMSNORM_SCALE_SHIFT;
+  const bool head_op = op == ADALN_OP_QK_HEAD_LAYERNORM || op == ADALN_OP_QK_RMSNORM;
+  if (!row_op && !head_op) return ADALN_ERR_ARG;
   if (D <= 0 || D % 4 != 0) return ADALN_ERR_SHAPE;
-  int v = (D % 8 == 0) ? 8 : 4;
-  int l;
-  if (op == ADALN_OP_LN_MODULATE || op == ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE ||
-      op == ADALN_OP_RMSNORM_SCALE_SHIFT)
-    l = 64;
-  else if (op == ADALN_OP_QK_HEAD_LAYERNORM || op == ADALN_OP_QK_RMSNORM)
-    l = 16;
-  else
-    return ADALN_ERR_ARG;
-  if (V) *V = v;
-  if (L) *L = l;
+  if (head_op && D > kMaxHeadD) return ADALN_ERR_SHAPE;
+  if (row_op && D > kMaxRowD) return ADALN_ERR_TOO_LARGE;
+  o->V = (D % 8 == 0) ? 8 : 4;
+  // row ops: the fewest waves (a power of two) that leave at most 64
+  // elements per lane; a q/k head is 16 lanes of one wave
+  int w = 1;
+  while (row_op && (int64_t)w * kWaveLanes * kLaneElems < D) w *= 2;
+  o->W = w;
+  o->L = head_op ? kHeadLanes : 64 * o->W;
+  o->map = ADALN_MAP_INTERLEAVED;
+  o->fold = ADALN_FOLD_PAIRWISE;
   return ADALN_OK;
+}
+
+// Elements per vector of op's order (D already validated by the caller).
+inline int vec_of(int op, int64_t D) {
+  adaln_order o{};
+  return order_of(op, D, &o) == ADALN_OK ? o.V : 0;
 }
 
 }  // namespace adaln

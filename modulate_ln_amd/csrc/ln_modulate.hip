@@ -32,6 +32,7 @@
 #include "device_common.hpp"
 #include "host_common.hpp"
 #include "ln_row.hpp"
+#include "mw_row.hpp"
 
 namespace adaln {
 namespace {
@@ -64,80 +65,6 @@ __device__ __forceinline__ float qinv_of(const LnArgs& a) {
   return 1.0f;
 }
 
-template <int V, int E>
-__device__ __forceinline__ float elem(const Vec<V>& v) {
-  return (E & 1) ? hi_f32(v.w[E / 2]) : lo_f32(v.w[E / 2]);
-}
-
-// push the V elements of the lane's K-th vector; counts K*V+1 .. K*V+V
-template <int V, int K, int... E>
-__device__ __forceinline__ void push_vec(const Vec<V>& v, float& mean, float& m2,
-                                         std::integer_sequence<int, E...>) {
-  (welford_push<K * V + E + 1>(mean, m2, elem<V, E>(v)), ...);
-}
-
-template <int V, int... K>
-__device__ __forceinline__ void welford_lane(const Vec<V>* buf, int64_t nvec, int lane, float& mean,
-                                             float& m2, std::integer_sequence<int, K...>) {
-  (
-      [&] {
-        if ((int64_t)K * kWave + lane < nvec)
-          push_vec<V, K>(buf[K], mean, m2, std::make_integer_sequence<int, V>{});
-      }(),
-      ...);
-}
-
-// RMSNorm: the lane's sum of squares, same element order as welford_lane
-template <int V, int K, int... E>
-__device__ __forceinline__ void sumsq_vec(const Vec<V>& v, float& ss, std::integer_sequence<int, E...>) {
-  ((ss = __builtin_fmaf(elem<V, E>(v), elem<V, E>(v), ss)), ...);
-}
-
-template <int V, int... K>
-__device__ __forceinline__ void sumsq_lane(const Vec<V>* buf, int64_t nvec, int lane, float& ss,
-                                           std::integer_sequence<int, K...>) {
-  (
-      [&] {
-        if ((int64_t)K * kWave + lane < nvec) sumsq_vec<V, K>(buf[K], ss, std::make_integer_sequence<int, V>{});
-      }(),
-      ...);
-}
-
-// the per-element tail for one vector (RMS: x * rinv, no mean): V/2 bf16
-// pairs (the chain's output also for the FP8 tail, quantized by put_vec)
-template <int V, bool RMS, int TAIL>
-__device__ __forceinline__ void modulate_vec(const Vec<V>& xv, const Vec<V>& sv, const Vec<V>& hv, float mean,
-                                             float rstd, uint32_t* o) {
-#pragma unroll
-  for (int i = 0; i < V / 2; ++i) {
-    const float n0 = RMS ? lo_f32(xv.w[i]) * rstd : (lo_f32(xv.w[i]) - mean) * rstd;
-    const float n1 = RMS ? hi_f32(xv.w[i]) * rstd : (hi_f32(xv.w[i]) - mean) * rstd;
-    float p0 = 1.0f + lo_f32(sv.w[i]);
-    float p1 = 1.0f + hi_f32(sv.w[i]);
-    round_pair(p0, p1);  // bf16(1 + scale)
-    o[i] = tail_pair<TAIL>(n0, n1, p0, p1, lo_f32(hv.w[i]), hi_f32(hv.w[i]));
-  }
-}
-
-// store one vector's output at element v*V of row orow (bf16 rows may be
-// misaligned under GATHER; FP8 rows are V-byte aligned)
-template <int V, bool GATHER, int TAIL>
-__device__ __forceinline__ void put_vec(void* orow, int64_t v, const uint32_t* o, float qinv) {
-  if constexpr (TAIL == kTailFp8) {
-    uint32_t q8[V / 4];
-    fp8_stage<V>(o, qinv, false, q8);
-    store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
-  } else {
-    Vec<V> ov;
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) ov.w[i] = o[i];
-    if constexpr (GATHER)
-      scatter_vec<V>(static_cast<uint16_t*>(orow) + v * V, ov);
-    else
-      store_vec<V>(static_cast<uint16_t*>(orow) + v * V, ov);
-  }
-}
-
 // NV = the largest number of vectors any lane owns for the rows this
 // instantiation serves (the launcher guarantees D/V <= 64*NV).
 template <int V, int NV, bool GATHER, bool RMS, int TAIL>
@@ -167,11 +94,10 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
     }
 
     float mean = 0.0f, m2 = 0.0f;
+    lane_stats<V, RMS>(buf, (int)nvec, lane, kWave, mean, m2, std::make_integer_sequence<int, NV>{});
     if constexpr (RMS) {
-      sumsq_lane<V>(buf, nvec, lane, m2, std::make_integer_sequence<int, NV>{});
       sum_lanes<64>(m2);
     } else {
-      welford_lane<V>(buf, nvec, lane, mean, m2, std::make_integer_sequence<int, NV>{});
       float n = (float)(nv_lane * V);
       merge_lanes<64>(mean, m2, n, lane);
     }
@@ -197,7 +123,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
       const int64_t v = (int64_t)k * kWave + lane;
       if (v < nvec) {
         uint32_t o[V / 2];
-        modulate_vec<V, RMS, TAIL>(buf[k], sv[k], hv[k], mean, rstd, o);
+        modulate_vec<V, RMS, TAIL, true>(buf[k], sv[k], hv[k], mean, rstd, o);
         put_vec<V, GATHER, TAIL>(orow, v, o, qinv);
       }
     }
@@ -477,79 +403,64 @@ __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sa
                                               a.rstd_out ? a.rstd_out + r : nullptr, qinv_of<TAIL>(a), tab_finite);
 }
 
-// Rows too long to hold in registers: the same order, pass 2 re-reads the
-// row (from L2 when it is still resident).  1/n comes from a table of
-// correctly rounded reciprocals built at compile time.
-constexpr int kMaxStreamSteps = 65536 / kWave;  // counts per lane at D = 65536
-struct RcpTable {
-  float v[kMaxStreamSteps + 1];
-};
-constexpr RcpTable make_rcp_table() {
-  RcpTable t{};
-  t.v[0] = 0.0f;
-  for (int i = 1; i <= kMaxStreamSteps; ++i) t.v[i] = 1.0f / (float)i;
-  return t;
-}
-__constant__ RcpTable kRcp = make_rcp_table();
-
-template <int V, bool GATHER, bool RMS, int TAIL>
-__global__ __launch_bounds__(256) void ln_modulate_stream(LnArgs a) {
-  const float qinv = qinv_of<TAIL>(a);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nvec = a.D / V;
+// ---------------------------------------------------------------------------
+// Rows of more than 4096 elements: W = 2 .. 16 waves per row (one row per
+// block of 64 * W threads at a time), every lane holding at most 64 elements
+// of the row in registers (a single HBM read and a single HBM write at any
+// D), the waves' states merged through LDS in the fixed tree of mw_row.hpp.
+// The per-sample adaLN rows are read through the caches (a sample's rows are
+// shared by all its tokens).  NV: the most vector steps a lane takes (8 for
+// V = 8, 16 for V = 4); UNIF: every lane takes all NV.
+// ---------------------------------------------------------------------------
+template <int V, int NV, bool UNIF, bool GATHER, bool RMS, int TAIL>
+__global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mw(LnArgs a) {
+  __shared__ MwSlots slots;
+  const int W = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+  const int L = W * kWave;
+  const int g = threadIdx.x;
+  const int lane = g & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(g >> 6);
+  const int nvec = (int)(a.D / V);
   const float Df = (float)a.D;
-  const int64_t nv_lane = nvec > lane ? (nvec - lane + kWave - 1) / kWave : 0;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < a.R;
-       r += (int64_t)gridDim.x * 4) {
+  const float qinv = qinv_of<TAIL>(a);
+  int parity = 0;
+  for (int64_t r = blockIdx.x; r < a.R; r += gridDim.x, parity ^= 1) {
     const int64_t b = r / a.S;
     const int64_t s = r - b * a.S;
     const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
-    float mean = 0.0f, m2 = 0.0f;
-    for (int64_t k = 0; k < nv_lane; ++k) {
-      const int64_t v = k * kWave + lane;
-      Vec<V> xv = GATHER ? gather_vec<V>(xr + v * V * a.sx_d, a.sx_d) : load_vec<V>(xr + v * V);
+    Vec<V> buf[NV];
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const float x = (e & 1) ? hi_f32(xv.w[e / 2]) : lo_f32(xv.w[e / 2]);
-        if constexpr (RMS) {
-          m2 = __builtin_fmaf(x, x, m2);
-        } else {
-          const float rc = kRcp.v[k * V + e + 1];
-          float delta = x - mean;
-          mean = __builtin_fmaf(delta, rc, mean);
-          m2 = __builtin_fmaf(delta, x - mean, m2);
-        }
+    for (int k = 0; k < NV; ++k) {
+      if (UNIF || k * L < nvec) {  // block-uniform: steps past the row are not loaded
+        const int v = k * L + g;
+        const int vc = v < nvec ? v : nvec - 1;
+        if constexpr (GATHER)
+          buf[k] = gather_vec<V>(xr + (int64_t)vc * V * a.sx_d, a.sx_d);
+        else
+          buf[k] = load_vec_nt<V>(xr + (uint32_t)(vc * V));  // 32-bit offset from a scalar row base
       }
     }
-    if constexpr (RMS) {
-      sum_lanes<64>(m2);
-    } else {
-      float n = (float)(nv_lane * V);
-      merge_lanes<64>(mean, m2, n, lane);
-    }
-    const float rstd = finalize_rstd(m2, Df, a.eps);
-    if (lane == 0) {
+    float mean, m2;
+    mw_stats<V, NV, UNIF, RMS>(buf, nvec, g, lane, wave, W, slots.s[parity], mean, m2);
+    const float rstd = finalize_rstd(m2, Df, a.eps, pow2_inverse_f(Df));
+    if (g == 0) {
       if (!RMS && a.mean_out) a.mean_out[r] = mean;
       if (a.rstd_out) a.rstd_out[r] = rstd;
     }
     const uint16_t* sc = a.scale + b * a.ssc_b;
     const uint16_t* sh = a.shift + b * a.ssh_b;
     void* orow = out_row<TAIL>(a, r);
-    for (int64_t k = 0; k < nv_lane; ++k) {
-      const int64_t v = k * kWave + lane;
-      uint32_t o[V / 2];
-      if constexpr (GATHER) {
-        Vec<V> xv = gather_vec<V>(xr + v * V * a.sx_d, a.sx_d);
-        Vec<V> sv = gather_vec<V>(sc + v * V, 1);
-        Vec<V> hv = gather_vec<V>(sh + v * V, 1);
-        modulate_vec<V, RMS, TAIL>(xv, sv, hv, mean, rstd, o);
-      } else {
-        Vec<V> xv = load_vec<V>(xr + v * V);
-        Vec<V> sv = load_vec<V>(sc + v * V);
-        Vec<V> hv = load_vec<V>(sh + v * V);
-        modulate_vec<V, RMS, TAIL>(xv, sv, hv, mean, rstd, o);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * L + g;
+      if (UNIF || v < nvec) {
+        const uint32_t off = (uint32_t)(v * V);
+        const Vec<V> sv = GATHER ? gather_vec<V>(sc + off, 1) : load_vec<V>(sc + off);
+        const Vec<V> hv = GATHER ? gather_vec<V>(sh + off, 1) : load_vec<V>(sh + off);
+        uint32_t o[V / 2];
+        modulate_vec<V, RMS, TAIL, true>(buf[k], sv, hv, mean, rstd, o);
+        put_vec<V, GATHER, TAIL>(orow, v, o, qinv);
       }
-      put_vec<V, GATHER, TAIL>(orow, v, o, qinv);
     }
   }
 }
@@ -568,13 +479,26 @@ int launch_rows(const LnArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-template <int V, bool GATHER, bool RMS, int TAIL>
-int launch_stream(const LnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ln_modulate_stream<V, GATHER, RMS, TAIL>), dim3(grid_for(a.R)), dim3(256), 0, st, a);
+// one row per block of 64 * W threads at a time: the hardware dispatcher
+// hands a compute unit a new row as soon as one of its blocks finishes
+template <int V, int NV, bool UNIF, bool GATHER, bool RMS, int TAIL>
+int launch_mw(const LnArgs& a, int W, hipStream_t st) {
+  const unsigned blocks = (unsigned)std::min<int64_t>(a.R, kMaxBlocks);
+  hipLaunchKernelGGL((ln_modulate_mw<V, NV, UNIF, GATHER, RMS, TAIL>), dim3(blocks), dim3(W * kWave), 0, st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-constexpr int kTabMaxD = 8192;  // 64 KiB of LDS tables
+// W waves per row (W = 2 .. 16): every lane holds at most 64 elements, NV
+// vector steps of V
+template <int V, bool GATHER, bool RMS, int TAIL>
+int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
+  constexpr int NV = 64 / V;
+  const int64_t nvec = a.D / V;
+  if constexpr (V == 8) {
+    if (nvec == (int64_t)NV * W * kWave) return launch_mw<V, NV, true, GATHER, RMS, TAIL>(a, W, st);
+  }
+  return launch_mw<V, NV, false, GATHER, RMS, TAIL>(a, W, st);
+}
 
 template <int V, int NV, bool UNIF, bool RMS, int TAIL>
 int launch_tab(const LnArgs& a, hipStream_t st) {
@@ -640,19 +564,22 @@ int dispatch_tab(const LnArgs& a, hipStream_t st) {
   ADALN_TAB_CASE(6)
   ADALN_TAB_CASE(7)
   ADALN_TAB_CASE(8)
-  ADALN_TAB_CASE(9)
-  ADALN_TAB_CASE(10)
-  ADALN_TAB_CASE(11)
-  ADALN_TAB_CASE(12)
-  ADALN_TAB_CASE(13)
-  ADALN_TAB_CASE(14)
-  ADALN_TAB_CASE(15)
-  ADALN_TAB_CASE(16)
+  if constexpr (V == 4) {  // rows of up to 4096 elements: 16 steps of 4
+    ADALN_TAB_CASE(9)
+    ADALN_TAB_CASE(10)
+    ADALN_TAB_CASE(11)
+    ADALN_TAB_CASE(12)
+    ADALN_TAB_CASE(13)
+    ADALN_TAB_CASE(14)
+    ADALN_TAB_CASE(15)
+    ADALN_TAB_CASE(16)
+  }
 #undef ADALN_TAB_CASE
   return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
 }
 
 // vectors per lane -> the register-resident instantiation that covers it
+// (one wave per row: at most 64 elements per lane)
 template <int V, bool GATHER, bool RMS, int TAIL>
 int dispatch(const LnArgs& a, hipStream_t st) {
   const int64_t nv = (a.D / V + kWave - 1) / kWave;
@@ -665,11 +592,13 @@ int dispatch(const LnArgs& a, hipStream_t st) {
   ADALN_NV_CASE(5)
   ADALN_NV_CASE(6)
   ADALN_NV_CASE(8)
-  ADALN_NV_CASE(10)
-  ADALN_NV_CASE(12)
-  ADALN_NV_CASE(16)
+  if constexpr (V == 4) {
+    ADALN_NV_CASE(10)
+    ADALN_NV_CASE(12)
+    ADALN_NV_CASE(16)
+  }
 #undef ADALN_NV_CASE
-  return launch_stream<V, GATHER, RMS, TAIL>(a, st);
+  return ADALN_ERR_TOO_LARGE;  // not reached: W == 1 rows hold at most 64 elements per lane
 }
 
 }  // namespace
@@ -706,8 +635,9 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   const int64_t R = B * S;
   if (R == 0) return ADALN_OK;
   if (!x || !scale || !shift || !out || (kFp8 && !qscale)) return ADALN_ERR_NULL;
-  int V = 0;
-  order_for(RMS ? ADALN_OP_RMSNORM_SCALE_SHIFT : ADALN_OP_LN_MODULATE, D, &V, nullptr);
+  adaln_order ord{};
+  order_of(RMS ? ADALN_OP_RMSNORM_SCALE_SHIFT : ADALN_OP_LN_MODULATE, D, &ord);
+  const int V = ord.V;
   if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(shift, 2) || !aligned(out, kFp8 ? V : 2) ||
       !aligned(mean_out, 4) || !aligned(rstd_out, 4) || !aligned(qscale, 4))
     return ADALN_ERR_ALIGN;
@@ -754,9 +684,12 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
                    aligned(out, ob) && stride_ok(B, sx_b) && stride_ok(S, sx_s) &&
                    stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
   hipStream_t st = (hipStream_t)stream;
+  if (ord.W > 1) {  // rows of more than 4096 elements: W waves per row
+    if (V == 8) return vec ? dispatch_mw<8, false, RMS, TAIL>(a, ord.W, st) : dispatch_mw<8, true, RMS, TAIL>(a, ord.W, st);
+    return vec ? dispatch_mw<4, false, RMS, TAIL>(a, ord.W, st) : dispatch_mw<4, true, RMS, TAIL>(a, ord.W, st);
+  }
   // the tabled fast path indexes rows, samples and offsets in 32 bits
-  const bool tab = vec && D <= kTabMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
-                   B <= INT32_MAX;
+  const bool tab = vec && S <= INT32_MAX / 4 && B <= INT32_MAX;
   if (tab) return V == 8 ? dispatch_tab<8, RMS, TAIL>(a, st) : dispatch_tab<4, RMS, TAIL>(a, st);
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&

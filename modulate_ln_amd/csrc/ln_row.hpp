@@ -12,6 +12,7 @@
 #include <utility>
 
 #include "device_common.hpp"
+#include "mw_row.hpp"
 
 namespace adaln {
 namespace {
@@ -47,20 +48,6 @@ __device__ __forceinline__ void welford_f32(const float (*xf)[V], int nvec, int 
           push_f32<V, K>(xf[K], mean, m2, std::make_integer_sequence<int, V>{});
       }(),
       ...);
-}
-
-// bf16 -> fp32 widening the compiler may not merge with an earlier one:
-// re-widening a row from its packed form costs one VALU op per element but
-// spares the VGPRs an fp32 copy of the row would hold.
-__device__ __forceinline__ float lo_f32_again(uint32_t w) {
-  uint32_t r;
-  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
-  return __builtin_bit_cast(float, r);
-}
-__device__ __forceinline__ float hi_f32_again(uint32_t w) {
-  uint32_t r;
-  asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
-  return __builtin_bit_cast(float, r);
 }
 
 // The per-sample tables: bf16(1 + scale) and shift as fp32, float4-packed
@@ -235,9 +222,12 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
     }
   };
   if constexpr (TAIL == kTailFp8) {
-    // FP8: with finite statistics, finite adaLN rows and a finite 1/qscale
-    // no output can be NaN (an overflow to infinity still clamps to +-448)
-    const bool no_nan = tab_finite && __builtin_isfinite(mean) && __builtin_isfinite(rstd) &&
+    // FP8: with a finite mean, a finite non-zero rstd (so m2 is finite and
+    // no x - mean overflows), finite adaLN rows and a finite 1/qscale no
+    // output can be NaN (an overflow to infinity still clamps to +-448).  A
+    // row whose m2 overflows has rstd = 0 while x - mean may be infinite:
+    // inf * 0 is NaN, which the NaN-preserving clamp keeps.
+    const bool no_nan = tab_finite && __builtin_isfinite(mean) && __builtin_isfinite(rstd) && rstd > 0.0f &&
                         __builtin_isfinite(qinv);
     if (no_nan)
       steps(std::true_type{});

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void mod_flat(ModArgs a, int bpr) {
   const int c = blockIdx.x - (int)r * bpr;
   const int64_t b = r / a.S;
   const int64_t s = r - b * a.S;
-  const int nvec = (int)(a.D / V);
+  const int64_t nvec = a.D / V;  // 64-bit: rows may exceed 2^31 elements
   const uint16_t* xr = a.x + b * a.sx_b + s * a.sx_s;
   const uint16_t* scr = a.scale + b * a.ssc_b + (PER_TOKEN ? s * a.ssc_s : 0);
   const uint16_t* shr = a.shift + b * a.ssh_b + (PER_TOKEN ? s * a.ssh_s : 0);
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void mod_flat(ModArgs a, int bpr) {
   bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     ok[u] = v < nvec;
     if (ok[u]) {
       xv[u] = load_vec_nt<V>(xr + v * V);
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void mod_flat(ModArgs a, int bpr) {
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     if (ok[u]) {
       float o[V], h[V];
       mod_rows<V>(sv[u], hv[u], o, h);

@@ -429,8 +429,7 @@ static int qk_norm(const void* q, int64_t sq_b, int64_t sq_s, int64_t sq_h, cons
   a.Rq = R;
   a.eps = eps;
 
-  int V = 0;
-  order_for(RMS ? ADALN_OP_QK_RMSNORM : ADALN_OP_QK_HEAD_LAYERNORM, Dh, &V, nullptr);
+  const int V = vec_of(RMS ? ADALN_OP_QK_RMSNORM : ADALN_OP_QK_HEAD_LAYERNORM, Dh);
   const uintptr_t vb = (uintptr_t)(2 * V);
   auto st_ok = [&](int64_t n, int64_t s) { return n <= 1 || ((uintptr_t)s * 2u) % vb == 0; };
   bool vec = true;

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void rga_flat(RgaArgs a, int bpr) {
   const int c = blockIdx.x - (int)r * bpr;
   const int64_t b = r / a.S;
   const int64_t s = r - b * a.S;
-  const int nvec = (int)(a.D / V);
+  const int64_t nvec = a.D / V;  // 64-bit: rows may exceed 2^31 elements
   const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
   const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
   const uint16_t* gr = a.gate + b * a.sg_b;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void rga_flat(RgaArgs a, int bpr) {
   bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     ok[u] = v < nvec;
     if (ok[u]) {
       rv[u] = load_vec_nt<V>(rr + v * V);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void rga_flat(RgaArgs a, int bpr) {
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     if (ok[u]) {
       const Vec<V> o = gate_add_vec<V>(rv[u], gv[u], uv[u]);
       if constexpr (ADALN_RGA_NT_STORE)

@@ -17,12 +17,15 @@
 // bf16, stores it, and hands the packed row to the same per-row routine as
 // ln_modulate.  Per element: 2 reads + 2 writes of bf16 (8 bytes), against
 // 6 + 4 for the two unfused ops, one launch instead of two.
-// Other layouts (unaligned rows, rows over 8192) run the two unfused entry
-// points back to back: same bits, two launches.
+// Rows of more than 4096 elements take W waves per row (rga_ln_modulate_mw)
+// when D % 8 == 0.  Rows that are not vector-aligned, and rows of more than
+// 4096 elements with D % 8 != 0, run the two unfused entry points back to
+// back: same bits, two launches.
 
 #include "device_common.hpp"
 #include "host_common.hpp"
 #include "ln_row.hpp"
+#include "mw_row.hpp"
 
 // the unfused entry points, for the layouts the fused kernel does not take
 extern "C" int residual_gate_add(const void* residual, int64_t sr_b, int64_t sr_s, const void* gate,
@@ -177,7 +180,80 @@ __global__ __launch_bounds__((FusedShape<NV, UNIF>::kWpb * 64)) void rga_ln_modu
   }
 }
 
-constexpr int kFusedMaxD = 8192;  // 96 KiB of LDS tables
+// bf16(residual + bf16(gate * update)) for one vector, packed
+template <int V>
+__device__ __forceinline__ Vec<V> gate_add_vec(const Vec<V>& r, const Vec<V>& u, const Vec<V>& g) {
+  Vec<V> x;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    float t0 = lo_f32(g.w[i]) * lo_f32(u.w[i]), t1 = hi_f32(g.w[i]) * hi_f32(u.w[i]);
+    round_pair(t0, t1);  // bf16(gate * update)
+    x.w[i] = pack_bf16(lo_f32(r.w[i]) + t0, hi_f32(r.w[i]) + t1);  // bf16(residual + t)
+  }
+  return x;
+}
+
+// Rows of more than 4096 elements: W = 2 .. 16 waves per row, one row per
+// block of 64 * W threads at a time (the layout of ln_modulate's long rows):
+// each lane forms the new residual of its vectors (at most 64 elements),
+// stores it, and the block reduces it in the fixed tree of mw_row.hpp.  The
+// per-sample gate, scale and shift rows are read through the caches.
+template <int V, int NV, bool UNIF>
+__global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mw(FusedArgs a) {
+  __shared__ MwSlots slots;
+  const int W = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+  const int L = W * kWave;
+  const int g = threadIdx.x;
+  const int lane = g & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(g >> 6);
+  const int nvec = (int)(a.D / V);
+  const float Df = (float)a.D;
+  int parity = 0;
+  for (int64_t r = blockIdx.x; r < a.R; r += gridDim.x, parity ^= 1) {
+    const int64_t b = r / a.S;
+    const int64_t s = r - b * a.S;
+    const uint16_t* rr = a.res + b * a.sr_b + s * a.sr_s;
+    const uint16_t* ur = a.upd + b * a.su_b + s * a.su_s;
+    const uint16_t* gt = a.gate + b * a.sg_b;
+    uint16_t* xrow = a.res_out + r * a.D;
+    Vec<V> xn[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (UNIF || k * L < nvec) {  // block-uniform: steps past the row are not loaded
+        const int v = k * L + g;
+        const int vc = v < nvec ? v : nvec - 1;
+        const uint32_t off = (uint32_t)(vc * V);  // 32-bit offsets from scalar row bases
+        const Vec<V> rv = load_vec_nt<V>(rr + off);
+        const Vec<V> uv = load_vec_nt<V>(ur + off);
+        const Vec<V> gv = load_vec<V>(gt + off);
+        xn[k] = gate_add_vec<V>(rv, uv, gv);
+        if (UNIF || v < nvec) store_vec_nt<V>(xrow + (uint32_t)(v * V), xn[k]);
+      }
+    }
+    float mean, m2;
+    mw_stats<V, NV, UNIF, false>(xn, nvec, g, lane, wave, W, slots.s[parity], mean, m2);
+    const float rstd = finalize_rstd(m2, Df, a.eps, pow2_inverse_f(Df));
+    if (g == 0) {
+      if (a.mean_out) a.mean_out[r] = mean;
+      if (a.rstd_out) a.rstd_out[r] = rstd;
+    }
+    const uint16_t* sc = a.scale + b * a.ssc_b;
+    const uint16_t* sh = a.shift + b * a.ssh_b;
+    uint16_t* orow = a.out + r * a.D;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = k * L + g;
+      if (UNIF || v < nvec) {
+        const Vec<V> sv = load_vec<V>(sc + v * V);
+        const Vec<V> hv = load_vec<V>(sh + v * V);
+        uint32_t o[V / 2];
+        modulate_vec<V, false, kTailChain, true>(xn[k], sv, hv, mean, rstd, o);
+        put_vec<V, false, kTailChain>(orow, v, o, 1.0f);
+      }
+    }
+  }
+}
+
 constexpr int64_t kLdsPerCu = 160 * 1024;
 
 template <int V, int NV, bool UNIF>
@@ -213,16 +289,32 @@ int dispatch_fused(const FusedArgs& a, hipStream_t st) {
   ADALN_FUSED_CASE(6)
   ADALN_FUSED_CASE(7)
   ADALN_FUSED_CASE(8)
-  ADALN_FUSED_CASE(9)
-  ADALN_FUSED_CASE(10)
-  ADALN_FUSED_CASE(11)
-  ADALN_FUSED_CASE(12)
-  ADALN_FUSED_CASE(13)
-  ADALN_FUSED_CASE(14)
-  ADALN_FUSED_CASE(15)
-  ADALN_FUSED_CASE(16)
+  if constexpr (V == 4) {  // rows of up to 4096 elements: 16 steps of 4
+    ADALN_FUSED_CASE(9)
+    ADALN_FUSED_CASE(10)
+    ADALN_FUSED_CASE(11)
+    ADALN_FUSED_CASE(12)
+    ADALN_FUSED_CASE(13)
+    ADALN_FUSED_CASE(14)
+    ADALN_FUSED_CASE(15)
+    ADALN_FUSED_CASE(16)
+  }
 #undef ADALN_FUSED_CASE
   return ADALN_ERR_TOO_LARGE;  // not reached: the caller bounds D
+}
+
+// W waves per row (W = 2 .. 16), every lane holding at most 64 elements in
+// 8 vectors of 8.  (Rows with D % 8 != 0 would need 16 steps of 4 with three
+// inputs each, more than the VGPRs of a 1024-thread block: they take the two
+// unfused kernels.)
+int dispatch_fused_mw(const FusedArgs& a, int W, hipStream_t st) {
+  constexpr int V = 8, NV = 8;
+  const unsigned blocks = (unsigned)std::min<int64_t>(a.R, (int64_t)1 << 20);
+  if (a.D / V == (int64_t)NV * W * kWave)
+    hipLaunchKernelGGL((rga_ln_modulate_mw<V, NV, true>), dim3(blocks), dim3(W * kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL((rga_ln_modulate_mw<V, NV, false>), dim3(blocks), dim3(W * kWave), 0, st, a);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 }  // namespace
@@ -299,12 +391,15 @@ extern "C" int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b,
     if (overlaps(sm, *t) || overlaps(sr, *t)) return ADALN_ERR_ALIAS;
   if (overlaps(sm, sr)) return ADALN_ERR_ALIAS;
 
-  int V = 0;
-  order_for(ADALN_OP_LN_MODULATE, D, &V, nullptr);
+  adaln_order ord{};
+  order_of(ADALN_OP_RESIDUAL_GATE_ADD_LN_MODULATE, D, &ord);
+  const int V = ord.V;
   const uintptr_t vb = (uintptr_t)(2 * V);
   auto stride_ok = [&](int64_t n, int64_t st) { return n <= 1 || ((uintptr_t)st * 2u) % vb == 0; };
-  const bool fused = D <= kFusedMaxD && D / V <= 16 * kWave && S <= INT32_MAX / 4 &&
-                     B <= INT32_MAX && aligned(residual, vb) && aligned(update, vb) &&
+  // one launch for vector-aligned rows (the tabled kernel indexes rows,
+  // samples and offsets in 32 bits)
+  const bool fused = (ord.W > 1 ? V == 8 : (S <= INT32_MAX / 4 && B <= INT32_MAX)) && aligned(residual, vb) &&
+                     aligned(update, vb) &&
                      aligned(gate, vb) && aligned(scale, vb) && aligned(shift, vb) &&
                      aligned(residual_out, vb) && aligned(out, vb) && stride_ok(B, sr_b) &&
                      stride_ok(S, sr_s) && stride_ok(B, su_b) && stride_ok(S, su_s) &&
@@ -339,5 +434,6 @@ extern "C" int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b,
   a.S = S;
   a.D = D;
   a.R = R;
+  if (ord.W > 1) return dispatch_fused_mw(a, ord.W, st);
   return V == 8 ? dispatch_fused<8>(a, st) : dispatch_fused<4>(a, st);
 }

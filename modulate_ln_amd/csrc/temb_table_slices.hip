@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void temb_flat(TembArgs a, int bpr) {
   const int64_t r = q - m * a.R;
   const int64_t b = r / a.L;
   const int64_t l = r - b * a.L;
-  const int nvec = (int)(a.D / V);
+  const int64_t nvec = a.D / V;  // 64-bit: rows may exceed 2^31 elements
   const T* er = static_cast<const T*>(a.temb) + b * a.se_b + l * a.se_l + m * a.se_m;
   const float* tr = a.table + m * a.st_m;
   float* orow = a.out + (m * a.R + r) * a.D;
@@ -151,13 +151,13 @@ __global__ __launch_bounds__(256) void temb_flat(TembArgs a, int bpr) {
   bool ok[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     ok[u] = v < nvec;
     if (ok[u]) loadv<V>(er + v * V, e[u]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = c * 256 * U + u * 256 + (int)threadIdx.x;
+    const int64_t v = (int64_t)c * 256 * U + u * 256 + (int)threadIdx.x;
     if (ok[u]) {
       float s[V];
 #pragma unroll

@@ -18,12 +18,17 @@ class Prepared:
     """A marshalled call: the C function and its argument tuple, ready to issue.
 
     Calling it enqueues the kernel(s) again with the same pointers, sizes and
-    stream (for tight loops where per-call marshalling would dominate)."""
+    stream (for tight loops where per-call marshalling would dominate).  It
+    holds a reference to every tensor whose address is in its arguments
+    (``keep``), so none of them is freed -- and its memory reused by the
+    allocator -- while the prepared call exists; the values read are those
+    the tensors hold when the call is issued."""
 
-    __slots__ = ("name", "fn", "args", "result")
+    __slots__ = ("name", "fn", "args", "result", "keep")
 
-    def __init__(self, name, fn, args, result):
+    def __init__(self, name, fn, args, result, keep=()):
         self.name, self.fn, self.args, self.result = name, fn, args, result
+        self.keep = tuple(t for t in keep if t is not None)
 
     def __call__(self):
         rc = self.fn(*self.args)
@@ -88,7 +93,8 @@ def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: 
         x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
         scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
         mean_out.data_ptr() if mean_out is not None else None,
-        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out,
+        keep=(x, scale, shift, out, mean_out, rstd_out))
     return call if prepare else call()
 
 
@@ -123,7 +129,8 @@ def ln_modulate_fold(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, 
         x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
         scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
         mean_out.data_ptr() if mean_out is not None else None,
-        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out,
+        keep=(x, scale, shift, out, mean_out, rstd_out))
     return call if prepare else call()
 
 
@@ -142,7 +149,8 @@ def ln_modulate_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, q
         x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
         scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), qscale.data_ptr(), N.BF16, out.data_ptr(),
         mean_out.data_ptr() if mean_out is not None else None,
-        rstd_out.data_ptr() if rstd_out is not None else None, st), out)
+        rstd_out.data_ptr() if rstd_out is not None else None, st), out,
+        keep=(x, scale, shift, qscale, out, mean_out, rstd_out))
     return call if prepare else call()
 
 
@@ -171,7 +179,7 @@ def rmsnorm_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
     call = Prepared("rmsnorm_scale_shift", N.lib().rmsnorm_scale_shift, (
         x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
         scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
-        rinv_out.data_ptr() if rinv_out is not None else None, st), out)
+        rinv_out.data_ptr() if rinv_out is not None else None, st), out, keep=(x, scale, shift, out, rinv_out))
     return call if prepare else call()
 
 
@@ -197,7 +205,8 @@ def residual_gate_add(residual: torch.Tensor, gate: torch.Tensor, update: torch.
     st = _stream_handle(residual, stream)
     call = Prepared("residual_gate_add", N.lib().residual_gate_add, (
         residual.data_ptr(), residual.stride(0), residual.stride(1), gate.data_ptr(), sg,
-        update.data_ptr(), update.stride(0), update.stride(1), B, S, D, N.BF16, out.data_ptr(), st), out)
+        update.data_ptr(), update.stride(0), update.stride(1), B, S, D, N.BF16, out.data_ptr(), st), out,
+        keep=(residual, gate, update, out))
     return call if prepare else call()
 
 
@@ -242,7 +251,8 @@ def residual_gate_add_ln_modulate(residual: torch.Tensor, gate: torch.Tensor, up
         scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16,
         residual_out.data_ptr(), out.data_ptr(),
         mean_out.data_ptr() if mean_out is not None else None,
-        rstd_out.data_ptr() if rstd_out is not None else None, st), (residual_out, out))
+        rstd_out.data_ptr() if rstd_out is not None else None, st), (residual_out, out),
+        keep=(residual, gate, update, scale, shift, residual_out, out, mean_out, rstd_out))
     return call if prepare else call()
 
 
@@ -281,7 +291,7 @@ def modulate_scale_shift(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tens
     st = _stream_handle(x, stream)
     call = Prepared("modulate_scale_shift", N.lib().modulate_scale_shift, (
         x.data_ptr(), x.stride(0), x.stride(1), scale.data_ptr(), ssc_b, ssc_s, shift.data_ptr(), ssh_b, ssh_s,
-        B, S, D, N.BF16, out.data_ptr(), st), out)
+        B, S, D, N.BF16, out.data_ptr(), st), out, keep=(x, scale, shift, out))
     return call if prepare else call()
 
 
@@ -316,7 +326,7 @@ def temb_table_slices(table: torch.Tensor, temb: torch.Tensor, *, out: torch.Ten
     st = _stream_handle(temb, stream)
     call = Prepared("temb_table_slices", N.lib().temb_table_slices, (
         table.data_ptr(), table.stride(0), temb.data_ptr(), temb.stride(0), temb.stride(1), temb.stride(2),
-        B, L, M, D, dt, out.data_ptr(), st), out)
+        B, L, M, D, dt, out.data_ptr(), st), out, keep=(table, temb, out))
     return call if prepare else call()
 
 
@@ -356,7 +366,7 @@ def qk_head_layernorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None 
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         B, S, H, Dh, ptr(wq), ptr(bq), ptr(wk), ptr(bk), float(eps), N.BF16,
-        q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out))
+        q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out), keep=(q, k, wq, bq, wk, bk, q_out, k_out))
     return call if prepare else call()
 
 
@@ -392,7 +402,8 @@ def qk_rmsnorm(q: torch.Tensor, k: torch.Tensor, wq: torch.Tensor | None = None,
     call = Prepared("qk_rmsnorm", N.lib().qk_rmsnorm, (
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
-        B, S, H, Dh, ptr(wq), ptr(wk), float(eps), N.BF16, q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out))
+        B, S, H, Dh, ptr(wq), ptr(wk), float(eps), N.BF16, q_out.data_ptr(), k_out.data_ptr(), st), (q_out, k_out),
+        keep=(q, k, wq, wk, q_out, k_out))
     return call if prepare else call()
 
 
@@ -416,5 +427,6 @@ def bias_gelu_tanh(x: torch.Tensor, bias: torch.Tensor, *, out: torch.Tensor | N
             raise ValueError("out must be a contiguous [rows, width] tensor")
     st = _stream_handle(x, stream)
     call = Prepared("bias_gelu_tanh", N.lib().bias_gelu_tanh,
-                    (x.data_ptr(), rows, width, x.stride(0), bias.data_ptr(), N.BF16, out.data_ptr(), st), out)
+                    (x.data_ptr(), rows, width, x.stride(0), bias.data_ptr(), N.BF16, out.data_ptr(), st), out,
+        keep=(x, bias, out))
     return call if prepare else call()

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.adaln_abi_version() == N.ABI_VERSION == 1
+    assert L.adaln_abi_version() == N.ABI_VERSION == 2
     codes = [N.OK, N.ERR_NULL, N.ERR_SHAPE, N.ERR_DTYPE, N.ERR_ALIGN, N.ERR_ALIAS, N.ERR_TOO_LARGE,
              N.ERR_STRIDE, N.ERR_HIP, N.ERR_ARG]
     names = [N.status_str(c) for c in codes]
@@ -54,21 +54,59 @@ def test_version_and_status_strings(L):
     assert N.status_str(12345) == "unknown status"
 
 
-@pytest.mark.parametrize("D,V", [(4, 4), (8, 8), (12, 4), (512, 8), (2240, 8), (4100, 4), (65536, 8)])
-def test_order_for(D, V):
-    assert N.order_for(N.OP_LN_MODULATE, D) == (V, 64)
-    assert N.order_for(N.OP_QK_HEAD_LAYERNORM, D) == (V, 16)
-    assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D) == (V, 64)
-    assert N.order_for(N.OP_RMSNORM_SCALE_SHIFT, D) == (V, 64)
-    assert N.order_for(N.OP_QK_RMSNORM, D) == (V, 16)
+# storage classes the entry points take, as (element stride, row-start alignment in bytes):
+# vector loads (16- and 8-byte rows), element gathers (2-byte rows, padded strides), and the
+# transposed tiles of tokens-contiguous storage (hidden elements S apart)
+LAYOUTS = [(1, 16), (1, 8), (1, 4), (1, 2), (3, 2), (1024, 16), (4096, 2)]
+ROW_OPS = (N.OP_LN_MODULATE, N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, N.OP_RMSNORM_SCALE_SHIFT)
+HEAD_OPS = (N.OP_QK_HEAD_LAYERNORM, N.OP_QK_RMSNORM)
 
 
-@pytest.mark.parametrize("D", [0, -4, 6, 2242])
-def test_order_for_rejects(D):
-    with pytest.raises(N.AdalnError):
-        N.order_for(N.OP_LN_MODULATE, D)
-    with pytest.raises(N.AdalnError):
-        N.order_for(7, 512)
+@pytest.mark.parametrize("D,V", [(4, 4), (8, 8), (12, 4), (512, 8), (2240, 8), (4096, 8), (4100, 4), (8192, 8),
+                                 (16392, 8), (65532, 4), (65536, 8)])
+def test_order_for_row_ops(D, V):
+    for op in ROW_OPS:
+        want = None
+        for sx_d, align in LAYOUTS:
+            o = N.order_for(op, D, sx_d, align)
+            d = o.as_dict()
+            assert d["V"] == V and d["map"] == N.MAP_INTERLEAVED and d["fold"] == N.FOLD_PAIRWISE, d
+            assert d["L"] == 64 * d["W"] and d["W"] >= 1 and (d["W"] & (d["W"] - 1)) == 0, d
+            # at most 64 elements per lane: the row is held in registers, read from memory once
+            assert 64 * d["L"] >= D, d
+            # the order is a function of op and D only: every storage class reduces alike
+            want = want or d
+            assert d == want, (sx_d, align, d, want)
+
+
+@pytest.mark.parametrize("D,V", [(4, 4), (12, 4), (64, 8), (128, 8), (132, 4), (256, 8)])
+def test_order_for_head_ops(D, V):
+    for op in HEAD_OPS:
+        for sx_d, align in LAYOUTS:
+            assert N.order_for(op, D, sx_d, align).as_dict() == {
+                "V": V, "L": 16, "W": 1, "map": N.MAP_INTERLEAVED, "fold": N.FOLD_PAIRWISE}
+
+
+def test_order_for_rejects(L):
+    def rc(op, D, sx_d=1, align=16, out=True):
+        import ctypes
+
+        o = N.Order()
+        return L.adaln_order_for(op, D, sx_d, align, ctypes.byref(o) if out else None)
+
+    for D in (0, -4, 6, 2242):
+        assert rc(N.OP_LN_MODULATE, D) == N.ERR_SHAPE
+        assert rc(N.OP_QK_HEAD_LAYERNORM, D) == N.ERR_SHAPE
+        with pytest.raises(N.AdalnError):
+            N.order_for(N.OP_LN_MODULATE, D)
+    assert rc(N.OP_QK_HEAD_LAYERNORM, 260) == N.ERR_SHAPE
+    assert rc(N.OP_LN_MODULATE, 65540) == N.ERR_TOO_LARGE
+    assert rc(7, 512) == N.ERR_ARG
+    assert rc(0, 512) == N.ERR_ARG
+    assert rc(N.OP_LN_MODULATE, 512, sx_d=-1) == N.ERR_STRIDE
+    for a in (0, 1, 3, 12, -16):
+        assert rc(N.OP_LN_MODULATE, 512, align=a) == N.ERR_ALIGN
+    assert rc(N.OP_LN_MODULATE, 512, out=False) == N.ERR_NULL
 
 
 def test_ln_modulate_can_use(L):

@@ -2,9 +2,9 @@
 with ln_modulate of its result) with the CPU oracle, through the C ABI.
 
 Bar: both outputs (the new residual and the modulated norm) and the fp32
-statistics bit-exact against the oracle's fixed-order fp32 mode (V = 8 when
-D % 8 == 0 else 4, L = 64), and bit-identical to the two unfused entry
-points run back to back.
+statistics bit-exact against the oracle's fixed-order fp32 mode, run in the
+order the library reports (adaln_order_for), and bit-identical to the two
+unfused entry points run back to back.
 """
 
 from __future__ import annotations
@@ -15,7 +15,7 @@ import torch
 
 from modulate_ln_amd import workloads as W
 
-from test_gpu_parity import DEV, FP32, assert_bits_equal, bits, gpu_chain, oracle_chain_rows, order, rand_bf16
+from test_gpu_parity import DEV, FP32, N_OP_FUSED, N_OP_LN, assert_bits_equal, bits, gpu_chain, oracle_chain_rows, order, rand_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,8 @@ def run_fused(ops, orc, res, gate, upd, scale, shift, eps, *, what="", residual_
     xo, y = ops.residual_gate_add_ln_modulate(res, gate, upd, scale, shift, eps, residual_out=residual_out,
                                               out=out, mean_out=mean, rstd_out=rstd)
     torch.cuda.synchronize()
-    V, L = order(D, 64)
+    V, L = order(N_OP_FUSED, D, res)
+    assert order(N_OP_FUSED, D, upd) == (V, L) == order(N_OP_LN, D, res)
     want_x, want_y, m32, r32 = orc.residual_gate_add_ln_modulate(res_b, g_b, upd_b, sc_b, sh_b, S, eps, FP32,
                                                                  V=V, L=L)
     assert_bits_equal(bits(xo.reshape(R, D)), want_x, "residual_out " + what)
@@ -75,6 +76,26 @@ def test_fused_hidden_sizes(ops, orc, D):
     upd = rand_bf16((B, S, D), g, std=3.0).to(DEV)
     emb = rand_bf16((B, 6, D), g, std=0.1).to(DEV)
     run_fused(ops, orc, res, emb[:, 2], upd, emb[:, 1], emb[:, 0], 1e-6, what="D=%d" % D)
+
+
+@pytest.mark.parametrize("D,W", [(8192, 2), (4100, 2), (12296, 4), (32768, 8), (65536, 16), (65532, 16)])
+def test_fused_waves_per_row(ops, orc, D, W):
+    """Rows of W > 1 waves take one fused launch (the cross-wave merge through LDS) and match
+    the oracle in the order the library reports."""
+    from modulate_ln_amd import _native as N
+
+    assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D).W == W
+    g = torch.Generator().manual_seed(D + 3)
+    B, S = 2, 3
+    res = rand_bf16((B, S, D), g, std=2.0).to(DEV)
+    upd = rand_bf16((B, S, D), g).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="W=%d D=%d" % (W, D))
+    # padded rows (still vector-aligned): the fused kernel reads strided rows
+    bigr = rand_bf16((B, S, D + 16), g).to(DEV)
+    run_fused(ops, orc, bigr[:, :, 8:8 + D], gate, upd, sc, sh, 1e-5, what="strided W=%d D=%d" % (W, D))
 
 
 @pytest.mark.parametrize("B,S", [(1, 1), (3, 1), (1, 5), (3, 37), (2, 1024), (5, 301)])

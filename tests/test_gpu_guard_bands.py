@@ -67,7 +67,7 @@ def same_bytes(got, want, what, fp8=False):
     assert bool(ok.all()), "%s: %d bytes differ from the unbanded call" % (what, int((~ok).sum()))
 
 
-SHAPES = [(3, 37, 2240), (1, 5, 4100), (2, 3, 12), (1, 7, 4096), (2, 1, 520)]
+SHAPES = [(3, 37, 2240), (1, 5, 4100), (2, 3, 12), (1, 7, 4096), (2, 1, 520), (2, 3, 12296), (1, 2, 65532)]
 SKEWS = {torch.bfloat16: (0, 2), torch.float32: (0, 4), torch.float8_e4m3fn: (0, 8)}
 
 

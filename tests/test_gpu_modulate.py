@@ -13,7 +13,7 @@ import torch
 
 from modulate_ln_amd import workloads as W
 
-from test_gpu_parity import DEV, FP32, assert_bits_equal, bits, rand_bf16
+from test_gpu_parity import DEV, FP32, assert_bits_equal, bits, device_normal_bf16, rand_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,24 @@ def test_modulate_large_per_sample(ops, orc):
     sc = rand_bf16((2, 4096), g, std=0.1).to(DEV)
     sh = rand_bf16((2, 4096), g, std=0.1).to(DEV)
     run_mod(ops, orc, x, sc, sh, what="(2,4096,4096) per sample")
+
+
+def test_modulate_row_beyond_2g_elements(ops, orc):
+    """One row of 2^31 + 4096 elements (the one-shot grid, 2 GiB+ per tensor): element offsets
+    pass 2^31, so its indexing must be 64-bit.  The oracle checks the first and the last 8192
+    elements (the op is element-wise)."""
+    D = (1 << 31) + 4096
+    x = device_normal_bf16((1, 1, D), 11)
+    sc = device_normal_bf16((1, 1, D), 12, std=0.1)
+    sh = device_normal_bf16((1, 1, D), 13, std=0.1)
+    y = ops.modulate_scale_shift(x, sc, sh)
+    torch.cuda.synchronize()
+    for lo in (0, D - 8192):
+        sl = slice(lo, lo + 8192)
+        want = orc.modulate_scale_shift(bits(x[0, :, sl]), bits(sc[0, :, sl]), bits(sh[0, :, sl]), 1, FP32)
+        assert_bits_equal(bits(y[0, :, sl]), want, "modulate beyond 2^31 at %d" % lo)
+    del x, sc, sh, y
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("D", [1, 3, 4, 8, 520, 2240, 4096, 4100, 12288])

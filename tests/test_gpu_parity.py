@@ -1,9 +1,10 @@
 """Parity of the HIP kernels (through the C ABI) with the CPU oracle.
 
 Bar: bit-exact against the oracle's fixed-order fp32 mode for ln_modulate,
-residual_gate_add and qk_head_layernorm (the kernels adopt that order: V = 8
-elements per vector when D % 8 == 0 else 4; L = 64 lanes per row, 16 per
-head); within one bf16 ulp of the fp64 oracle for bias + tanh-GELU.  The
+residual_gate_add and qk_head_layernorm, run in the order the library reports
+through adaln_order_for (V elements per vector, L = 64 W lanes per row for W
+waves, 16 per q/k head); within one bf16 ulp of the fp64 oracle for bias +
+tanh-GELU.  The
 fp64 mode is checked too, at the tolerances the statistics contract states.
 Inputs are the seeded synthetic workloads at full size where the oracle is
 fast enough, plus edge shapes (tails, tiny and maximal D, strided and
@@ -22,6 +23,7 @@ pytestmark = pytest.mark.gpu
 
 FP32, FP64 = 1, 0
 DEV = "cuda"
+N_OP_LN, N_OP_QK, N_OP_FUSED, N_OP_RMS, N_OP_QK_RMS = 1, 2, 3, 4, 5  # ADALN_OP_* (include/adaln.h)
 
 
 @pytest.fixture(scope="module")
@@ -34,8 +36,26 @@ def ops():
     return m
 
 
-def order(D: int, L: int):
-    return (8 if D % 8 == 0 else 4), L
+def row_align(t) -> int:
+    """Largest power of two (2..16) dividing the byte address of every row start of t."""
+    a = t.data_ptr()
+    for st, n in zip(t.stride()[:-1], t.shape[:-1]):
+        if n > 1:
+            a |= st * t.element_size()
+    a |= 16
+    return a & -a
+
+
+def order(op: int, D: int, t=None):
+    """(V, L) of the reduction order the library reports for op on rows of D elements
+    (adaln_order_for through the C ABI), for the storage of the device view t if given."""
+    from modulate_ln_amd import _native as N
+
+    sx_d = t.stride(-1) if t is not None else 1
+    o = N.order_for(op, D, sx_d, row_align(t) if t is not None else 16)
+    assert o.L == (16 if op in (N.OP_QK_HEAD_LAYERNORM, N.OP_QK_RMSNORM) else 64 * o.W), o.as_dict()
+    assert o.map == N.MAP_INTERLEAVED and o.fold == N.FOLD_PAIRWISE, o.as_dict()
+    return o.V, o.L
 
 
 def bits(t):
@@ -78,7 +98,7 @@ def run_ln(ops, orc, x_dev, scale_dev, shift_dev, eps, *, stats=True, out=None, 
     sh_b = bits(sh.expand(B, D))
     y = ops.ln_modulate(x_dev, scale_dev, shift_dev, eps, out=out, mean_out=mean, rstd_out=rstd)
     torch.cuda.synchronize()
-    V, L = order(D, 64)
+    V, L = order(N_OP_LN, D, x_dev)
     want, m32, r32 = orc.ln_modulate(x_log, sc_b, sh_b, S, eps, FP32, V=V, L=L)
     assert_bits_equal(bits(y.reshape(B * S, D)), want, "ln_modulate %s" % what)
     if stats:
@@ -126,6 +146,31 @@ def test_ln_hidden_sizes(ops, orc, D):
     sc = rand_bf16((B, D), g, std=0.1).to(DEV)
     sh = rand_bf16((B, D), g, std=0.1).to(DEV)
     run_ln(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
+
+
+# rows held by W = 1, 2, 4, 8, 16 waves (the cross-wave merge through LDS), with every lane
+# full (D = 4096 W) or a ragged last step (and V = 4 when D % 8 != 0)
+WAVE_ROWS = [(4096, 1), (4092, 1), (8192, 2), (4100, 2), (8200, 4), (16384, 4), (12296, 4), (32768, 8),
+             (16392, 8), (32764, 8), (65536, 16), (40968, 16), (65532, 16)]
+
+
+@pytest.mark.parametrize("D,W", WAVE_ROWS)
+def test_ln_waves_per_row(ops, orc, D, W):
+    """The order the library reports for the row (W waves, L = 64 W lanes) is the one the
+    kernels follow, on contiguous rows, padded (strided) rows and misaligned rows."""
+    from modulate_ln_amd import _native as N
+
+    o = N.order_for(N.OP_LN_MODULATE, D)
+    assert (o.W, o.L) == (W, 64 * W)
+    g = torch.Generator().manual_seed(7 * D + W)
+    B, S = 2, 3
+    x = rand_bf16((B, S, D), g, std=2.0, mean=-1.0).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, what="W=%d D=%d" % (W, D))
+    big = rand_bf16((B, S, D + 24), g).to(DEV)
+    run_ln(ops, orc, big[:, :, 8:8 + D], sc, sh, 1e-5, what="padded W=%d D=%d" % (W, D))
+    run_ln(ops, orc, big[:, :, 1:1 + D], sc, sh, 1e-5, what="misaligned W=%d D=%d" % (W, D))
 
 
 @pytest.mark.parametrize("D", [8, 64, 520, 1000, 2240, 3072, 4096, 4104, 8192])
@@ -289,6 +334,31 @@ def test_rga_large_one_shot_ragged(ops, orc):
     assert torch.equal(res.view(torch.int16), ref.view(torch.int16))
 
 
+def device_normal_bf16(shape, seed, std=1.0):
+    """A large seeded normal tensor drawn on the device (the host draw of billions of values
+    would take minutes); the oracle gets the same values back through a copy."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * std).to(torch.bfloat16)
+
+
+def test_rga_row_beyond_2g_elements(ops, orc):
+    """One row of 2^31 + 4096 elements (4 GiB per tensor): the one-shot grid's element offsets
+    pass 2^31, so its indexing must be 64-bit.  The oracle checks the first and the last 8192
+    elements (the op is element-wise with a per-sample gate)."""
+    D = (1 << 31) + 4096
+    res = device_normal_bf16((1, 1, D), 1)
+    upd = device_normal_bf16((1, 1, D), 2)
+    gate = device_normal_bf16((1, D), 3, std=0.5)
+    y = ops.residual_gate_add(res, gate, upd)
+    torch.cuda.synchronize()
+    for lo in (0, D - 8192):
+        sl = slice(lo, lo + 8192)
+        want = orc.residual_gate_add(bits(res[0, :, sl]), bits(gate[:, sl]), bits(upd[0, :, sl]), 1, FP32)
+        assert_bits_equal(bits(y[0, :, sl]), want, "rga beyond 2^31 at %d" % lo)
+    del res, upd, gate, y
+    torch.cuda.empty_cache()
+
+
 def test_rga_inplace_and_views(ops, orc):
     g = torch.Generator().manual_seed(11)
     B, S, D = 2, 17, 3072
@@ -320,7 +390,8 @@ def test_rga_inplace_and_views(ops, orc):
 
 def run_qk(ops, orc, q, k, w, eps, *, what="", q_out=None, k_out=None):
     B, S, H, Dh = q.shape
-    V, L = order(Dh, 16)
+    V, L = order(N_OP_QK, Dh, q)
+    assert order(N_OP_QK, Dh, k) == (V, L)
     wq, bq, wk, bk = w if w is not None else (None, None, None, None)
     qo, ko = ops.qk_head_layernorm(q, k, wq, bq, wk, bk, eps, q_out=q_out, k_out=k_out)
     torch.cuda.synchronize()
@@ -444,7 +515,7 @@ def test_gelu_tails_and_views(ops, orc):
 def oracle_chain_rows(orc, x_rows, embs, b, eps):
     """Oracle chain on a few rows of batch sample b (rows are independent)."""
     D = x_rows.shape[1]
-    V, L = order(D, 64)
+    V, L = order(N_OP_LN, D)
     x = x_rows
     S = x.shape[0]
     for emb in embs:

@@ -14,7 +14,7 @@ import torch
 
 from modulate_ln_amd import workloads as W
 
-from test_gpu_parity import DEV, FP32, assert_bits_equal, bits, order, rand_bf16
+from test_gpu_parity import DEV, FP32, N_OP_LN, assert_bits_equal, bits, order, rand_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def run_fp8(ops, orc, x, sc, sh, eps, qscale, what=""):
     rstd = torch.empty(B * S, dtype=torch.float32, device=DEV)
     y = ops.ln_modulate_fp8(x, sc, sh, q, eps, mean_out=mean, rstd_out=rstd)
     torch.cuda.synchronize()
-    V, L = order(D, 64)
+    V, L = order(N_OP_LN, D, x)
     want, m32, r32 = orc.ln_modulate_fp8(bits(x.contiguous().reshape(B * S, D)), rows2d(sc, B, D), rows2d(sh, B, D),
                                          S, eps, qscale, FP32, V=V, L=L)
     got = y.view(torch.uint8).cpu().numpy().reshape(B * S, D)
@@ -94,11 +94,35 @@ def test_fp8_layouts_and_specials(ops, orc):
     q.fill_(0.25)
     b = ops.ln_modulate_fp8(x2, z, z, q, 1e-6)
     torch.cuda.synchronize()
-    V, L = order(512, 64)
+    V, L = order(N_OP_LN, 512, x2)
     zb = bits(z)
     for got, qs in ((a, 0.5), (b, 0.25)):
         want, _, _ = orc.ln_modulate_fp8(bits(x2.reshape(64, 512)), zb, zb, 64, 1e-6, qs, FP32, V=V, L=L)
         assert np.array_equal(got.view(torch.uint8).cpu().numpy().reshape(64, 512), want)
+
+
+def test_fp8_overflowing_variance_row(ops, orc):
+    """A row whose fp32 m2 overflows (rstd = 1/sqrt(inf) = 0) while its mean stays finite: one
+    element's x - mean is then infinite and its normalized value inf * 0 is NaN, which must reach
+    the FP8 output as NaN (as in the oracle) on the tabled, transposed and gather paths."""
+    g = torch.Generator().manual_seed(97)
+    B, S, D = 1, 8, 512
+    big = 3.3895313892515355e38  # largest finite bf16
+    x = rand_bf16((B, S, D), g)
+    row = torch.zeros(D, dtype=torch.float32)
+    row[0] = big          # lane 0's first element (vector 0)
+    row[256:] = -big      # vectors 32..63: lanes 32..63
+    x[0, 3] = row.to(torch.bfloat16)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    xd = x.to(DEV)
+    y = run_fp8(ops, orc, xd, sc, sh, 1e-6, 0.5, "overflowing m2, tabled")
+    assert ((y.view(torch.uint8)[0, 3, 0] & 0x7F) == 0x7F).item()
+    run_fp8(ops, orc, xd.transpose(1, 2).contiguous().transpose(1, 2), sc, sh, 1e-6, 0.5,
+            "overflowing m2, transposed")
+    pad = torch.zeros((B, S, D + 1), dtype=torch.bfloat16, device=DEV)
+    pad[:, :, 1:] = xd
+    run_fp8(ops, orc, pad[:, :, 1:], sc, sh, 1e-6, 0.5, "overflowing m2, gather")
 
 
 def test_fp8_decodes_within_half_e4m3_ulp_of_bf16_chain(ops):
@@ -120,7 +144,7 @@ def run_fold(ops, orc, x, sc, sh, eps, what=""):
     rstd = torch.empty(B * S, dtype=torch.float32, device=DEV)
     y = ops.ln_modulate_fold(x, sc, sh, eps, mean_out=mean, rstd_out=rstd)
     torch.cuda.synchronize()
-    V, L = order(D, 64)
+    V, L = order(N_OP_LN, D, x)
     want, m32, r32 = orc.ln_modulate_fold(bits(x.contiguous().reshape(B * S, D)), rows2d(sc, B, D),
                                           rows2d(sh, B, D), S, eps, FP32, V=V, L=L)
     assert_bits_equal(bits(y.reshape(B * S, D)), want, "ln_modulate_fold " + what)

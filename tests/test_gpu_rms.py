@@ -1,11 +1,12 @@
 """Parity of the RMSNorm kernels -- rmsnorm_scale_shift and qk_rmsnorm -- with
 the CPU oracle, through the C ABI.
 
-Bar: bit-exact against the oracle's fixed-order fp32 mode (V = 8 when
-D % 8 == 0 else 4; L = 64 lanes per row, 16 per head); the fp32 1/rms of
-each row within 1e-5 relative of the fp64 two-pass mode.  Same shapes and
-layouts as the LayerNorm tests: every kernel family (tabled rows, transposed
-tiles, general rows, streaming rows; heads in flight, general heads).
+Bar: bit-exact against the oracle's fixed-order fp32 mode, run in the order
+the library reports (adaln_order_for: V elements per vector, L = 64 W lanes
+per row, 16 per head); the fp32 1/rms of each row within 1e-5 relative of
+the fp64 two-pass mode.  Same shapes and layouts as the LayerNorm tests:
+every kernel family (tabled rows, transposed tiles, general rows, rows of
+several waves; heads in flight, general heads).
 """
 
 from __future__ import annotations
@@ -16,7 +17,7 @@ import torch
 
 from modulate_ln_amd import workloads as W
 
-from test_gpu_parity import DEV, FP32, FP64, assert_bits_equal, bits, order, rand_bf16
+from test_gpu_parity import DEV, FP32, N_OP_QK_RMS, N_OP_RMS, FP64, assert_bits_equal, bits, order, rand_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +41,7 @@ def run_rms(ops, orc, x_dev, scale_dev, shift_dev, eps, *, out=None, check_fp64=
     sc_b, sh_b = bits(sc.expand(B, D)), bits(sh.expand(B, D))
     y = ops.rmsnorm_scale_shift(x_dev, scale_dev, shift_dev, eps, out=out, rinv_out=rinv)
     torch.cuda.synchronize()
-    V, L = order(D, 64)
+    V, L = order(N_OP_RMS, D, x_dev)
     want, r32 = orc.rmsnorm_scale_shift(x_log, sc_b, sh_b, S, eps, FP32, V=V, L=L)
     assert_bits_equal(bits(y.reshape(B * S, D)), want, "rmsnorm_scale_shift %s" % what)
     assert np.array_equal(rinv.cpu().numpy().astype(np.float64), r32), "rinv " + what
@@ -147,7 +148,8 @@ def test_rms_vs_rocm_eager_tolerance(ops):
 
 def run_qk_rms(ops, orc, q, k, w, eps, *, what="", q_out=None, k_out=None):
     B, S, H, Dh = q.shape
-    V, L = order(Dh, 16)
+    V, L = order(N_OP_QK_RMS, Dh, q)
+    assert order(N_OP_QK_RMS, Dh, k) == (V, L)
     wq, wk = w if w is not None else (None, None)
     qo, ko = ops.qk_rmsnorm(q, k, wq, wk, eps, q_out=q_out, k_out=k_out)
     torch.cuda.synchronize()
