@@ -248,10 +248,11 @@ def main() -> int:
 
 
 def stream_reference(dev, stream, log, nbytes=1 << 30):
-    """The box's streaming ceilings with torch's own kernels on 1 GiB buffers (far past the
-    MALL): write-only (fill), read-only (a float32 sum), and a copy (read + write).  Context for
-    `roofline`: HBM writes run well below the 8 TB/s peak, so a stream that writes as much as it
-    reads tops out near the copy rate."""
+    """Streaming rates of torch's own kernels on 1 GiB buffers (far past the MALL): write-only
+    (fill), a copy (read + write), and torch's float32 sum -- a reduction kernel, reported for
+    context only: it is not a read-only ceiling (plain read-only streams measured 6.6-7.1 TB/s
+    on this part).  Context for `roofline`: HBM writes run well below the 8 TB/s peak, so a
+    stream that writes as much as it reads tops out near the copy rate."""
     import torch
 
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
@@ -272,13 +273,13 @@ def stream_reference(dev, stream, log, nbytes=1 << 30):
 
     out = {"bytes": nbytes}
     for name, fn, moved in (("write_only_fill", lambda: a.fill_(2.0), nbytes),
-                            ("read_only_sum", lambda: a.sum(dtype=torch.float32), nbytes),
+                            ("torch_sum_fp32_reduction", lambda: a.sum(dtype=torch.float32), nbytes),
                             ("copy", lambda: b.copy_(a), 2 * nbytes)):
         ms = ms_per(fn)
         out[name] = {"ms": round(ms, 4), "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
     del a, b
-    log("stream ceilings (1 GiB, torch kernels): write-only %.0f GB/s, read-only %.0f GB/s, copy %.0f GB/s"
-        % (out["write_only_fill"]["GBps"], out["read_only_sum"]["GBps"], out["copy"]["GBps"]))
+    log("torch streams (1 GiB): write-only fill %.0f GB/s, fp32 sum (a reduction) %.0f GB/s, copy %.0f GB/s"
+        % (out["write_only_fill"]["GBps"], out["torch_sum_fp32_reduction"]["GBps"], out["copy"]["GBps"]))
     return out
 
 
@@ -474,6 +475,33 @@ def other_workloads(m, W, dev, stream, log):
     res["residual_gate_add_ln_modulate_1x4096x4096"] = {"us": round(us, 3),
                                                         "GBps": round(fused_bytes(R, D, 1) / us / 1e3, 1)}
     del rs, us_, ros, hs, calls
+
+    # rows longer than 4096 elements (W = 2..16 waves per row) at the same 2^24 elements: D % 8 == 4
+    # (4100, W = 2, V = 4), 16384 (W = 4), 65536 (W = 16); the fused residual update at D = 16384
+    g = torch.Generator().manual_seed(2)
+    for D in (4100, 16384, 65536):
+        S = (1 << 24) // D
+        x = W.normal((1, S, D), g).to(dev)
+        sc = W.normal((1, D), g, std=0.1).to(dev)
+        sh = W.normal((1, D), g, std=0.1).to(dev)
+        nb = rot(lnm_bytes(S, D, 1))
+        xs_ = [x.clone() for _ in range(nb)]
+        outs = [torch.empty_like(x) for _ in range(nb)]
+        calls = [m.ln_modulate(xs_[i], sc, sh, 1e-6, out=outs[i], prepare=True) for i in range(nb)]
+        us = time_loop(calls, 500, stream)
+        res["ln_modulate_1x%dx%d" % (S, D)] = {"us": round(us, 3), "GBps": round(lnm_bytes(S, D, 1) / us / 1e3, 1),
+                                               "waves_per_row": m.order_for(1, D).W}
+        if D == 16384:
+            gate = W.normal((1, D), g, std=0.5).to(dev)
+            ups = [W.normal((1, S, D), g).to(dev)] * nb
+            ros = [torch.empty_like(x) for _ in range(nb)]
+            calls = [m.residual_gate_add_ln_modulate(xs_[i], gate, ups[i], sc, sh, 1e-6, residual_out=ros[i],
+                                                     out=outs[i], prepare=True) for i in range(nb)]
+            us = time_loop(calls, 300, stream)
+            res["residual_gate_add_ln_modulate_1x%dx%d" % (S, D)] = {
+                "us": round(us, 3), "GBps": round(fused_bytes(S, D, 1) / us / 1e3, 1)}
+            del ups, ros
+        del xs_, outs, calls, x
 
     # 20-block DiT chain on (4,4096,3072)
     wl = W.dit_chain()

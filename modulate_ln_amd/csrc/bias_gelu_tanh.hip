@@ -50,16 +50,51 @@ __device__ __forceinline__ float gelu_tanh_f32(float z) {
   return num * __builtin_amdgcn_rcpf(1.0f + e);  // 1 + e in [1, 2]
 }
 
+// The same function in fewer operations, for t >= kFastMinT: sigmoid(2u) =
+// 1 / (1 + 2^-t) directly.  There 2^-t is a normal number (or underflows
+// where the result is z itself) and 1 / (1 + 2^-t) >= 2^-120 stays normal,
+// so no rescaling and no select are needed: one exponential, one add, one
+// reciprocal, one product.  Below kFastMinT (z < -9.4, and -inf) the
+// reciprocal would leave the normal range: gelu_tanh_f32 takes those.
+constexpr float kGeluC0 = 2.302208198144324889f;  // 2 * sqrt(2/pi) * log2(e)
+constexpr float kGeluC1 = 0.102943239580023487f;  // 0.044715 * c0
+constexpr float kFastMinT = -120.0f;
+
+__device__ __forceinline__ float gelu_fast(float z, float t) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+}
+
+// gelu of z given its t: the fast form, or gelu_tanh_f32 below kFastMinT
+__device__ __forceinline__ float gelu_eval(float z, float t) {
+  return t < kFastMinT ? gelu_tanh_f32(z) : gelu_fast(z, t);
+}
+
 template <int V>
 __device__ __forceinline__ Vec<V> bias_gelu_vec(const Vec<V>& xv, const Vec<V>& bv) {
-  Vec<V> o;
+  float z[V], t[V];
+  bool tail = false;
 #pragma unroll
   for (int i = 0; i < V / 2; ++i) {
-    float z0 = lo_f32(xv.w[i]) + lo_f32(bv.w[i]);
-    float z1 = hi_f32(xv.w[i]) + hi_f32(bv.w[i]);
-    round_pair(z0, z1);  // bf16(x + bias)
-    o.w[i] = pack_bf16(gelu_tanh_f32(z0), gelu_tanh_f32(z1));
+    z[2 * i] = lo_f32(xv.w[i]) + lo_f32(bv.w[i]);
+    z[2 * i + 1] = hi_f32(xv.w[i]) + hi_f32(bv.w[i]);
+    round_pair(z[2 * i], z[2 * i + 1]);  // bf16(x + bias)
   }
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    t[e] = z[e] * __builtin_fmaf(z[e] * z[e], kGeluC1, kGeluC0);
+    tail = tail || t[e] < kFastMinT;
+  }
+  float g[V];
+  if (__builtin_amdgcn_ballot_w64(tail) != 0) {  // wave-uniform: a far negative z somewhere
+#pragma unroll
+    for (int e = 0; e < V; ++e) g[e] = gelu_eval(z[e], t[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) g[e] = gelu_fast(z[e], t[e]);
+  }
+  Vec<V> o;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) o.w[i] = pack_bf16(g[2 * i], g[2 * i + 1]);
   return o;
 }
 
@@ -149,7 +184,7 @@ __global__ __launch_bounds__(256) void gelu_rows_scalar(GeluArgs a) {
     uint16_t* orow = a.out + r * a.width;
     for (int64_t j = lane; j < a.width; j += kWave) {
       float z = u16_f32(to_bf16(u16_f32(xr[j]) + u16_f32(a.bias[j])));
-      orow[j] = to_bf16(gelu_tanh_f32(z));
+      orow[j] = to_bf16(gelu_eval(z, z * __builtin_fmaf(z * z, kGeluC1, kGeluC0)));
     }
   }
 }

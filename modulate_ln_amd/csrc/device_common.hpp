@@ -346,6 +346,31 @@ __device__ __forceinline__ uint32_t tail_pair(float n0, float n1, float o0, floa
   }
 }
 
+// The chain's output for one element as the fp32 value of its bf16 (the
+// rounding of x_hat, of x_hat * (1 + scale) and of + shift), for a stage
+// that consumes it in fp32 rather than as packed bf16.
+__device__ __forceinline__ float chain_f32(float n, float o, float h) {
+  return round_f32(round_f32(round_f32(n) * o) + h);
+}
+
+// The FP8 stage for V values y (the chain's output as fp32): q = e4m3(clamp(
+// y * qinv)), packed four bytes per word into q[0 .. V/4); no_nan as below.
+template <int V>
+__device__ __forceinline__ void fp8_stage_f32(const float* y, float qinv, bool no_nan, uint32_t* q) {
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = y[i] * qinv;
+  if (no_nan) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = clamp448_finite(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = clamp448(v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) q[i] = fp8_quad(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
 // The FP8 stage for V/2 bf16 pairs w (the chain's output): q = e4m3(clamp(y *
 // qinv)), packed four bytes per word into q[0 .. V/4).  no_nan: the caller
 // knows no value can be NaN (finite row statistics and finite adaLN rows),

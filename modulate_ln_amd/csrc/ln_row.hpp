@@ -187,6 +187,7 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
       const int v = k * kWave + lane;
       if (UNIF || v < nvec) {
         uint32_t o[V / 2];  // bf16 pairs
+        float y8[TAIL == kTailFp8 ? V : 1];  // FP8: the chain's output as fp32 values
 #pragma unroll
         for (int q = 0; q < V / 4; ++q) {
           float n0, n1, n2, n3;
@@ -202,12 +203,19 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
             n3 = (xval(k, 4 * q + 3) - mean) * rstd;
           }
           // n = rstd * (x - mean), or x * rinv; then the output stage
-          o[2 * q] = tail_pair<TAIL>(n0, n1, oc[q].x, oc[q].y, hc[q].x, hc[q].y);
-          o[2 * q + 1] = tail_pair<TAIL>(n2, n3, oc[q].z, oc[q].w, hc[q].z, hc[q].w);
+          if constexpr (TAIL == kTailFp8) {
+            y8[4 * q] = chain_f32(n0, oc[q].x, hc[q].x);
+            y8[4 * q + 1] = chain_f32(n1, oc[q].y, hc[q].y);
+            y8[4 * q + 2] = chain_f32(n2, oc[q].z, hc[q].z);
+            y8[4 * q + 3] = chain_f32(n3, oc[q].w, hc[q].w);
+          } else {
+            o[2 * q] = tail_pair<TAIL>(n0, n1, oc[q].x, oc[q].y, hc[q].x, hc[q].y);
+            o[2 * q + 1] = tail_pair<TAIL>(n2, n3, oc[q].z, oc[q].w, hc[q].z, hc[q].w);
+          }
         }
         if constexpr (TAIL == kTailFp8) {
           uint32_t q8[V / 4];
-          fp8_stage<V>(o, qinv, NO_NAN, q8);
+          fp8_stage_f32<V>(y8, qinv, NO_NAN, q8);
           store_fp8_nt<V>(static_cast<uint8_t*>(orow) + v * V, q8);
         } else {
           Vec<V> ov;
