@@ -37,7 +37,7 @@ METRIC = "µs/call + achieved HBM GB/s (% of peak), ln_modulate bf16 (1,4096,409
 # while the kernel sources are the ones the counters were taken on
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "ln_modulate_1x4096x4096_traffic.txt")
 TRAFFIC_SOURCES = ["modulate_ln_amd/csrc/ln_modulate.hip", "modulate_ln_amd/csrc/ln_row.hpp",
-                   "modulate_ln_amd/csrc/device_common.hpp"]
+                   "modulate_ln_amd/csrc/mw_row.hpp", "modulate_ln_amd/csrc/device_common.hpp"]
 
 
 def source_sha256(paths) -> str:

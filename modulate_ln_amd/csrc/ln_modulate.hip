@@ -169,6 +169,9 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #ifndef ADALN_TAB_WPB_RMS
 #define ADALN_TAB_WPB_RMS 4
 #endif
+#ifndef ADALN_TAB_WPB_FP8
+#define ADALN_TAB_WPB_FP8 4
+#endif
 #ifndef ADALN_TAB_PF_SHORT
 #define ADALN_TAB_PF_SHORT 0
 #endif
@@ -238,7 +241,7 @@ struct TabShape {
   // the Welford work per element, 11.04 at 4, 11.45 at 16.  The fold keeps
   // its prefetch (11.32 us; 11.66 with one row per wave in 16-wave blocks).
   static constexpr int kWpbLong = TAIL == kTailFold   ? ADALN_TAB_WPB_FOLD
-                                  : TAIL == kTailFp8  ? 4
+                                  : TAIL == kTailFp8  ? ADALN_TAB_WPB_FP8
                                   : RMS               ? ADALN_TAB_WPB_RMS
                                                       : ADALN_TAB_WPB_LN;
   static constexpr int kWpb = (kLong && !kPrefetch && UNIF) ? kWpbLong : 4;
@@ -323,23 +326,19 @@ __global__ __launch_bounds__((TabShape<NV, UNIF, RMS, TAIL>::kWpb * 64)) void ln
 // Transposed input: tokens contiguous (sx_s == 1), hidden elements sx_d apart
 // -- the permuted activations the Sana report describes (实现拆解 §3, the
 // layout copy aten's LayerNorm pays).  A block of 8 waves takes a tile of 8
-// consecutive tokens of one sample.  Thread i loads, for each of its
-// vectors' 8 hidden positions, the 8 tokens as one 16-byte load (so every
-// 128-byte line of the input is read once, by the 8 tiles that share it),
-// transposes the 8x8 bf16 block in registers and writes whole vectors into
-// an LDS tile [token][vector].  Wave w then runs the same per-row routine
-// as the contiguous kernel on token w, reading its row from LDS: identical
-// bits, one HBM read and one HBM write, no layout copy.
+// consecutive tokens of one sample.  Thread i loads hidden positions i,
+// i + 512, ..., each as one 16-byte load of the tile's 8 tokens (so every
+// 128-byte line of the input is read once, by the 8 tiles that share it,
+// and the lanes of a wave read consecutive hidden positions), and scatters
+// the 8 values into an LDS tile [token][hidden].  Wave w then runs the same
+// per-row routine as the contiguous kernel on token w, reading its row from
+// LDS: identical bits, one HBM read and one HBM write, no layout copy.
+// (Measured on MI355X at (2,1024,2240): 10.52 us against 10.70 us when each
+// thread loaded its vector's 8 hidden positions and transposed 8x8 blocks
+// in registers; 4-token tiles (twice the blocks, 8-byte loads) 13.1 us and
+// 16-token tiles 14.5 us in a copy of the same layout.)
 // ---------------------------------------------------------------------------
 constexpr int kTrTokens = 8;
-
-// bytes (lo, hi) of a and bytes (lo, hi) of b -> one word: lo halves or hi halves
-__device__ __forceinline__ uint32_t join_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t join_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
 
 template <int NV, bool UNIF, bool RMS, int TAIL>
 __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sample) {
@@ -359,22 +358,26 @@ __global__ __launch_bounds__(512) void ln_modulate_tr(LnArgs a, int tiles_per_sa
   uint4* xt = reinterpret_cast<uint4*>(smem + 4 * nvec);
 
   const uint16_t* xb = a.x + (int64_t)b * a.sx_b + t0;
-  for (int v = threadIdx.x; v < nvec; v += 512) {
-    uint4 c[V];  // c[j]: tokens t0..t0+7 of hidden position 8v + j
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xt);  // the tile as [token][D] bf16
+  uint4 c[NV];  // c[k]: tokens t0..t0+7 of hidden position threadIdx.x + 512 k
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      u32x4 t = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(xb + (int64_t)(V * v + j) * a.sx_d));
-      c[j] = make_uint4(t[0], t[1], t[2], t[3]);
+  for (int k = 0; k < NV; ++k) {
+    const int h = threadIdx.x + 512 * k;
+    if (h < D) {
+      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb + (int64_t)h * a.sx_d));
+      c[k] = make_uint4(t[0], t[1], t[2], t[3]);
     }
-    // token 2q (+1) lives in the low (high) half of word q of every c[j]
+  }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w0 = (&c[0].x)[q], w1 = (&c[1].x)[q], w2 = (&c[2].x)[q], w3 = (&c[3].x)[q];
-      const uint32_t w4 = (&c[4].x)[q], w5 = (&c[5].x)[q], w6 = (&c[6].x)[q], w7 = (&c[7].x)[q];
-      xt[(2 * q) * nvec + v] = make_uint4(join_lo(w0, w1), join_lo(w2, w3), join_lo(w4, w5), join_lo(w6, w7));
-      xt[(2 * q + 1) * nvec + v] =
-          make_uint4(join_hi(w0, w1), join_hi(w2, w3), join_hi(w4, w5), join_hi(w6, w7));
+  for (int k = 0; k < NV; ++k) {
+    const int h = threadIdx.x + 512 * k;
+    if (h < D) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = (&c[k].x)[q];
+        xs[(2 * q) * D + h] = (uint16_t)(w & 0xffffu);
+        xs[(2 * q + 1) * D + h] = (uint16_t)(w >> 16);
+      }
     }
   }
   const bool fin = build_tables<V>(tab, a.scale + (int64_t)b * a.ssc_b, a.shift + (int64_t)b * a.ssh_b, nvec,

