@@ -13,8 +13,9 @@
  *    pointer is a DEVICE pointer, at least 2-byte aligned.  Strides are in
  *    elements, non-negative.  Outputs are written contiguously (row-major).
  *  - Ownership: the caller owns every buffer.  The library never allocates,
- *    frees or synchronises; it keeps no state between calls, so calls are
- *    reentrant and thread-safe.
+ *    frees or synchronises; it keeps no state between calls (beyond cached
+ *    device attributes, and the caller-owned workspace of ln_modulate_ws),
+ *    so calls are reentrant and thread-safe.
  *  - Execution: each call enqueues its kernel(s) on `stream` (a hipStream_t
  *    passed as void*, NULL = the null stream) and returns at once.
  *  - Errors: 0 = ADALN_OK.  Argument errors are negative codes returned
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 2
+#define ADALN_ABI_VERSION 3
 
 /* status codes */
 #define ADALN_OK 0
@@ -103,6 +104,55 @@ int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, in
 /* 1 if ln_modulate accepts these sizes/strides/dtype (no pointer is read). */
 int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s, int64_t sx_d,
                         int64_t sscale_b, int64_t sshift_b, int dtype);
+
+/*
+ * ln_modulate_ws -- ln_modulate with a workspace: the same operation, the
+ * same arguments and the same bits (the fixed statistics order above, the
+ * eager roundings), faster on the transposed storage of Sana's permuted
+ * activations (prhub report on sglang PR #34015, 实现拆解 §3: the [B,D,S]
+ * layout whose copy aten's LayerNorm pays).
+ *
+ * With sx_s == 1 the rows of x are strided; a 128-byte line then holds 64
+ * consecutive tokens of one hidden position.  This entry point reads such
+ * lines whole: 8 blocks share each 64-token group, each block reading
+ * lanes 8c .. 8c+7 of the order and merging them at offsets 1, 2, 4, then
+ * handing its partial states to the others through `workspace`, where each
+ * block takes them and merges at offsets 8, 16, 32 -- the same tree.
+ *
+ *  workspace        device memory of at least ln_modulate_workspace_size()
+ *                   bytes, 16-byte aligned, ZERO-FILLED before its first use
+ *                   and then left as the calls leave it (every call returns
+ *                   it ready for the next, whatever the shape).  It must not
+ *                   overlap x, scale, shift, out, mean_out or rstd_out
+ *                   (ADALN_ERR_ALIAS), and calls that share one workspace
+ *                   must not run concurrently (their hand-overs would mix).
+ *  workspace_bytes  its size.  NULL or fewer bytes than the shape needs:
+ *                   the call is ln_modulate (no workspace is touched).
+ *  Other arguments, layouts, aliasing and errors: as ln_modulate, plus
+ *  ADALN_ERR_ALIGN (workspace not 16-byte aligned) and ADALN_ERR_ARG
+ *  (workspace_bytes < 0).
+ *
+ * The workspace path runs when sx_s == 1, D % 8 == 0, D <= 4096,
+ * S % 64 == 0, sx_d % 8 == 0, sx_b % 8 == 0 (B > 1), x, scale, shift and
+ * out are 16-byte aligned and the scale/shift row strides are multiples of
+ * 8; any other shape takes ln_modulate's kernels.  Its grid is sized to be
+ * resident on the device at once, and a block that waits too long for
+ * another's state (ADALN_WS_WAIT_US microseconds, default 200, read at each
+ * call; 0 = never wait) recomputes that state from x: same arithmetic,
+ * same bits.
+ */
+int ln_modulate_ws(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                   int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                   int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                   float* rstd_out, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ln_modulate_ws uses for this shape: 8256 per group of
+ * 64 tokens (B * S / 64 groups; group g always uses bytes [8256 g, 8256 g +
+ * 8256), so one workspace sized for the largest shape serves every smaller
+ * one); 0 when the shape never takes the workspace path (or is not accepted
+ * at all).  No pointer is read, no HIP call is made. */
+int64_t ln_modulate_workspace_size(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                   int64_t sx_d);
 
 /*
  * residual_gate_add -- out = residual + gate * update, two eager ops:

@@ -32,12 +32,14 @@ OP_RMSNORM_SCALE_SHIFT = 4
 OP_QK_RMSNORM = 5
 MAP_INTERLEAVED = 1
 FOLD_PAIRWISE = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/adaln.h declares
 EXPORTS = (
     "ln_modulate",
     "ln_modulate_can_use",
+    "ln_modulate_ws",
+    "ln_modulate_workspace_size",
     "residual_gate_add",
     "residual_gate_add_can_use",
     "qk_head_layernorm",
@@ -86,6 +88,9 @@ def lib():
     vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     L.ln_modulate.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp]
     L.ln_modulate_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
+    L.ln_modulate_ws.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp, i64,
+                                 vp]
+    L.ln_modulate_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     L.residual_gate_add.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, i64, i64, i64, ci, vp, vp]
     L.residual_gate_add_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.qk_head_layernorm.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64,
@@ -116,6 +121,7 @@ def lib():
     for name in EXPORTS:
         if name != "adaln_status_str":
             getattr(L, name).restype = ci
+    L.ln_modulate_workspace_size.restype = i64
     if L.adaln_abi_version() != ABI_VERSION:
         raise ImportError("libadaln.so ABI version %d, binding expects %d" % (L.adaln_abi_version(), ABI_VERSION))
     _lib = L

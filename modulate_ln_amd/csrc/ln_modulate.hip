@@ -27,6 +27,11 @@
 // statistics: each lane accumulates fma(x, x, ss) in the same element order,
 // the lanes' sums are added pairwise nearest-first, rinv = 1/sqrt(ss/D +
 // eps), and x_hat = bf16(x * rinv) enters the same modulate tail.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <atomic>
+
 #include <utility>
 
 #include "device_common.hpp"
@@ -468,6 +473,314 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mw(LnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Transposed storage read in whole lines, with a workspace (ln_modulate_ws).
+// A 128-byte line of [B, D, S] storage holds 64 consecutive tokens of one
+// hidden position, so whole-line reads need 64 tokens per block; to keep 256
+// compute units busy the 64 lanes of the fixed order are split over 8
+// blocks: block c of a 64-token group owns lanes 8c .. 8c + 7 of every token
+// (vectors 64k + 8c + j), reads those hidden positions in whole lines, runs
+// the lanes' Welford passes and merges them at offsets 1, 2, 4 -- the first
+// three levels of the one-wave tree.  Every block then takes the 8 blocks'
+// states of its tokens and merges them at offsets 1, 2, 4 -- the tree's
+// levels 8, 16, 32.  Same order, same merges: the bits of ln_modulate.
+//
+// The hand-over needs no fence: each state travels as two 64-bit relaxed
+// atomics (tag | mean, tag | m2; the count is known from D), so a reader
+// that sees the expected tag in a word has that word's value.  The tag is
+// the group's exchange number, kept in one 64-bit word per group
+// (generation << 32 | arrivals): each block arrives with one atomic add,
+// which returns the generation g, and tags with g + 1; the 8th arrival
+// writes generation g + 1 with no arrivals.  After a call every record of
+// the group carries the group's generation, so a record of an earlier call
+// never carries the tag a reader waits for.  Each group's records and word
+// sit in a slab of their own at a fixed place, so this holds whatever
+// shapes used the workspace before, as long as it started zero-filled.
+//
+// The grid is at most what the device holds at once (occupancy x compute
+// units), so the 8 blocks of a group run together; the 8 blocks of a slot
+// take groups slot, slot + nslots, ... .  The wait is bounded all the same:
+// past wait_ticks of the constant-rate clock a thread recomputes the state
+// it is missing from x itself (the same arithmetic, so the same bits).
+// Measured on MI355X against the one-block-per-8-token-tile kernel above,
+// same bits: (2,1024,2240) 8.6 us vs 10.7, (1,4096,4096) 17.5 vs 33.3,
+// (4,4096,3072) 56.9 vs 89.2; the hand-over costs about two device-scope
+// memory latencies (~2.3 us per group).
+// ---------------------------------------------------------------------------
+constexpr int kCoopTokens = 64;  // tokens per group (one 128-byte line per hidden position)
+constexpr int kCoopBlocks = 8;   // blocks per group (8 lanes of the 64 each)
+
+// The workspace: one slab of kCoopSlab bytes per token group, at the same
+// place whatever the shape of the call (so calls of different shapes can
+// share a workspace): [64 tokens][8 blocks] words tag << 32 | mean bits,
+// the same for m2, then the group's word generation << 32 | arrivals (no
+// arrivals between calls).
+constexpr int kCoopRecs = kCoopTokens * kCoopBlocks;  // records per group
+constexpr int64_t kCoopSlab = 2 * kCoopRecs * 8 + 64;  // bytes per group (64-byte aligned slabs)
+constexpr int64_t coop_ws_bytes(int64_t ntg) { return ntg * kCoopSlab; }
+
+// bytes (lo, hi) of a and bytes (lo, hi) of b -> one word: lo halves or hi halves
+__device__ __forceinline__ uint32_t join_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t join_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Lane g's Welford pass over its vectors g, g + 64, ... of one token
+// (element h at xt + h * sx_d), one gathered vector at a time, as a runtime
+// loop: the k-th element's 1/k is the correctly rounded reciprocal, the
+// same value as the compile-time constant of the main pass.
+__device__ __forceinline__ void coop_lane_state(const uint16_t* xt, int64_t sx_d, int nvec, int g, float& mean,
+                                                float& m2, float& n) {
+  mean = 0.0f;
+  m2 = 0.0f;
+  int cnt = 0;
+#pragma unroll 1
+  for (int v = g; v < nvec; v += kWave) {
+    const Vec<8> x = gather_vec<8>(xt + (int64_t)(8 * v) * sx_d, sx_d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xe = (e & 1) ? hi_f32(x.w[e / 2]) : lo_f32(x.w[e / 2]);
+      ++cnt;
+      const float r = __fdiv_rn(1.0f, (float)cnt);
+      const float delta = xe - mean;
+      mean = __builtin_fmaf(delta, r, mean);
+      m2 = __builtin_fmaf(delta, xe - mean, m2);
+    }
+  }
+  n = (float)cnt;
+}
+
+// The state of lanes 8c .. 8c + 7 of one token merged at offsets 1, 2, 4 --
+// the recompute of another block's share when its hand-over is late.  The
+// lanes are taken in turn and merged as a binary counter (after an odd lane
+// its pair, after lane 3 mod 4 its quad, after lane 7 the eight), the lower
+// state first: the same merges in the same order as the lanes' tree, so the
+// same bits.
+__device__ __forceinline__ void coop_group_state(const uint16_t* xt, int64_t sx_d, int nvec, int c, float& mean,
+                                                 float& m2) {
+  float m0 = 0.0f, q0 = 0.0f, n0 = 0.0f;  // pending pair (lane i - 1)
+  float m1 = 0.0f, q1 = 0.0f, n1 = 0.0f;  // pending quad half (lanes i - 3 .. i - 2)
+  float m4 = 0.0f, q4 = 0.0f, n4 = 0.0f;  // lanes 0 .. 3
+  float m = 0.0f, q = 0.0f, n = 0.0f;
+#pragma unroll 1
+  for (int i = 0; i < 8; ++i) {
+    coop_lane_state(xt, sx_d, nvec, 8 * c + i, m, q, n);
+    if (i & 1) {
+      welford_merge(m0, q0, n0, m, q, n);
+      m = m0, q = q0, n = n0;
+      if (i & 2) {
+        welford_merge(m1, q1, n1, m, q, n);
+        m = m1, q = q1, n = n1;
+        if (i & 4) {
+          welford_merge(m4, q4, n4, m, q, n);
+          m = m4, q = q4, n = n4;
+        } else {
+          m4 = m, q4 = q, n4 = n;
+        }
+      } else {
+        m1 = m, q1 = q, n1 = n;
+      }
+    } else {
+      m0 = m, q0 = q, n0 = n;
+    }
+  }
+  mean = m;
+  m2 = q;
+}
+
+template <int NV>
+__global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int groups_per_sample, int ngroups,
+                                                      uint64_t wait_ticks) {
+  constexpr int V = 8;
+  // [step][token][lane of the block ^ (token / 8)]: 16-byte vectors; the xor
+  // spreads the 8 tokens 8 apart that one transpose writes over the banks
+  __shared__ uint4 tile[NV][kCoopTokens][8];
+  __shared__ float4 otab[NV][8][2];  // bf16(1 + scale) of the block's vectors
+  __shared__ float4 htab[NV][8][2];  // shift of the block's vectors
+  __shared__ uint32_t tag_sh;
+  const int D = (int)a.D;
+  const float Df = (float)D;
+  // 8 consecutive blocks form a slot (one block per XCD); a slot takes token
+  // groups slot, slot + nslots, ... (the grid is sized to be resident at once)
+  const int slot = blockIdx.x / kCoopBlocks;
+  const int c = blockIdx.x - slot * kCoopBlocks;
+  const int nslots = gridDim.x / kCoopBlocks;
+
+  for (int tg = slot; tg < ngroups; tg += nslots) {
+    const int b = tg / groups_per_sample;
+    const int t0 = (tg - b * groups_per_sample) * kCoopTokens;
+    const uint16_t* xg = a.x + (int64_t)b * a.sx_b + t0;  // token t0 of hidden position 0
+    uint64_t* mst = reinterpret_cast<uint64_t*>(ws + (int64_t)tg * kCoopSlab);  // the group's slab
+    uint64_t* vst = mst + kCoopRecs;
+    uint64_t* sync = vst + kCoopRecs;
+    if (tg != slot) __syncthreads();  // the previous group's tile, tables and tag have been read
+    // the thread index, hidden stride and vector count, opaque to the compiler
+    // in each group: what derives from them (indices, LDS and memory offsets,
+    // lane counts) is recomputed per group rather than held in registers
+    // across the loop
+    int tid = threadIdx.x;
+    int64_t sx_d = a.sx_d;
+    int nvec = D / V;
+    __asm__ volatile("" : "+v"(tid), "+s"(sx_d), "+s"(nvec));
+
+    // loads: wave 7 first issues the block's adaLN vectors and the arrival
+    // (one atomic add returns the generation and the arrivals before it: the
+    // 8th arrival writes the next generation); then thread (k, j, p) of waves
+    // 0 .. NV - 1 reads the 8 hidden positions of vector 64k + 8c + j for
+    // tokens 8p .. 8p + 7 (a wave's load instruction covers 8 whole lines) and
+    // transposes the 8x8 block.  The arrival's result is first used after the
+    // transposes, so no wait lies between the loads.
+    {
+      const int k = tid >> 6, j = (tid >> 3) & 7, p = tid & 7;
+      const int tl = tid & (kWave - 1), tk = tl >> 3, tj = tl & 7, tv = 64 * tk + 8 * c + tj;
+      const bool tab = k == 7 && tl < NV * 8 && tv < nvec;
+      Vec<V> sv, hv;
+      if (tab) {
+        sv = load_vec<V>(a.scale + (int64_t)b * a.ssc_b + V * tv);
+        hv = load_vec<V>(a.shift + (int64_t)b * a.ssh_b + V * tv);
+      }
+      uint64_t old = 0;
+      if (tid == 7 * kWave) {
+        int z = 0;  // an index the compiler cannot see is zero: a plain one-lane atomic
+        __asm__ volatile("" : "+v"(z));
+        old = __hip_atomic_fetch_add(sync + z, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int v = 64 * k + 8 * c + j;
+      const bool act = k < NV && v < nvec;
+      uint4 cc[V];
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          u32x4 t = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(xg + (int64_t)(V * v + e) * sx_d + 8 * p));
+          cc[e] = make_uint4(t[0], t[1], t[2], t[3]);
+        }
+      }
+      if (act) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = (&cc[0].x)[q], w1 = (&cc[1].x)[q], w2 = (&cc[2].x)[q], w3 = (&cc[3].x)[q];
+          const uint32_t w4 = (&cc[4].x)[q], w5 = (&cc[5].x)[q], w6 = (&cc[6].x)[q], w7 = (&cc[7].x)[q];
+          tile[k][8 * p + 2 * q][j ^ p] =
+              make_uint4(join_lo(w0, w1), join_lo(w2, w3), join_lo(w4, w5), join_lo(w6, w7));
+          tile[k][8 * p + 2 * q + 1][j ^ p] =
+              make_uint4(join_hi(w0, w1), join_hi(w2, w3), join_hi(w4, w5), join_hi(w6, w7));
+        }
+      }
+      if (tab) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
+          float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
+          round_pair(o0, o1);  // bf16(1 + scale)
+          round_pair(o2, o3);
+          otab[tk][tj][q] = make_float4(o0, o1, o2, o3);
+          htab[tk][tj][q] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]), lo_f32(hv.w[2 * q + 1]),
+                                        hi_f32(hv.w[2 * q + 1]));
+        }
+      }
+      __asm__ volatile("" : "+v"(old));  // the arrival's result is first needed here
+      if (tid == 7 * kWave) {
+        const uint32_t g0 = (uint32_t)(old >> 32);
+        if ((uint32_t)old == kCoopBlocks - 1)
+          __hip_atomic_store(sync, (uint64_t)(g0 + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tag_sh = g0 + 1u;
+      }
+    }
+    __syncthreads();
+
+    // thread (t, j): token t, lane 8c + j of the order; the 8 lanes of a token are adjacent
+    const int t = tid >> 3, j = tid & 7, lane = tid & (kWave - 1);
+    const int g = 8 * c + j;
+    const int col = j ^ (t >> 3);
+    float mean = 0.0f, m2 = 0.0f;
+    {
+      Vec<V> buf[NV];  // live for the pass only: the output re-reads the tile
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (64 * k + g < nvec) {
+          const uint4 w = tile[k][t][col];
+          buf[k].w[0] = w.x;
+          buf[k].w[1] = w.y;
+          buf[k].w[2] = w.z;
+          buf[k].w[3] = w.w;
+        }
+      lane_stats<V, false>(buf, nvec, g, kWave, mean, m2, std::make_integer_sequence<int, NV>{});
+    }
+    float n = (float)((nvec > g ? (nvec - g + kWave - 1) / kWave : 0) * V);
+    merge_level<1>(mean, m2, n, lane);
+    merge_level<2>(mean, m2, n, lane);
+    merge_level<4>(mean, m2, n, lane);  // every lane of the token: the state of lanes 8c .. 8c + 7
+
+    // hand the state over, take the 8 blocks' states of token t (block j's in lane j)
+    const uint64_t tag = (uint64_t)tag_sh << 32;
+    const int ri = t * kCoopBlocks;
+    if (j == 0) {
+      __hip_atomic_store(mst + ri + c, tag | __builtin_bit_cast(uint32_t, mean), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(vst + ri + c, tag | __builtin_bit_cast(uint32_t, m2), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    n = 0.0f;  // elements of lanes 8j .. 8j + 7: whole numbers, exact in any order
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gi = 8 * j + i;
+      n += (float)((nvec > gi ? (nvec - gi + kWave - 1) / kWave : 0) * V);
+    }
+    if (j != c) {
+      // poll both words (each wave's 64 pairs are 512 contiguous bytes twice)
+      const uint64_t deadline = wall_clock64() + wait_ticks;
+      uint64_t w0, w1;
+      bool ok;
+      while (true) {
+        w0 = __hip_atomic_load(mst + ri + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w1 = __hip_atomic_load(vst + ri + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = (w0 & ~0xffffffffull) == tag && (w1 & ~0xffffffffull) == tag;
+        if (ok || wall_clock64() > deadline) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (ok) {
+        mean = __builtin_bit_cast(float, (uint32_t)w0);
+        m2 = __builtin_bit_cast(float, (uint32_t)w1);
+      } else {
+        coop_group_state(xg + t, sx_d, nvec, j, mean, m2);
+      }
+    }
+    merge_level<1>(mean, m2, n, lane);  // the tree's levels 8, 16, 32: the row's state in every lane
+    merge_level<2>(mean, m2, n, lane);
+    merge_level<4>(mean, m2, n, lane);
+    const float rstd = finalize_rstd(m2, Df, a.eps, pow2_inverse_f(Df));
+    const int64_t r = (int64_t)b * a.S + t0 + t;
+    if (c == 0 && j == 0) {
+      if (a.mean_out) a.mean_out[r] = mean;
+      if (a.rstd_out) a.rstd_out[r] = rstd;
+    }
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + r * D;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int v = 64 * k + g;
+      if (v < nvec) {
+        const uint4 xw = tile[k][t][col];
+        const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
+        Vec<V> ov;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4 o = otab[k][j][q], h = htab[k][j][q];
+          const float n0 = (lo_f32(xs[2 * q]) - mean) * rstd;
+          const float n1 = (hi_f32(xs[2 * q]) - mean) * rstd;
+          const float n2 = (lo_f32(xs[2 * q + 1]) - mean) * rstd;
+          const float n3 = (hi_f32(xs[2 * q + 1]) - mean) * rstd;
+          ov.w[2 * q] = tail_pair<kTailChain>(n0, n1, o.x, o.y, h.x, h.y);
+          ov.w[2 * q + 1] = tail_pair<kTailChain>(n2, n3, o.z, o.w, h.z, h.w);
+        }
+        store_vec_nt<V>(orow + V * v, ov);
+      }
+    }
+  }
+}
+
 constexpr int kRowsPerBlock = 4;
 constexpr int64_t kMaxBlocks = (int64_t)1 << 20;
 
@@ -604,6 +917,76 @@ int dispatch(const LnArgs& a, hipStream_t st) {
   return ADALN_ERR_TOO_LARGE;  // not reached: W == 1 rows hold at most 64 elements per lane
 }
 
+// whole 64-token groups of transposed storage, 16-byte runs, one wave per row
+inline bool coop_shape_ok(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s, int64_t sx_d) {
+  return sx_s == 1 && D % 8 == 0 && D <= kTrMaxD && S % kCoopTokens == 0 && sx_d % 8 == 0 &&
+         (B <= 1 || sx_b % 8 == 0) && B * (S / kCoopTokens) * kCoopBlocks < INT32_MAX;
+}
+
+constexpr int kMaxDevices = 64;  // device ordinals with cached launch attributes
+
+// How long a thread waits for another block's state before recomputing it
+// from x itself: ADALN_WS_WAIT_US microseconds (default 200; 0 recomputes
+// every state), in ticks of the device's constant-rate clock.
+inline uint64_t coop_wait_ticks(int dev) {
+  static std::atomic<int> rate_khz[kMaxDevices];
+  int khz = dev >= 0 && dev < kMaxDevices ? rate_khz[dev].load(std::memory_order_relaxed) : 0;
+  if (khz <= 0) {
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+    if (dev >= 0 && dev < kMaxDevices) rate_khz[dev].store(khz, std::memory_order_relaxed);
+  }
+  long us = 200;
+  const char* e = getenv("ADALN_WS_WAIT_US");
+  if (e && *e) us = std::max(0L, std::min(strtol(e, nullptr, 10), 10000000L));
+  return (uint64_t)us * (uint64_t)khz / 1000u;
+}
+
+// Blocks of ln_modulate_trc<NV> resident at once on the device (cached per
+// device): the grid never exceeds it, so the 8 blocks of a slot run together.
+template <int NV>
+int coop_resident_blocks(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  int v = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV>, 512, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = per_cu * cus;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int NV>
+int launch_trc(const LnArgs& a, void* ws, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ADALN_ERR_HIP;
+  const int64_t groups_per_sample = a.S / kCoopTokens;
+  const int64_t ntg = (a.R / a.S) * groups_per_sample;
+  const int64_t slots = coop_resident_blocks<NV>(dev) / kCoopBlocks;
+  if (slots < 1) return ADALN_ERR_HIP;
+  const unsigned grid = (unsigned)(std::min(ntg, slots) * kCoopBlocks);
+  hipLaunchKernelGGL((ln_modulate_trc<NV>), dim3(grid), dim3(512), 0, st, a, static_cast<char*>(ws),
+                     (int)groups_per_sample, (int)ntg,
+                     coop_wait_ticks(dev));
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+int dispatch_trc(const LnArgs& a, void* ws, hipStream_t st) {
+  const int64_t nv = (a.D / 8 + kWave - 1) / kWave;
+  switch (nv) {
+    case 1: return launch_trc<1>(a, ws, st);
+    case 2: return launch_trc<2>(a, ws, st);
+    case 3: return launch_trc<3>(a, ws, st);
+    case 4: return launch_trc<4>(a, ws, st);
+    case 5: return launch_trc<5>(a, ws, st);
+    case 6: return launch_trc<6>(a, ws, st);
+    case 7: return launch_trc<7>(a, ws, st);
+    case 8: return launch_trc<8>(a, ws, st);
+    default: return ADALN_ERR_TOO_LARGE;  // not reached: coop_shape_ok bounds D
+  }
+}
+
 }  // namespace
 
 // Shape/stride/dtype acceptance shared by the entry point and its predicate.
@@ -630,7 +1013,8 @@ template <bool RMS, int TAIL>
 static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
                          int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
                          int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
-                         float* rstd_out, const float* qscale, void* stream) {
+                         float* rstd_out, const float* qscale, void* stream, void* ws = nullptr,
+                         int64_t ws_bytes = 0) {
   constexpr bool kFp8 = TAIL == kTailFp8;
   int rc = ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype);
   if (rc != ADALN_OK) return rc;
@@ -659,6 +1043,13 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   for (const Span* t : {&so, &sx, &ssc, &ssh, &sq})
     if (overlaps(sm, *t) || overlaps(sr, *t)) return ADALN_ERR_ALIAS;
   if (overlaps(sm, sr)) return ADALN_ERR_ALIAS;
+  if (ws_bytes < 0) return ADALN_ERR_ARG;
+  if (ws) {
+    if (!aligned(ws, 16)) return ADALN_ERR_ALIGN;
+    const Span sw = Span{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)ws_bytes};
+    for (const Span* t : {&so, &sx, &ssc, &ssh, &sq, &sm, &sr})
+      if (overlaps(sw, *t)) return ADALN_ERR_ALIAS;
+  }
 
   LnArgs a;
   a.x = (const uint16_t*)x;
@@ -694,6 +1085,13 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   // the tabled fast path indexes rows, samples and offsets in 32 bits
   const bool tab = vec && S <= INT32_MAX / 4 && B <= INT32_MAX;
   if (tab) return V == 8 ? dispatch_tab<8, RMS, TAIL>(a, st) : dispatch_tab<4, RMS, TAIL>(a, st);
+  // transposed storage with a workspace: whole lines, 8 blocks per 64-token group
+  if constexpr (!RMS && TAIL == kTailChain) {
+    if (ws && coop_shape_ok(B, S, D, sx_b, sx_s, sx_d) && ws_bytes >= coop_ws_bytes(B * (S / kCoopTokens)) &&
+        aligned(x, 16) && aligned(scale, 16) && aligned(shift, 16) && aligned(out, 16) &&
+        stride_ok(B, sscale_b) && stride_ok(B, sshift_b))
+      return dispatch_trc(a, ws, st);
+  }
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
                   B * (S / kTrTokens) < INT32_MAX && aligned(x, 16) && sx_d % 8 == 0 &&
@@ -719,6 +1117,22 @@ extern "C" int ln_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64
                            float* mean_out, float* rstd_out, void* stream) {
   return norm_modulate<false, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
                                           eps, dtype, out, mean_out, rstd_out, nullptr, stream);
+}
+
+extern "C" int64_t ln_modulate_workspace_size(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                              int64_t sx_d) {
+  if (ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, 0, 0, ADALN_BF16) != ADALN_OK) return 0;
+  if (B * S == 0 || !coop_shape_ok(B, S, D, sx_b, sx_s, sx_d)) return 0;
+  return coop_ws_bytes(B * (S / kCoopTokens));
+}
+
+extern "C" int ln_modulate_ws(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                              int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                              int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                              float* rstd_out, void* workspace, int64_t workspace_bytes, void* stream) {
+  return norm_modulate<false, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
+                                          eps, dtype, out, mean_out, rstd_out, nullptr, stream, workspace,
+                                          workspace_bytes);
 }
 
 extern "C" int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b,

@@ -66,10 +66,29 @@ def _rows_view(t: torch.Tensor, B: int, D: int, name: str):
     return t, sb
 
 
+def ln_modulate_workspace_size(x: torch.Tensor) -> int:
+    """Bytes of workspace ln_modulate(..., workspace=...) uses for x's shape and strides
+    (0 when that shape never takes the workspace path)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D], got %s" % (tuple(x.shape),))
+    B, S, D = x.shape
+    return int(N.lib().ln_modulate_workspace_size(B, S, D, x.stride(0), x.stride(1), x.stride(2)))
+
+
+def ln_modulate_workspace(x: torch.Tensor, nbytes: int | None = None) -> torch.Tensor:
+    """A zero-filled uint8 workspace on x's device, large enough for x (or nbytes); reuse it
+    across calls (the calls leave it ready), one workspace per concurrently running call."""
+    n = ln_modulate_workspace_size(x) if nbytes is None else int(nbytes)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=x.device)
+
+
 def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
                 out: torch.Tensor | None = None, mean_out: torch.Tensor | None = None,
-                rstd_out: torch.Tensor | None = None, stream=None, prepare: bool = False):
-    """LN(x) * (1 + scale) + shift with every eager bf16 rounding (x: [B,S,D], any strides)."""
+                rstd_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+                prepare: bool = False):
+    """LN(x) * (1 + scale) + shift with every eager bf16 rounding (x: [B,S,D], any strides).
+    With `workspace` (from ln_modulate_workspace) the call goes through ln_modulate_ws: the
+    same bits, whole-line reads of transposed storage."""
     _require(x, "x")
     _require(scale, "scale")
     _require(shift, "shift")
@@ -89,12 +108,20 @@ def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: 
                               or t.device != x.device):
             raise ValueError("%s must be a contiguous float32 tensor of B*S elements on x's device" % name)
     st = _stream_handle(x, stream)
-    call = Prepared("ln_modulate", N.lib().ln_modulate, (
-        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
-        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
-        mean_out.data_ptr() if mean_out is not None else None,
-        rstd_out.data_ptr() if rstd_out is not None else None, st), out,
-        keep=(x, scale, shift, out, mean_out, rstd_out))
+    args = (x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+            scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
+            mean_out.data_ptr() if mean_out is not None else None,
+            rstd_out.data_ptr() if rstd_out is not None else None)
+    if workspace is None:
+        call = Prepared("ln_modulate", N.lib().ln_modulate, args + (st,), out,
+                        keep=(x, scale, shift, out, mean_out, rstd_out))
+    else:
+        if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+                or not workspace.is_contiguous() or workspace.device != x.device):
+            raise ValueError("workspace must be a contiguous uint8 tensor on x's device (ln_modulate_workspace)")
+        call = Prepared("ln_modulate_ws", N.lib().ln_modulate_ws,
+                        args + (workspace.data_ptr(), workspace.numel(), st), out,
+                        keep=(x, scale, shift, out, mean_out, rstd_out, workspace))
     return call if prepare else call()
 
 

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.adaln_abi_version() == N.ABI_VERSION == 2
+    assert L.adaln_abi_version() == N.ABI_VERSION == 3
     codes = [N.OK, N.ERR_NULL, N.ERR_SHAPE, N.ERR_DTYPE, N.ERR_ALIGN, N.ERR_ALIAS, N.ERR_TOO_LARGE,
              N.ERR_STRIDE, N.ERR_HIP, N.ERR_ARG]
     names = [N.status_str(c) for c in codes]
@@ -168,6 +168,60 @@ def test_ln_modulate_rejections(L):
     # an empty problem is a successful no-op even with NULL pointers
     assert lnm(L, x=None, scale=None, shift=None, out=None, B=0) == N.OK
     assert lnm(L, x=None, scale=None, shift=None, out=None, S=0) == N.OK
+
+
+def lnw(L, ws=P4 + 0x1000000, wsb=1 << 20, **kw):
+    """ln_modulate_ws with ln_modulate's arguments (lnm's defaults) and a workspace."""
+    a = dict(x=P0, B=1, S=4, D=8, sx=None, scale=P1, ssc=8, shift=P2, ssh=8, eps=1e-6, dtype=N.BF16, out=P3,
+             mean=None, rstd=None)
+    a.update(kw)
+    S, D = a["S"], a["D"]
+    sx_b, sx_s, sx_d = a["sx"] if a["sx"] is not None else (S * D, D, 1)
+    return L.ln_modulate_ws(a["x"], a["B"], S, D, sx_b, sx_s, sx_d, a["scale"], a["ssc"], a["shift"], a["ssh"],
+                            a["eps"], a["dtype"], a["out"], a["mean"], a["rstd"], ws, wsb, None)
+
+
+def test_ln_modulate_ws_rejections(L):
+    # every ln_modulate rejection holds
+    assert lnw(L, dtype=2) == N.ERR_DTYPE
+    assert lnw(L, D=6) == N.ERR_SHAPE
+    assert lnw(L, D=65540) == N.ERR_TOO_LARGE
+    assert lnw(L, sx=(32, -8, 1)) == N.ERR_STRIDE
+    assert lnw(L, eps=-1.0) == N.ERR_ARG
+    assert lnw(L, x=None) == N.ERR_NULL
+    assert lnw(L, x=P0 + 1) == N.ERR_ALIGN
+    assert lnw(L, out=P0 + 16) == N.ERR_ALIAS
+    # the workspace: 16-byte aligned, a non-negative size, overlapping no tensor
+    assert lnw(L, ws=P4 + 0x1000008) == N.ERR_ALIGN
+    assert lnw(L, wsb=-1) == N.ERR_ARG
+    assert lnw(L, ws=P0 - 64, wsb=128) == N.ERR_ALIAS  # over x
+    assert lnw(L, ws=P3 + 16, wsb=64) == N.ERR_ALIAS  # over out
+    assert lnw(L, ws=P2, wsb=16) == N.ERR_ALIAS  # over shift
+    assert lnw(L, ws=P4, wsb=64, mean=P4 + 32) == N.ERR_ALIAS  # over the statistics
+    # an empty problem is a successful no-op
+    assert lnw(L, x=None, scale=None, shift=None, out=None, B=0) == N.OK
+
+
+def test_ln_modulate_workspace_size(L):
+    def size(B, S, D, sx=None):
+        sx_b, sx_s, sx_d = sx if sx is not None else (D * S, 1, S)  # transposed storage
+        return L.ln_modulate_workspace_size(B, S, D, sx_b, sx_s, sx_d)
+
+    group = 64 * 8 * 16 + 64  # 64 tokens x 8 blocks x (mean, m2) words + the group's word, 64-byte slabs
+    assert group == 8256
+    assert size(2, 1024, 2240) == 32 * group
+    assert size(1, 4096, 4096) == 64 * group
+    assert size(3, 64, 8) == 3 * group
+    assert size(2, 1024, 2240, sx=(2240 * 1088, 1, 1088)) == 32 * group  # padded token rows
+    # shapes that never take the workspace path
+    assert size(1, 4096, 4096, sx=(4096 * 4096, 4096, 1)) == 0  # contiguous rows
+    assert size(2, 96, 512) == 0  # S % 64 != 0
+    assert size(1, 128, 516) == 0  # D % 8 != 0
+    assert size(1, 64, 4104) == 0  # D > 4096
+    assert size(1, 128, 512, sx=(512 * 132, 1, 132)) == 0  # token rows not 16-byte multiples
+    assert size(2, 128, 512, sx=(512 * 128 + 4, 1, 128)) == 0  # sample stride not 16-byte multiples
+    assert size(0, 64, 512) == 0  # empty
+    assert size(1, 64, 6) == 0  # rejected shape
 
 
 def test_residual_gate_add_rejections(L):
