@@ -146,6 +146,28 @@ int ln_modulate_ws(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b,
                    int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
                    float* rstd_out, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * ln_modulate_noalloc -- ln_modulate_ws whose workspace is a fixed array of
+ * device memory inside the library, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The call itself allocates nothing and frees nothing.
+ *
+ * Same arguments, bits, layouts and errors as ln_modulate; the shapes that
+ * take the workspace path (see ln_modulate_ws) use the library's array of
+ * 8454144 bytes = 1024 groups of 64 tokens, so B * S beyond 65536 tokens on
+ * that path is ADALN_ERR_TOO_LARGE (returned before any HIP call); other
+ * shapes run ln_modulate's kernels and need no array.  Each device the
+ * library runs on holds its own array from its first call there until the
+ * process ends (its address is looked up once per device, with that device
+ * current); every call on a device shares that device's array and leaves it
+ * ready for the next call, so calls on one device must be ordered (one
+ * stream, or events): calls that overlap on one device race.
+ */
+int ln_modulate_noalloc(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                        int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                        int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                        float* rstd_out, void* stream);
+
 /* Bytes of workspace ln_modulate_ws uses for this shape: 8256 per group of
  * 64 tokens (B * S / 64 groups; group g always uses bytes [8256 g, 8256 g +
  * 8256), so one workspace sized for the largest shape serves every smaller

@@ -40,6 +40,7 @@ EXPORTS = (
     "ln_modulate_can_use",
     "ln_modulate_ws",
     "ln_modulate_workspace_size",
+    "ln_modulate_noalloc",
     "residual_gate_add",
     "residual_gate_add_can_use",
     "qk_head_layernorm",
@@ -91,6 +92,7 @@ def lib():
     L.ln_modulate_ws.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp, i64,
                                  vp]
     L.ln_modulate_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
+    L.ln_modulate_noalloc.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, i64, f32, ci, vp, vp, vp, vp]
     L.residual_gate_add.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, i64, i64, i64, ci, vp, vp]
     L.residual_gate_add_can_use.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, ci]
     L.qk_head_layernorm.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, i64, i64,

@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include <utility>
 
@@ -957,10 +958,15 @@ int coop_resident_blocks(int dev) {
   return v;
 }
 
+// the device a stream belongs to (the current device for the null stream)
+inline hipError_t stream_device(hipStream_t st, int* dev) {
+  return st == nullptr ? hipGetDevice(dev) : hipStreamGetDevice(st, dev);
+}
+
 template <int NV>
 int launch_trc(const LnArgs& a, void* ws, hipStream_t st) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ADALN_ERR_HIP;
+  if (stream_device(st, &dev) != hipSuccess) return ADALN_ERR_HIP;
   const int64_t groups_per_sample = a.S / kCoopTokens;
   const int64_t ntg = (a.R / a.S) * groups_per_sample;
   const int64_t slots = coop_resident_blocks<NV>(dev) / kCoopBlocks;
@@ -985,6 +991,44 @@ int dispatch_trc(const LnArgs& a, void* ws, hipStream_t st) {
     case 8: return launch_trc<8>(a, ws, st);
     default: return ADALN_ERR_TOO_LARGE;  // not reached: coop_shape_ok bounds D
   }
+}
+
+// ---------------------------------------------------------------------------
+// The workspace of ln_modulate_noalloc: a fixed array of device memory, for
+// callers that cannot allocate (each device the library runs on holds its
+// own copy until the process ends; device globals start zero-filled, which
+// is the state the hand-over protocol starts from, and every call leaves it
+// ready for the next).  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels get the address hipGetSymbolAddress
+// returns for the device, looked up once per device with it current.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchGroups = 1024;  // 65536 tokens of transposed storage
+constexpr int64_t kScratchBytes = kScratchGroups * kCoopSlab;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_address(hipStream_t st, void** out) {
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex lookup;
+  int dev = 0;
+  if (stream_device(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ADALN_ERR_HIP;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> hold(lookup);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      if (hipGetDevice(&cur) != hipSuccess) return ADALN_ERR_HIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return ADALN_ERR_HIP;
+      void* q = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return ADALN_ERR_HIP;
+      if (e != hipSuccess || q == nullptr) return ADALN_ERR_HIP;
+      addr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return ADALN_OK;
 }
 
 }  // namespace
@@ -1014,7 +1058,7 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
                          int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
                          int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
                          float* rstd_out, const float* qscale, void* stream, void* ws = nullptr,
-                         int64_t ws_bytes = 0) {
+                         int64_t ws_bytes = 0, bool lib_scratch = false) {
   constexpr bool kFp8 = TAIL == kTailFp8;
   int rc = ln_modulate_check_shape(B, S, D, sx_b, sx_s, sx_d, sscale_b, sshift_b, dtype);
   if (rc != ADALN_OK) return rc;
@@ -1085,12 +1129,20 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   // the tabled fast path indexes rows, samples and offsets in 32 bits
   const bool tab = vec && S <= INT32_MAX / 4 && B <= INT32_MAX;
   if (tab) return V == 8 ? dispatch_tab<8, RMS, TAIL>(a, st) : dispatch_tab<4, RMS, TAIL>(a, st);
-  // transposed storage with a workspace: whole lines, 8 blocks per 64-token group
+  // transposed storage with a workspace (the caller's, or the library's
+  // scratch): whole lines, 8 blocks per 64-token group
   if constexpr (!RMS && TAIL == kTailChain) {
-    if (ws && coop_shape_ok(B, S, D, sx_b, sx_s, sx_d) && ws_bytes >= coop_ws_bytes(B * (S / kCoopTokens)) &&
-        aligned(x, 16) && aligned(scale, 16) && aligned(shift, 16) && aligned(out, 16) &&
-        stride_ok(B, sscale_b) && stride_ok(B, sshift_b))
-      return dispatch_trc(a, ws, st);
+    if ((ws || lib_scratch) && coop_shape_ok(B, S, D, sx_b, sx_s, sx_d) && aligned(x, 16) && aligned(scale, 16) &&
+        aligned(shift, 16) && aligned(out, 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b)) {
+      const int64_t need = coop_ws_bytes(B * (S / kCoopTokens));
+      if (lib_scratch) {
+        if (need > kScratchBytes) return ADALN_ERR_TOO_LARGE;
+        void* p = nullptr;
+        rc = scratch_address(st, &p);
+        return rc != ADALN_OK ? rc : dispatch_trc(a, p, st);
+      }
+      if (ws_bytes >= need) return dispatch_trc(a, ws, st);
+    }
   }
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
@@ -1133,6 +1185,14 @@ extern "C" int ln_modulate_ws(const void* x, int64_t B, int64_t S, int64_t D, in
   return norm_modulate<false, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
                                           eps, dtype, out, mean_out, rstd_out, nullptr, stream, workspace,
                                           workspace_bytes);
+}
+
+extern "C" int ln_modulate_noalloc(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
+                                   int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,
+                                   int64_t sshift_b, float eps, int dtype, void* out, float* mean_out,
+                                   float* rstd_out, void* stream) {
+  return norm_modulate<false, kTailChain>(x, B, S, D, sx_b, sx_s, sx_d, scale, sscale_b, shift, sshift_b,
+                                          eps, dtype, out, mean_out, rstd_out, nullptr, stream, nullptr, 0, true);
 }
 
 extern "C" int rmsnorm_scale_shift_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b,

@@ -202,6 +202,27 @@ def test_ln_modulate_ws_rejections(L):
     assert lnw(L, x=None, scale=None, shift=None, out=None, B=0) == N.OK
 
 
+def test_ln_modulate_noalloc_rejections(L):
+    def lna(**kw):
+        a = dict(x=P0, B=1, S=4, D=8, sx=None, scale=P1, ssc=8, shift=P2, ssh=8, eps=1e-6, dtype=N.BF16, out=P3,
+                 mean=None, rstd=None)
+        a.update(kw)
+        S, D = a["S"], a["D"]
+        sx_b, sx_s, sx_d = a["sx"] if a["sx"] is not None else (S * D, D, 1)
+        return L.ln_modulate_noalloc(a["x"], a["B"], S, D, sx_b, sx_s, sx_d, a["scale"], a["ssc"], a["shift"],
+                                     a["ssh"], a["eps"], a["dtype"], a["out"], a["mean"], a["rstd"], None)
+
+    assert lna(dtype=2) == N.ERR_DTYPE
+    assert lna(D=6) == N.ERR_SHAPE
+    assert lna(x=None) == N.ERR_NULL
+    assert lna(x=P0 + 1) == N.ERR_ALIGN
+    assert lna(out=P0 + 16) == N.ERR_ALIAS
+    # transposed storage beyond the library's array (1024 groups of 64 tokens), before any HIP call
+    assert lna(S=65600, D=8, sx=(8 * 65600, 1, 65600)) == N.ERR_TOO_LARGE
+    assert lna(B=2, S=32832, D=8, sx=(8 * 32832, 1, 32832)) == N.ERR_TOO_LARGE
+    assert lna(x=None, scale=None, shift=None, out=None, B=0) == N.OK
+
+
 def test_ln_modulate_workspace_size(L):
     def size(B, S, D, sx=None):
         sx_b, sx_s, sx_d = sx if sx is not None else (D * S, 1, S)  # transposed storage
