@@ -338,11 +338,35 @@ def other_workloads(m, W, dev, stream, log):
     b = lnm_bytes(2048, 2240, 2)
     res["ln_modulate_2x1024x2240_transposed"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
                                                   "pages_H200_us": 14.3}
+    # the same calls with a workspace (ln_modulate_ws: whole-line reads, 8 blocks per 64 tokens)
+    ws = m.ln_modulate_workspace(xts[0].transpose(1, 2))
+    calls = [m.ln_modulate(xts[i].transpose(1, 2), emb[:, 5], emb[:, 0], 1e-6, out=outs[i], workspace=ws,
+                           prepare=True) for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["ln_modulate_2x1024x2240_transposed_ws"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                                                     "pages_H200_us": 14.3}
     xcs = [xt.transpose(1, 2).contiguous() for _ in range(nb)]
     calls = [m.ln_modulate(xcs[i], emb[:, 5], emb[:, 0], 1e-6, out=outs[i], prepare=True) for i in range(nb)]
     us = time_loop(calls, 500, stream)
     res["ln_modulate_2x1024x2240_contiguous"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
     del xts, xcs, outs
+
+    # (1,4096,4096) stored transposed, with and without a workspace
+    g = torch.Generator().manual_seed(4096)
+    xt = W.normal((1, 4096, 4096), g).to(dev)
+    sc = W.normal((1, 4096), g, std=0.1).to(dev)
+    sh = W.normal((1, 4096), g, std=0.1).to(dev)
+    nb = rot(2 * xt.numel() * 2)
+    xts = [xt.clone() for _ in range(nb)]
+    outs = [torch.empty(1, 4096, 4096, dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    ws = m.ln_modulate_workspace(xt.transpose(1, 2))
+    b = lnm_bytes(4096, 4096, 1)
+    for tag, w in (("", None), ("_ws", ws)):
+        calls = [m.ln_modulate(xts[i].transpose(1, 2), sc, sh, 1e-6, out=outs[i], workspace=w, prepare=True)
+                 for i in range(nb)]
+        us = time_loop(calls, 300, stream)
+        res["ln_modulate_1x4096x4096_transposed" + tag] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
+    del xts, outs, calls
 
     # GLM-Image q/k heads (1,4360,32,128)
     wl = W.glm_qk()
