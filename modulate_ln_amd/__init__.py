@@ -4,7 +4,7 @@ kernels (``libadaln.so``) and this thin torch binding.
     from modulate_ln_amd import ln_modulate, residual_gate_add, qk_head_layernorm, bias_gelu_tanh
     from modulate_ln_amd import residual_gate_add_ln_modulate, rmsnorm_scale_shift, qk_rmsnorm
     from modulate_ln_amd import modulate_scale_shift, temb_table_slices, ln_modulate_fold, ln_modulate_fp8
-    from modulate_ln_amd import ln_modulate_workspace  # ln_modulate(..., workspace=ws)
+    from modulate_ln_amd import ln_modulate_workspace, ln_modulate_noalloc  # transposed x
 
 The binding only marshals arguments; torch provides device memory and
 streams.  Importing the package does not load the library; the first call
@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     ln_modulate,
     ln_modulate_fold,
     ln_modulate_fp8,
+    ln_modulate_noalloc,
     ln_modulate_workspace,
     ln_modulate_workspace_size,
     modulate_scale_shift,
@@ -32,6 +33,7 @@ __all__ = [
     "ln_modulate",
     "ln_modulate_workspace",
     "ln_modulate_workspace_size",
+    "ln_modulate_noalloc",
     "residual_gate_add",
     "residual_gate_add_ln_modulate",
     "rmsnorm_scale_shift",

@@ -162,8 +162,10 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // once, one row per wave and four waves per SIMD, with the fp32 copy (108
 // VGPRs): their VALU work per row is what the last waves to get their data
 // wait on, and a prefetched second row costs the fp32 copy (two waves per
-// SIMD would remain).  The FP8 stage keeps the prefetch at two blocks per
-// compute unit, the fold at three.  Shorter rows keep one buffer and an fp32
+// SIMD would remain).  The FP8 stage runs every row in flight too, but
+// re-widens x (an fp32 copy would spill at 128 VGPRs): 13.23 us against
+// 13.40 with the prefetch at two blocks per compute unit (15.66 at three).
+// The fold keeps the prefetch at three blocks per compute unit.  Shorter rows keep one buffer and an fp32
 // copy of x at five blocks per compute unit; longer rows (up to 16 vectors
 // per lane, 64 KiB of tables) keep one buffer and re-widen.
 #ifndef ADALN_TAB_WPB_LN
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #define ADALN_TAB_WPB_RMS 4
 #endif
 #ifndef ADALN_TAB_WPB_FP8
-#define ADALN_TAB_WPB_FP8 4
+#define ADALN_TAB_WPB_FP8 16
 #endif
 #ifndef ADALN_TAB_PF_SHORT
 #define ADALN_TAB_PF_SHORT 0
@@ -212,13 +214,13 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #define ADALN_TAB_XF32_RMS 1
 #endif
 #ifndef ADALN_TAB_PF_FP8
-#define ADALN_TAB_PF_FP8 1
+#define ADALN_TAB_PF_FP8 0
 #endif
 #ifndef ADALN_TAB_BPC_FP8
 #define ADALN_TAB_BPC_FP8 2
 #endif
 #ifndef ADALN_TAB_XF32_FP8
-#define ADALN_TAB_XF32_FP8 1
+#define ADALN_TAB_XF32_FP8 0
 #endif
 template <int NV, bool UNIF, bool RMS, int TAIL>
 struct TabShape {

@@ -125,6 +125,36 @@ def ln_modulate(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: 
     return call if prepare else call()
 
 
+def ln_modulate_noalloc(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float = 1e-6, *,
+                        out: torch.Tensor, mean_out: torch.Tensor | None = None,
+                        rstd_out: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """ln_modulate through ln_modulate_noalloc: the workspace path with the library's own
+    device array, for callers that cannot allocate (so `out` must be given).  Calls on one
+    device share that array: order them (one stream, or events)."""
+    _require(x, "x")
+    _require(scale, "scale")
+    _require(shift, "shift")
+    _require(out, "out")
+    if x.dim() != 3:
+        raise ValueError("x must be [B,S,D], got %s" % (tuple(x.shape),))
+    B, S, D = x.shape
+    scale, ssc = _rows_view(scale, B, D, "scale")
+    shift, ssh = _rows_view(shift, B, D, "shift")
+    if tuple(out.shape) != (B, S, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,S,D] tensor")
+    for name, t in (("mean_out", mean_out), ("rstd_out", rstd_out)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * S or not t.is_contiguous()
+                              or t.device != x.device):
+            raise ValueError("%s must be a contiguous float32 tensor of B*S elements on x's device" % name)
+    call = Prepared("ln_modulate_noalloc", N.lib().ln_modulate_noalloc, (
+        x.data_ptr(), B, S, D, x.stride(0), x.stride(1), x.stride(2),
+        scale.data_ptr(), ssc, shift.data_ptr(), ssh, float(eps), N.BF16, out.data_ptr(),
+        mean_out.data_ptr() if mean_out is not None else None,
+        rstd_out.data_ptr() if rstd_out is not None else None, _stream_handle(x, stream)), out,
+        keep=(x, scale, shift, out, mean_out, rstd_out))
+    return call if prepare else call()
+
+
 def _ln_common(x, scale, shift, out, out_dtype, mean_out, rstd_out):
     _require(x, "x")
     _require(scale, "scale")

@@ -69,3 +69,45 @@ def test_graph_replays_equal_eager(ops, shape):
         assert torch.equal(h.view(torch.int16), he.view(torch.int16)), "replay %d" % rep
         ops.ln_modulate(x0, embs[0][:, 1], embs[0][:, 0], eps)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["workspace", "noalloc"])
+def test_graph_workspace_paths(ops, path):
+    """ln_modulate_ws (a workspace of the caller's) and ln_modulate_noalloc (the library's
+    array) on transposed storage, captured once and replayed on new inputs: each replay
+    equals the eager ln_modulate of the inputs it ran on (the hand-over tags advance on the
+    device from replay to replay)."""
+    g0 = torch.Generator().manual_seed(2024)
+    B, S, D = 2, 1024, 2240
+    xs = [W.normal((B, D, S), g0, mean=0.1 * i, std=1.0 + i).to(DEV) for i in range(4)]
+    emb = W.normal((B, 2, D), g0, std=0.1).to(DEV)
+    xt = xs[0].clone()
+    x = xt.transpose(1, 2)
+    out = torch.empty((B, S, D), dtype=torch.bfloat16, device=DEV)
+    ws = ops.ln_modulate_workspace(x) if path == "workspace" else None
+
+    def call():
+        if path == "workspace":
+            ops.ln_modulate(x, emb[:, 1], emb[:, 0], 1e-6, out=out, workspace=ws)
+        else:
+            ops.ln_modulate_noalloc(x, emb[:, 1], emb[:, 0], 1e-6, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as capture requires
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(8):
+        xt.copy_(xs[rep % 4])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = ops.ln_modulate(xs[rep % 4].transpose(1, 2), emb[:, 1], emb[:, 0], 1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), "replay %d" % rep
+        call()  # eager work between replays, on the same workspace
+        torch.cuda.synchronize()
