@@ -506,9 +506,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mw(LnArgs a) {
 // past wait_ticks of the constant-rate clock a thread recomputes the state
 // it is missing from x itself (the same arithmetic, so the same bits).
 // Measured on MI355X against the one-block-per-8-token-tile kernel above,
-// same bits: (2,1024,2240) 8.6 us vs 10.7, (1,4096,4096) 17.5 vs 33.3,
-// (4,4096,3072) 56.9 vs 89.2; the hand-over costs about two device-scope
-// memory latencies (~2.3 us per group).
+// same bits: (2,1024,2240) 8.46 us vs 10.7 (one block per group, row and
+// adaLN values in registers: 8.80 with them re-read from LDS), (1,4096,4096)
+// 17.5 vs 33.3, (4,4096,3072) 57.9 vs 89.3; the hand-over costs about two
+// device-scope memory latencies (~2.3 us per group).
 // ---------------------------------------------------------------------------
 constexpr int kCoopTokens = 64;  // tokens per group (one 128-byte line per hidden position)
 constexpr int kCoopBlocks = 8;   // blocks per group (8 lanes of the 64 each)
@@ -593,15 +594,22 @@ __device__ __forceinline__ void coop_group_state(const uint16_t* xt, int64_t sx_
   m2 = q;
 }
 
-template <int NV>
+// ONE: every group has a block of its own (the grid covers the groups in one
+// pass, one block per compute unit), so registers are no longer shared with a
+// second block: each thread keeps its row and its own fp32 adaLN values
+// (loaded while it waits for the hand-over) in registers, and the tail reads
+// no LDS.  Otherwise the tail re-reads the row from the LDS tile and the
+// adaLN values from per-block LDS tables (two blocks per compute unit).
+template <int NV, bool ONE>
 __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int groups_per_sample, int ngroups,
                                                       uint64_t wait_ticks) {
   constexpr int V = 8;
+  constexpr int NT = ONE ? 1 : NV;  // steps of the LDS tables
   // [step][token][lane of the block ^ (token / 8)]: 16-byte vectors; the xor
   // spreads the 8 tokens 8 apart that one transpose writes over the banks
   __shared__ uint4 tile[NV][kCoopTokens][8];
-  __shared__ float4 otab[NV][8][2];  // bf16(1 + scale) of the block's vectors
-  __shared__ float4 htab[NV][8][2];  // shift of the block's vectors
+  __shared__ float4 otab[NT][8][2];  // bf16(1 + scale) of the block's vectors
+  __shared__ float4 htab[NT][8][2];  // shift of the block's vectors
   __shared__ uint32_t tag_sh;
   const int D = (int)a.D;
   const float Df = (float)D;
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
     {
       const int k = tid >> 6, j = (tid >> 3) & 7, p = tid & 7;
       const int tl = tid & (kWave - 1), tk = tl >> 3, tj = tl & 7, tv = 64 * tk + 8 * c + tj;
-      const bool tab = k == 7 && tl < NV * 8 && tv < nvec;
+      const bool tab = !ONE && k == 7 && tl < NV * 8 && tv < nvec;
       Vec<V> sv, hv;
       if (tab) {
         sv = load_vec<V>(a.scale + (int64_t)b * a.ssc_b + V * tv);
@@ -679,9 +687,9 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
           float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
           round_pair(o0, o1);  // bf16(1 + scale)
           round_pair(o2, o3);
-          otab[tk][tj][q] = make_float4(o0, o1, o2, o3);
-          htab[tk][tj][q] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]), lo_f32(hv.w[2 * q + 1]),
-                                        hi_f32(hv.w[2 * q + 1]));
+          otab[ONE ? 0 : tk][tj][q] = make_float4(o0, o1, o2, o3);
+          htab[ONE ? 0 : tk][tj][q] = make_float4(lo_f32(hv.w[2 * q]), hi_f32(hv.w[2 * q]),
+                                                  lo_f32(hv.w[2 * q + 1]), hi_f32(hv.w[2 * q + 1]));
         }
       }
       __asm__ volatile("" : "+v"(old));  // the arrival's result is first needed here
@@ -699,19 +707,28 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
     const int g = 8 * c + j;
     const int col = j ^ (t >> 3);
     float mean = 0.0f, m2 = 0.0f;
-    {
-      Vec<V> buf[NV];  // live for the pass only: the output re-reads the tile
+    Vec<V> buf[NV];  // with ONE kept for the tail; else live for the pass only (the tail re-reads the tile)
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (64 * k + g < nvec) {
+        const uint4 w = tile[k][t][col];
+        buf[k].w[0] = w.x;
+        buf[k].w[1] = w.y;
+        buf[k].w[2] = w.z;
+        buf[k].w[3] = w.w;
+      }
+    // ONE: this thread's adaLN vectors, issued now and turned into fp32 values while the
+    // hand-over is in flight
+    Vec<V> sv[ONE ? NV : 1], hv[ONE ? NV : 1];
+    if constexpr (ONE) {
 #pragma unroll
       for (int k = 0; k < NV; ++k)
         if (64 * k + g < nvec) {
-          const uint4 w = tile[k][t][col];
-          buf[k].w[0] = w.x;
-          buf[k].w[1] = w.y;
-          buf[k].w[2] = w.z;
-          buf[k].w[3] = w.w;
+          sv[k] = load_vec<V>(a.scale + (int64_t)b * a.ssc_b + V * (64 * k + g));
+          hv[k] = load_vec<V>(a.shift + (int64_t)b * a.ssh_b + V * (64 * k + g));
         }
-      lane_stats<V, false>(buf, nvec, g, kWave, mean, m2, std::make_integer_sequence<int, NV>{});
     }
+    lane_stats<V, false>(buf, nvec, g, kWave, mean, m2, std::make_integer_sequence<int, NV>{});
     float n = (float)((nvec > g ? (nvec - g + kWave - 1) / kWave : 0) * V);
     merge_level<1>(mean, m2, n, lane);
     merge_level<2>(mean, m2, n, lane);
@@ -725,6 +742,19 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
                          __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(vst + ri + c, tag | __builtin_bit_cast(uint32_t, m2), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float of[ONE ? NV : 1][V], hf[ONE ? NV : 1][V];
+    if constexpr (ONE) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (64 * k + g < nvec) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const uint32_t sw = sv[k].w[e / 2], hw = hv[k].w[e / 2];
+            of[k][e] = round_f32(1.0f + ((e & 1) ? hi_f32(sw) : lo_f32(sw)));  // bf16(1 + scale)
+            hf[k][e] = (e & 1) ? hi_f32(hw) : lo_f32(hw);
+          }
+        }
     }
     n = 0.0f;  // elements of lanes 8j .. 8j + 7: whole numbers, exact in any order
 #pragma unroll
@@ -765,12 +795,25 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
     for (int k = 0; k < NV; ++k) {
       const int v = 64 * k + g;
       if (v < nvec) {
-        const uint4 xw = tile[k][t][col];
-        const uint32_t xs[4] = {xw.x, xw.y, xw.z, xw.w};
+        uint32_t xs[4];
+        if constexpr (ONE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xs[i] = buf[k].w[i];
+        } else {
+          const uint4 xw = tile[k][t][col];
+          xs[0] = xw.x, xs[1] = xw.y, xs[2] = xw.z, xs[3] = xw.w;
+        }
         Vec<V> ov;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const float4 o = otab[k][j][q], h = htab[k][j][q];
+          float4 o, h;
+          if constexpr (ONE) {
+            o = make_float4(of[k][4 * q], of[k][4 * q + 1], of[k][4 * q + 2], of[k][4 * q + 3]);
+            h = make_float4(hf[k][4 * q], hf[k][4 * q + 1], hf[k][4 * q + 2], hf[k][4 * q + 3]);
+          } else {
+            o = otab[NT == 1 ? 0 : k][j][q];
+            h = htab[NT == 1 ? 0 : k][j][q];
+          }
           const float n0 = (lo_f32(xs[2 * q]) - mean) * rstd;
           const float n1 = (hi_f32(xs[2 * q]) - mean) * rstd;
           const float n2 = (lo_f32(xs[2 * q + 1]) - mean) * rstd;
@@ -944,15 +987,15 @@ inline uint64_t coop_wait_ticks(int dev) {
   return (uint64_t)us * (uint64_t)khz / 1000u;
 }
 
-// Blocks of ln_modulate_trc<NV> resident at once on the device (cached per
+// Blocks of ln_modulate_trc<NV, ONE> resident at once on the device (cached per
 // device): the grid never exceeds it, so the 8 blocks of a slot run together.
-template <int NV>
+template <int NV, bool ONE>
 int coop_resident_blocks(int dev) {
   static std::atomic<int> cache[kMaxDevices];
   int v = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV>, 512, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV, ONE>, 512, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   v = per_cu * cus;
@@ -971,10 +1014,20 @@ int launch_trc(const LnArgs& a, void* ws, hipStream_t st) {
   if (stream_device(st, &dev) != hipSuccess) return ADALN_ERR_HIP;
   const int64_t groups_per_sample = a.S / kCoopTokens;
   const int64_t ntg = (a.R / a.S) * groups_per_sample;
-  const int64_t slots = coop_resident_blocks<NV>(dev) / kCoopBlocks;
+  // one block per group when the groups fit one pass of the register-heavy kernel (its
+  // row and adaLN values fit the registers up to 5 vector steps, D <= 2560)
+  if constexpr (NV <= 5) {
+    const int64_t one_slots = coop_resident_blocks<NV, true>(dev) / kCoopBlocks;
+    if (ntg <= one_slots) {
+      hipLaunchKernelGGL((ln_modulate_trc<NV, true>), dim3((unsigned)(ntg * kCoopBlocks)), dim3(512), 0, st, a,
+                         static_cast<char*>(ws), (int)groups_per_sample, (int)ntg, coop_wait_ticks(dev));
+      return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+    }
+  }
+  const int64_t slots = coop_resident_blocks<NV, false>(dev) / kCoopBlocks;
   if (slots < 1) return ADALN_ERR_HIP;
   const unsigned grid = (unsigned)(std::min(ntg, slots) * kCoopBlocks);
-  hipLaunchKernelGGL((ln_modulate_trc<NV>), dim3(grid), dim3(512), 0, st, a, static_cast<char*>(ws),
+  hipLaunchKernelGGL((ln_modulate_trc<NV, false>), dim3(grid), dim3(512), 0, st, a, static_cast<char*>(ws),
                      (int)groups_per_sample, (int)ntg,
                      coop_wait_ticks(dev));
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
