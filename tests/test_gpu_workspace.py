@@ -162,6 +162,13 @@ def test_ws_recompute_path(ops, orc, monkeypatch):
     x2 = transposed(1, 256, 8, g)
     emb2 = rand_bf16((1, 2, 8), g, std=0.1).to(DEV)
     run_ws(ops, x2, emb2[:, 1], emb2[:, 0], 1e-6, ws, orc=orc, what="recompute D=8")
+    # the persistent kernel (more groups than one pass of one block per group holds; at
+    # D = 4096 the kernel that re-reads its row from LDS) recomputes in the same order
+    for shape in ((3, 1024, 2240), (1, 4096, 4096)):
+        x3 = transposed(*shape, g)
+        emb3 = rand_bf16((shape[0], 2, shape[2]), g, std=0.1).to(DEV)
+        run_ws(ops, x3, emb3[:, 1], emb3[:, 0], 1e-6, ops.ln_modulate_workspace(x3), orc=orc,
+               what="recompute %s" % (shape,))
     monkeypatch.delenv("ADALN_WS_WAIT_US")
     run_ws(ops, x, emb[:, 1], emb[:, 0], 1e-6, ws, what="after recompute")
 
