@@ -217,3 +217,23 @@ def test_ws_fallbacks_are_ln_modulate(ops, orc):
     small = torch.full((ops.ln_modulate_workspace_size(x) - 8,), 0x5A, dtype=torch.uint8, device=DEV)
     run_ws(ops, x, emb[:, 1], emb[:, 0], 1e-6, small, what="workspace too small")
     assert bool((small == 0x5A).all()), "too-small workspace written"
+
+
+def test_ws_broadcast_row_and_no_stats(ops, orc):
+    """One adaLN row for every sample (row stride 0), and calls that ask for no statistics."""
+    g = torch.Generator().manual_seed(17)
+    B, S, D = 3, 1024, 520
+    x = transposed(B, S, D, g)
+    sc1 = rand_bf16((1, D), g, std=0.1).to(DEV)
+    sh1 = rand_bf16((1, D), g, std=0.1).to(DEV)
+    sc, sh = sc1.expand(B, D), sh1.expand(B, D)
+    assert sc.stride(0) == 0
+    ws = ops.ln_modulate_workspace(x)
+    run_ws(ops, x, sc, sh, 1e-6, ws, orc=orc, what="broadcast row")
+    for shape in ((2, 1024, 2240), (1, 4096, 4096)):
+        xs = transposed(*shape, g)
+        e = rand_bf16((shape[0], 2, shape[2]), g, std=0.1).to(DEV)
+        y = ops.ln_modulate(xs, e[:, 1], e[:, 0], 1e-6, workspace=ops.ln_modulate_workspace(xs))
+        y0 = ops.ln_modulate(xs, e[:, 1], e[:, 0], 1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), "no stats %s" % (shape,)
