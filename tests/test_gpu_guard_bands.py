@@ -259,3 +259,32 @@ def test_gelu_bands(ops, rows, width, skew):
     what = "bias_gelu_tanh (%d,%d) skew=%d" % (rows, width, skew)
     o.check(what)
     same_bytes(o.t, ref, what)
+
+
+@pytest.mark.parametrize("shape", [(2, 1024, 2240), (3, 1024, 2240), (1, 64, 8), (2, 128, 4096), (1, 192, 520)])
+@pytest.mark.parametrize("skew", [0, 1])
+def test_ln_modulate_workspace_bands(ops, shape, skew):
+    """ln_modulate_ws on transposed storage: the output, the statistics and the workspace
+    itself (zero-filled inside its bands) are written within their bounds only; skew 1
+    puts the output off the 16-byte alignment the workspace path needs (ln_modulate's
+    kernels then run, the workspace untouched)."""
+    B, S, D = shape
+    x, sc, sh = ln_inputs(shape, 41 + D, transposed=True)
+    ref_m = torch.empty(B * S, dtype=torch.float32, device=DEV)
+    ref_r = torch.empty(B * S, dtype=torch.float32, device=DEV)
+    ref = ops.ln_modulate(x, sc, sh, 1e-6, mean_out=ref_m, rstd_out=ref_r)
+    nb = ops.ln_modulate_workspace_size(x)
+    assert nb > 0
+    w = Banded((nb,), torch.uint8)
+    w.t.zero_()
+    o = Banded((B, S, D), torch.bfloat16, SKEWS[torch.bfloat16][skew])
+    m, r = stats_pair(B, S, SKEWS[torch.float32][skew])
+    for call in range(2):  # the second call finds the workspace as the first left it
+        ops.ln_modulate(x, sc, sh, 1e-6, out=o.t, mean_out=m.t, rstd_out=r.t, workspace=w.t)
+        what = "ln_modulate_ws %s skew=%d call %d" % (shape, skew, call)
+        for band, want, name in ((o, ref, "out"), (m, ref_m, "mean"), (r, ref_r, "rstd")):
+            band.check("%s %s" % (what, name))
+            same_bytes(band.t, want, "%s %s" % (what, name))
+        w.check("%s workspace" % what)
+        if skew:
+            assert not bool(w.t.any()), "%s: workspace written off the workspace path" % what
