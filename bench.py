@@ -99,7 +99,7 @@ def main() -> int:
     ap.add_argument("--buffers", type=int, default=12, help="rotated buffer sets (>= 1 GiB total)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads' timings")
-    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall-time budget of the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the CPU baseline")
     args = ap.parse_args()
 
     if args.gpus != 1:
