@@ -764,14 +764,14 @@ __global__ __launch_bounds__(512) void ln_modulate_trc(LnArgs a, char* ws, int g
     }
     if (j != c) {
       // poll both words (each wave's 64 pairs are 512 contiguous bytes twice)
-      const uint64_t deadline = wall_clock64() + wait_ticks;
+      const uint64_t deadline = (uint64_t)wall_clock64() + wait_ticks;
       uint64_t w0, w1;
       bool ok;
       while (true) {
         w0 = __hip_atomic_load(mst + ri + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         w1 = __hip_atomic_load(vst + ri + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = (w0 & ~0xffffffffull) == tag && (w1 & ~0xffffffffull) == tag;
-        if (ok || wall_clock64() > deadline) break;
+        if (ok || (uint64_t)wall_clock64() > deadline) break;
         __builtin_amdgcn_s_sleep(1);
       }
       if (ok) {
