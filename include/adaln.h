@@ -139,7 +139,9 @@ int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t s
  * resident on the device at once, and a block that waits too long for
  * another's state (ADALN_WS_WAIT_US microseconds, default 200, read at each
  * call; 0 = never wait) recomputes that state from x: same arithmetic,
- * same bits.
+ * same bits.  Calls on different streams with workspaces of their own may
+ * run concurrently; the device may then not hold both grids at once, and
+ * the bounded waits keep them correct (same bits, more time).
  */
 int ln_modulate_ws(const void* x, int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s,
                    int64_t sx_d, const void* scale, int64_t sscale_b, const void* shift,

@@ -237,3 +237,26 @@ def test_ws_broadcast_row_and_no_stats(ops, orc):
         y0 = ops.ln_modulate(xs, e[:, 1], e[:, 0], 1e-6)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), "no stats %s" % (shape,)
+
+
+def test_ws_concurrent_streams(ops):
+    """Calls on two streams at once, each with a workspace of its own: each grid is sized to
+    be resident alone, so together they may not be; a block whose partner is not running
+    waits a bounded time and recomputes, so both still give ln_modulate's bits."""
+    g = torch.Generator().manual_seed(23)
+    shapes = [(2, 1024, 2240), (1, 4096, 4096)]
+    xs = [transposed(*s, g) for s in shapes]
+    es = [rand_bf16((s[0], 2, s[2]), g, std=0.1).to(DEV) for s in shapes]
+    wss = [ops.ln_modulate_workspace(x) for x in xs]
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+    want = [ops.ln_modulate(x, e[:, 1], e[:, 0], 1e-6) for x, e in zip(xs, es)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                for _ in range(3):
+                    ops.ln_modulate(xs[i], es[i][:, 1], es[i][:, 0], 1e-6, out=outs[i], workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i].view(torch.int16), want[i].view(torch.int16)), "rep %d stream %d" % (rep, i)
