@@ -994,10 +994,13 @@ int coop_resident_blocks(int dev) {
   static std::atomic<int> cache[kMaxDevices];
   int v = dev >= 0 && dev < kMaxDevices ? cache[dev].load(std::memory_order_relaxed) : 0;
   if (v > 0) return v;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV, ONE>, 512, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+  int per_cu = 0, cus = 0, cur = 0;
+  // the occupancy query reads the current device: make it the stream's for the query
+  if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) return 0;
+  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV, ONE>, 512, 0) ==
+                      hipSuccess &&
+                  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  if ((cur != dev && hipSetDevice(cur) != hipSuccess) || !ok) return 0;
   v = per_cu * cus;
   if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
   return v;
