@@ -345,6 +345,11 @@ def other_workloads(m, W, dev, stream, log):
     us = time_loop(calls, 500, stream)
     res["ln_modulate_2x1024x2240_transposed_ws"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
                                                      "pages_H200_us": 14.3}
+    # and with the library's own array (ln_modulate_noalloc)
+    calls = [m.ln_modulate_noalloc(xts[i].transpose(1, 2), emb[:, 5], emb[:, 0], 1e-6, out=outs[i], prepare=True)
+             for i in range(nb)]
+    us = time_loop(calls, 500, stream)
+    res["ln_modulate_2x1024x2240_transposed_noalloc"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1)}
     xcs = [xt.transpose(1, 2).contiguous() for _ in range(nb)]
     calls = [m.ln_modulate(xcs[i], emb[:, 5], emb[:, 0], 1e-6, out=outs[i], prepare=True) for i in range(nb)]
     us = time_loop(calls, 500, stream)

@@ -112,3 +112,13 @@ def test_noalloc_rejects_beyond_its_array(N):
         assert rc == rc_want, (S, N.status_str(rc))
         if rc_want != N.OK:
             assert not out.any(), "a rejected call wrote its output"
+        else:  # the largest size the array holds: 1024 groups, the same bits as ln_modulate
+            import modulate_ln_amd as ops
+
+            m0 = torch.empty_like(m)
+            r0 = torch.empty_like(r)
+            want = ops.ln_modulate(x, e[:, 1], e[:, 0], 1e-6, mean_out=m0, rstd_out=r0)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+            assert torch.equal(m.view(torch.int32), m0.view(torch.int32))
+            assert torch.equal(r.view(torch.int32), r0.view(torch.int32))
