@@ -133,9 +133,9 @@ int ln_modulate_can_use(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t s
  *  (workspace_bytes < 0).
  *
  * The workspace path runs when sx_s == 1, D % 8 == 0, D <= 4096,
- * S % 64 == 0, sx_d % 8 == 0, sx_b % 8 == 0 (B > 1), x, scale, shift and
- * out are 16-byte aligned and the scale/shift row strides are multiples of
- * 8; any other shape takes ln_modulate's kernels.  Its grid is sized to be
+ * S % 64 == 0, S < 2^31, sx_d % 8 == 0, sx_b % 8 == 0 (B > 1), x, scale,
+ * shift and out are 16-byte aligned and the scale/shift row strides are
+ * multiples of 8; any other shape takes ln_modulate's kernels.  Its grid is sized to be
  * resident on the device at once, and a block that waits too long for
  * another's state (ADALN_WS_WAIT_US microseconds, default 200, read at each
  * call; 0 = never wait) recomputes that state from x: same arithmetic,

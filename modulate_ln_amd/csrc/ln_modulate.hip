@@ -964,8 +964,9 @@ int dispatch(const LnArgs& a, hipStream_t st) {
 }
 
 // whole 64-token groups of transposed storage, 16-byte runs, one wave per row
+// (the kernel indexes tokens within a sample and blocks in 32 bits)
 inline bool coop_shape_ok(int64_t B, int64_t S, int64_t D, int64_t sx_b, int64_t sx_s, int64_t sx_d) {
-  return sx_s == 1 && D % 8 == 0 && D <= kTrMaxD && S % kCoopTokens == 0 && sx_d % 8 == 0 &&
+  return sx_s == 1 && D % 8 == 0 && D <= kTrMaxD && S % kCoopTokens == 0 && S < INT32_MAX && sx_d % 8 == 0 &&
          (B <= 1 || sx_b % 8 == 0) && B * (S / kCoopTokens) * kCoopBlocks < INT32_MAX;
 }
 

@@ -243,6 +243,9 @@ def test_ln_modulate_workspace_size(L):
     assert size(2, 128, 512, sx=(512 * 128 + 4, 1, 128)) == 0  # sample stride not 16-byte multiples
     assert size(0, 64, 512) == 0  # empty
     assert size(1, 64, 6) == 0  # rejected shape
+    # tokens within a sample are indexed in 32 bits on that path
+    assert size(1, 2**31 - 64, 8) == (2**31 - 64) // 64 * group
+    assert size(1, 2**31, 8) == 0
 
 
 def test_residual_gate_add_rejections(L):
