@@ -891,6 +891,13 @@ int launch_tr(const LnArgs& a, hipStream_t st) {
 
 constexpr int kTrMaxD = 4096;  // 96 KiB of LDS (tables + tile)
 
+// One-shot grids stay under 2^32 work-items (a dispatch counts its grid in
+// 32 bits): the tabled kernels take up to 1024 threads per sample, the
+// 8-token tile kernel 512 per tile; larger launches go to the row kernels,
+// whose grids are capped and walk the rows.
+constexpr int64_t kMaxTabSamples = ((int64_t)1 << 22) - 1;
+constexpr int64_t kMaxTrTiles = (int64_t)1 << 23;
+
 template <bool RMS, int TAIL>
 int dispatch_tr(const LnArgs& a, hipStream_t st) {
   const int64_t nvec = a.D / 8;
@@ -1185,8 +1192,9 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
     if (V == 8) return vec ? dispatch_mw<8, false, RMS, TAIL>(a, ord.W, st) : dispatch_mw<8, true, RMS, TAIL>(a, ord.W, st);
     return vec ? dispatch_mw<4, false, RMS, TAIL>(a, ord.W, st) : dispatch_mw<4, true, RMS, TAIL>(a, ord.W, st);
   }
-  // the tabled fast path indexes rows, samples and offsets in 32 bits
-  const bool tab = vec && S <= INT32_MAX / 4 && B <= INT32_MAX;
+  // the tabled fast path indexes rows, samples and offsets in 32 bits, and
+  // launches a block of up to 1024 threads per sample
+  const bool tab = vec && S <= INT32_MAX / 4 && B <= kMaxTabSamples;
   if (tab) return V == 8 ? dispatch_tab<8, RMS, TAIL>(a, st) : dispatch_tab<4, RMS, TAIL>(a, st);
   // transposed storage with a workspace (the caller's, or the library's
   // scratch): whole lines, 8 blocks per 64-token group
@@ -1205,7 +1213,7 @@ static int norm_modulate(const void* x, int64_t B, int64_t S, int64_t D, int64_t
   }
   // transposed storage: whole 8-token tiles, each tile's 16-byte token runs aligned
   const bool tr = sx_s == 1 && V == 8 && D <= kTrMaxD && S % kTrTokens == 0 && S < INT32_MAX &&
-                  B * (S / kTrTokens) < INT32_MAX && aligned(x, 16) && sx_d % 8 == 0 &&
+                  B * (S / kTrTokens) < kMaxTrTiles && aligned(x, 16) && sx_d % 8 == 0 &&
                   (B == 1 || sx_b % 8 == 0) && aligned(scale, 16) && aligned(shift, 16) &&
                   aligned(out, kFp8 ? 8 : 16) && stride_ok(B, sscale_b) && stride_ok(B, sshift_b);
   if (tr) return dispatch_tr<RMS, TAIL>(a, st);

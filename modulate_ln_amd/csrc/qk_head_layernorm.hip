@@ -310,7 +310,9 @@ __global__ __launch_bounds__(256) void qk_heads(QkArgs a) {
 #ifndef ADALN_QK_HP1
 #define ADALN_QK_HP1 2
 #endif
-constexpr int64_t kMaxHeadBlocks = (int64_t)1 << 30;
+// at most 2^31 work-items (a dispatch counts its grid in 32 bits); the
+// groups of a smaller grid walk the remaining heads
+constexpr int64_t kMaxHeadBlocks = (int64_t)1 << 23;
 
 template <bool RMS, int V, int NV, bool UNIFORM, bool AFFINE, bool EQ>
 int launch_heads(const QkArgs& a, hipStream_t st) {

@@ -397,8 +397,9 @@ extern "C" int residual_gate_add_ln_modulate(const void* residual, int64_t sr_b,
   const uintptr_t vb = (uintptr_t)(2 * V);
   auto stride_ok = [&](int64_t n, int64_t st) { return n <= 1 || ((uintptr_t)st * 2u) % vb == 0; };
   // one launch for vector-aligned rows (the tabled kernel indexes rows,
-  // samples and offsets in 32 bits)
-  const bool fused = (ord.W > 1 ? V == 8 : (S <= INT32_MAX / 4 && B <= INT32_MAX)) && aligned(residual, vb) &&
+  // samples and offsets in 32 bits and launches a block of up to 1024
+  // threads per sample: under 2^32 work-items)
+  const bool fused = (ord.W > 1 ? V == 8 : (S <= INT32_MAX / 4 && B < ((int64_t)1 << 22))) && aligned(residual, vb) &&
                      aligned(update, vb) &&
                      aligned(gate, vb) && aligned(scale, vb) && aligned(shift, vb) &&
                      aligned(residual_out, vb) && aligned(out, vb) && stride_ok(B, sr_b) &&
