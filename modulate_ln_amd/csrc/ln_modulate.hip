@@ -476,6 +476,96 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mw(LnArgs a) {
   }
 }
 
+// Rows of 4097 .. 16384 elements with 16-byte vectors, P = 16 / W rows of one
+// sample per block of 16 waves: group q (waves qW .. qW + W - 1) takes row
+// s0 + q.  The sample's tables -- bf16(1 + scale) and shift as fp32, the
+// tabled kernel's layout -- are built in LDS once per block, where
+// ln_modulate_mw has each row's block fetch the bf16 rows through the caches
+// and widen and round them per element.  Lanes, steps and merges are
+// ln_modulate_mw's (the group's lanes g = 0 .. 64W - 1 in the same fixed
+// tree), and the tables hold the values its tail computes, so the bits are
+// the same.
+template <int NV, bool UNIF, bool RMS, int TAIL>
+__global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mwt(LnArgs a, int bps, int W) {
+  constexpr int V = 8;
+  constexpr int kRuns = 2;  // adaLN vectors per thread: D <= 2 * 1024 * 8
+  extern __shared__ float4 tab[];  // [2][V / 4][D / V]
+  __shared__ MwSlots slots;
+  const int L = W * kWave;
+  const int P = kMaxWaves / W;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = wave / W;              // the block's row group
+  const int g = threadIdx.x - q * L;   // lane of the row's lane map
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = (int)(a.D / V);
+  const float Df = (float)a.D;
+  const float qinv = qinv_of<TAIL>(a);
+  const int64_t b = blockIdx.x / bps;
+  const int64_t s = (int64_t)(blockIdx.x - b * bps) * P + q;
+  const bool act = s < a.S;
+  const int64_t r = b * a.S + (act ? s : a.S - 1);  // a group past the sample's rows reads its last row
+
+  // the adaLN vectors are issued first and turned into tables once the row's loads are out
+  const uint16_t* sc = a.scale + b * a.ssc_b;
+  const uint16_t* sh = a.shift + b * a.ssh_b;
+  Vec<V> ts[kRuns], th[kRuns];
+#pragma unroll
+  for (int i = 0; i < kRuns; ++i) {
+    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < V / 2; ++e) ts[i].w[e] = th[i].w[e] = 0u;
+    if (j < nvec) {
+      ts[i] = load_vec<V>(sc + j * V);
+      th[i] = load_vec<V>(sh + j * V);
+    }
+  }
+  const uint16_t* xr = a.x + b * a.sx_b + (r - b * a.S) * a.sx_s;
+  Vec<V> buf[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (UNIF || k * L < nvec) {  // wave-uniform: steps past the row are not loaded
+      const int v = k * L + g;
+      const int vc = v < nvec ? v : nvec - 1;
+      buf[k] = load_vec_nt<V>(xr + (uint32_t)(vc * V));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRuns; ++i) {
+    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    if (j < nvec) put_tables<V>(tab, ts[i], th[i], j, nvec);
+  }
+  float mean, m2;
+  // the group's slots; the barrier inside also publishes the tables
+  mw_stats<V, NV, UNIF, RMS>(buf, nvec, g, lane, wave - q * W, W, slots.s[0] + q * W, mean, m2);
+  if (!act) return;  // no barrier follows
+  const float rstd = finalize_rstd(m2, Df, a.eps, pow2_inverse_f(Df));
+  if (g == 0) {
+    if (!RMS && a.mean_out) a.mean_out[r] = mean;
+    if (a.rstd_out) a.rstd_out[r] = rstd;
+  }
+  void* orow = out_row<TAIL>(a, r);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = k * L + g;
+    if (UNIF || v < nvec) {
+      uint32_t o[V / 2];
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) {
+        const float4 oc = tab[h * nvec + v], hc = tab[(V / 4 + h) * nvec + v];
+        const float x0 = lo_f32_again(buf[k].w[2 * h]), x1 = hi_f32_again(buf[k].w[2 * h]);
+        const float x2 = lo_f32_again(buf[k].w[2 * h + 1]), x3 = hi_f32_again(buf[k].w[2 * h + 1]);
+        const float n0 = RMS ? x0 * rstd : (x0 - mean) * rstd;
+        const float n1 = RMS ? x1 * rstd : (x1 - mean) * rstd;
+        const float n2 = RMS ? x2 * rstd : (x2 - mean) * rstd;
+        const float n3 = RMS ? x3 * rstd : (x3 - mean) * rstd;
+        o[2 * h] = tail_pair<TAIL>(n0, n1, oc.x, oc.y, hc.x, hc.y);
+        o[2 * h + 1] = tail_pair<TAIL>(n2, n3, oc.z, oc.w, hc.z, hc.w);
+      }
+      put_vec<V, false, TAIL>(orow, v, o, qinv);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Transposed storage read in whole lines, with a workspace (ln_modulate_ws).
 // A 128-byte line of [B, D, S] storage holds 64 consecutive tokens of one
@@ -850,14 +940,34 @@ int launch_mw(const LnArgs& a, int W, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+// 16-wave blocks of 16 / W rows of one sample, the sample's adaLN rows in LDS
+template <int NV, bool UNIF, bool RMS, int TAIL>
+int launch_mwt(const LnArgs& a, int W, hipStream_t st) {
+  const int64_t P = kMaxWaves / W;
+  const int64_t B = a.R / a.S;
+  const int64_t bps = (a.S + P - 1) / P;
+  const size_t lds = (size_t)a.D * 2 * sizeof(float);
+  hipLaunchKernelGGL((ln_modulate_mwt<NV, UNIF, RMS, TAIL>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
+                     st, a, (int)bps, W);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
 // W waves per row (W = 2 .. 16): every lane holds at most 64 elements, NV
-// vector steps of V
+// vector steps of V.  Vector-aligned rows of up to 16384 elements whose
+// samples have at least 16 / W rows share each sample's adaLN tables across
+// the rows of a block (ln_modulate_mwt; under 2^22 blocks of 1024 threads).
 template <int V, bool GATHER, bool RMS, int TAIL>
 int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
   constexpr int NV = 64 / V;
   const int64_t nvec = a.D / V;
+  const bool unif = V == 8 && nvec == (int64_t)NV * W * kWave;
+  if constexpr (V == 8 && !GATHER) {
+    const int64_t P = kMaxWaves / W;
+    if (W <= 4 && a.S >= P && (a.R / a.S) * ((a.S + P - 1) / P) < ((int64_t)1 << 22))
+      return unif ? launch_mwt<NV, true, RMS, TAIL>(a, W, st) : launch_mwt<NV, false, RMS, TAIL>(a, W, st);
+  }
   if constexpr (V == 8) {
-    if (nvec == (int64_t)NV * W * kWave) return launch_mw<V, NV, true, GATHER, RMS, TAIL>(a, W, st);
+    if (unif) return launch_mw<V, NV, true, GATHER, RMS, TAIL>(a, W, st);
   }
   return launch_mw<V, NV, false, GATHER, RMS, TAIL>(a, W, st);
 }

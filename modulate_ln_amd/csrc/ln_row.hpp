@@ -54,28 +54,37 @@ __device__ __forceinline__ void welford_f32(const float (*xf)[V], int nvec, int 
 // [table][V/4][nvec] so a lane's reads for vector v are contiguous across
 // the wave.  Built cooperatively by the nthreads threads of a block.
 // Returns whether every value this thread wrote is finite.
+// Vector v of the tables from the sample's scale and shift vectors; returns
+// whether the values written are finite.
+template <int V>
+__device__ __forceinline__ bool put_tables(float4* tab, const Vec<V>& sv, const Vec<V>& hv, int v, int nvec) {
+  const int shift_off = (V / 4) * nvec;
+  bool finite = true;
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q) {
+    float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
+    float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
+    round_pair(o0, o1);  // bf16(1 + scale)
+    round_pair(o2, o3);
+    tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
+    const float h0 = lo_f32(hv.w[2 * q]), h1 = hi_f32(hv.w[2 * q]);
+    const float h2 = lo_f32(hv.w[2 * q + 1]), h3 = hi_f32(hv.w[2 * q + 1]);
+    tab[shift_off + q * nvec + v] = make_float4(h0, h1, h2, h3);
+    finite = finite && __builtin_isfinite(o0) && __builtin_isfinite(o1) && __builtin_isfinite(o2) &&
+             __builtin_isfinite(o3) && __builtin_isfinite(h0) && __builtin_isfinite(h1) &&
+             __builtin_isfinite(h2) && __builtin_isfinite(h3);
+  }
+  return finite;
+}
+
 template <int V>
 __device__ __forceinline__ bool build_tables(float4* tab, const uint16_t* sc, const uint16_t* sh,
                                              int nvec, int tid, int nthreads) {
-  const int shift_off = (V / 4) * nvec;
   bool finite = true;
   for (int v = tid; v < nvec; v += nthreads) {
     const Vec<V> sv = load_vec<V>(sc + v * V);
     const Vec<V> hv = load_vec<V>(sh + v * V);
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      float o0 = 1.0f + lo_f32(sv.w[2 * q]), o1 = 1.0f + hi_f32(sv.w[2 * q]);
-      float o2 = 1.0f + lo_f32(sv.w[2 * q + 1]), o3 = 1.0f + hi_f32(sv.w[2 * q + 1]);
-      round_pair(o0, o1);  // bf16(1 + scale)
-      round_pair(o2, o3);
-      tab[q * nvec + v] = make_float4(o0, o1, o2, o3);
-      const float h0 = lo_f32(hv.w[2 * q]), h1 = hi_f32(hv.w[2 * q]);
-      const float h2 = lo_f32(hv.w[2 * q + 1]), h3 = hi_f32(hv.w[2 * q + 1]);
-      tab[shift_off + q * nvec + v] = make_float4(h0, h1, h2, h3);
-      finite = finite && __builtin_isfinite(o0) && __builtin_isfinite(o1) && __builtin_isfinite(o2) &&
-               __builtin_isfinite(o3) && __builtin_isfinite(h0) && __builtin_isfinite(h1) &&
-               __builtin_isfinite(h2) && __builtin_isfinite(h3);
-    }
+    finite = put_tables<V>(tab, sv, hv, v, nvec) && finite;
   }
   return finite;
 }

@@ -173,6 +173,23 @@ def test_ln_waves_per_row(ops, orc, D, W):
     run_ln(ops, orc, big[:, :, 1:1 + D], sc, sh, 1e-5, what="misaligned W=%d D=%d" % (W, D))
 
 
+# vector-aligned rows of 4097 .. 16384 elements whose samples have at least 16 / W rows: a block
+# of 16 waves holds 16 / W rows of one sample and builds the sample's tables once; the lanes and
+# merges are those of one row per block, so the order (and the bits) stay the same.  Whole
+# blocks, a partial last block per sample, and several samples.
+@pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (8200, 4), (16384, 4), (12296, 4)])
+@pytest.mark.parametrize("B,S", [(1, 16), (3, 9), (2, 37)])
+def test_ln_waves_per_row_shared_tables(ops, orc, D, W, B, S):
+    from modulate_ln_amd import _native as N
+
+    assert N.order_for(N.OP_LN_MODULATE, D).W == W
+    g = torch.Generator().manual_seed(11 * D + S)
+    x = rand_bf16((B, S, D), g, std=2.0, mean=0.25).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, what="shared tables W=%d D=%d (%d,%d)" % (W, D, B, S))
+
+
 @pytest.mark.parametrize("D", [8, 64, 520, 1000, 2240, 3072, 4096, 4104, 8192])
 @pytest.mark.parametrize("B,S", [(1, 8), (2, 40), (3, 1024)])
 def test_ln_transposed_storage(ops, orc, B, S, D):

@@ -73,6 +73,18 @@ def test_fp8_hidden_sizes(ops, orc, D):
     run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "D=%d" % D)
 
 
+@pytest.mark.parametrize("D", [8192, 16384])
+def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D):
+    """Rows of 2 and 4 waves, 19 per sample (blocks of 16 waves sharing the sample's tables,
+    a partial last block per sample): the FP8 producer and the fold."""
+    g = torch.Generator().manual_seed(850 + D)
+    x = rand_bf16((2, 19, D), g, std=3.0, mean=0.5).to(DEV)
+    sc = rand_bf16((2, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((2, D), g, std=0.1).to(DEV)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "shared tables D=%d" % D)
+    run_fold(ops, orc, x, sc, sh, 1e-6, "shared tables D=%d" % D)
+
+
 def test_fp8_layouts_and_specials(ops, orc):
     g = torch.Generator().manual_seed(81)
     B, S, D = 2, 1024, 2240
