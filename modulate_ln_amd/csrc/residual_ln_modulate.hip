@@ -254,6 +254,99 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mw(FusedArgs a
   }
 }
 
+// Rows of 4097 .. 16384 elements, P = 16 / W rows of one sample per block of
+// 16 waves (group q of W waves takes row s0 + q), the layout of
+// ln_modulate_mwt: the sample's tables bf16(1 + scale) and shift are built
+// in LDS as fp32 once per block, where rga_ln_modulate_mw fetches the bf16
+// rows through the caches and widens and rounds them per element.  The gate
+// is needed before the statistics, so it comes through the caches as there.
+// Same lanes, merges and values, so the same bits.
+template <int NV, bool UNIF>
+__global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mwt(FusedArgs a, int bps, int W) {
+  constexpr int V = 8;
+  constexpr int kRuns = 2;  // adaLN vectors per thread: D <= 2 * 1024 * 8
+  extern __shared__ float4 tab[];  // [2][V / 4][D / V]
+  __shared__ MwSlots slots;
+  const int L = W * kWave;
+  const int P = kMaxWaves / W;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = wave / W;              // the block's row group
+  const int g = threadIdx.x - q * L;   // lane of the row's lane map
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = (int)(a.D / V);
+  const float Df = (float)a.D;
+  const int64_t b = blockIdx.x / bps;
+  const int64_t s = (int64_t)(blockIdx.x - b * bps) * P + q;
+  const bool act = s < a.S;
+  const int64_t sr = act ? s : a.S - 1;  // a group past the sample's rows reads its last row
+  const int64_t r = b * a.S + sr;
+
+  // the adaLN vectors are issued first and turned into tables once the row's loads are out
+  const uint16_t* sc = a.scale + b * a.ssc_b;
+  const uint16_t* sh = a.shift + b * a.ssh_b;
+  Vec<V> ts[kRuns], th[kRuns];
+#pragma unroll
+  for (int i = 0; i < kRuns; ++i) {
+    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < V / 2; ++e) ts[i].w[e] = th[i].w[e] = 0u;
+    if (j < nvec) {
+      ts[i] = load_vec<V>(sc + j * V);
+      th[i] = load_vec<V>(sh + j * V);
+    }
+  }
+  const uint16_t* rr = a.res + b * a.sr_b + sr * a.sr_s;
+  const uint16_t* ur = a.upd + b * a.su_b + sr * a.su_s;
+  const uint16_t* gt = a.gate + b * a.sg_b;
+  uint16_t* xrow = a.res_out + r * a.D;
+  Vec<V> xn[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (UNIF || k * L < nvec) {  // wave-uniform: steps past the row are not loaded
+      const int v = k * L + g;
+      const uint32_t off = (uint32_t)((v < nvec ? v : nvec - 1) * V);  // 32-bit offsets from scalar row bases
+      const Vec<V> rv = load_vec_nt<V>(rr + off);
+      const Vec<V> uv = load_vec_nt<V>(ur + off);
+      const Vec<V> gv = load_vec<V>(gt + off);
+      xn[k] = gate_add_vec<V>(rv, uv, gv);
+      if (act && (UNIF || v < nvec)) store_vec_nt<V>(xrow + (uint32_t)(v * V), xn[k]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRuns; ++i) {
+    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    if (j < nvec) put_tables<V>(tab, ts[i], th[i], j, nvec);
+  }
+  float mean, m2;
+  // the group's slots; the barrier inside also publishes the tables
+  mw_stats<V, NV, UNIF, false>(xn, nvec, g, lane, wave - q * W, W, slots.s[0] + q * W, mean, m2);
+  if (!act) return;  // no barrier follows
+  const float rstd = finalize_rstd(m2, Df, a.eps, pow2_inverse_f(Df));
+  if (g == 0) {
+    if (a.mean_out) a.mean_out[r] = mean;
+    if (a.rstd_out) a.rstd_out[r] = rstd;
+  }
+  uint16_t* orow = a.out + r * a.D;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = k * L + g;
+    if (UNIF || v < nvec) {
+      uint32_t o[V / 2];
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) {
+        const float4 oc = tab[h * nvec + v], hc = tab[(V / 4 + h) * nvec + v];
+        const float n0 = (lo_f32_again(xn[k].w[2 * h]) - mean) * rstd;
+        const float n1 = (hi_f32_again(xn[k].w[2 * h]) - mean) * rstd;
+        const float n2 = (lo_f32_again(xn[k].w[2 * h + 1]) - mean) * rstd;
+        const float n3 = (hi_f32_again(xn[k].w[2 * h + 1]) - mean) * rstd;
+        o[2 * h] = tail_pair<kTailChain>(n0, n1, oc.x, oc.y, hc.x, hc.y);
+        o[2 * h + 1] = tail_pair<kTailChain>(n2, n3, oc.z, oc.w, hc.z, hc.w);
+      }
+      put_vec<V, false, kTailChain>(orow, v, o, 1.0f);
+    }
+  }
+}
+
 constexpr int64_t kLdsPerCu = 160 * 1024;
 
 template <int V, int NV, bool UNIF>
@@ -309,8 +402,22 @@ int dispatch_fused(const FusedArgs& a, hipStream_t st) {
 // unfused kernels.)
 int dispatch_fused_mw(const FusedArgs& a, int W, hipStream_t st) {
   constexpr int V = 8, NV = 8;
+  const bool unif = a.D / V == (int64_t)NV * W * kWave;
+  // rows of up to 16384 elements, samples of at least 16 / W rows: blocks of
+  // 16 waves sharing the sample's tables (under 2^22 blocks of 1024 threads)
+  const int64_t P = kMaxWaves / W, B = a.R / a.S, bps = (a.S + P - 1) / P;
+  if (W <= 4 && a.S >= P && B * bps < ((int64_t)1 << 22)) {
+    const size_t lds = (size_t)a.D * 2 * sizeof(float);
+    if (unif)
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, true>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
+                         st, a, (int)bps, W);
+    else
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, false>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
+                         st, a, (int)bps, W);
+    return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+  }
   const unsigned blocks = (unsigned)std::min<int64_t>(a.R, (int64_t)1 << 20);
-  if (a.D / V == (int64_t)NV * W * kWave)
+  if (unif)
     hipLaunchKernelGGL((rga_ln_modulate_mw<V, NV, true>), dim3(blocks), dim3(W * kWave), 0, st, a);
   else
     hipLaunchKernelGGL((rga_ln_modulate_mw<V, NV, false>), dim3(blocks), dim3(W * kWave), 0, st, a);

@@ -98,6 +98,27 @@ def test_fused_waves_per_row(ops, orc, D, W):
     run_fused(ops, orc, bigr[:, :, 8:8 + D], gate, upd, sc, sh, 1e-5, what="strided W=%d D=%d" % (W, D))
 
 
+@pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (16384, 4), (12296, 4)])
+@pytest.mark.parametrize("B,S", [(1, 16), (3, 9)])
+def test_fused_waves_per_row_shared_tables(ops, orc, D, W, B, S):
+    """Samples of at least 16 / W rows of up to 16384 elements: blocks of 16 waves hold 16 / W
+    rows of one sample and build its tables once (whole blocks, then a partial last block per
+    sample); both outputs and the statistics match the oracle, on contiguous and padded rows."""
+    from modulate_ln_amd import _native as N
+
+    assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D).W == W
+    g = torch.Generator().manual_seed(5 * D + S)
+    res = rand_bf16((B, S, D), g, std=2.0).to(DEV)
+    upd = rand_bf16((B, S, D), g).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="shared tables W=%d D=%d (%d,%d)" % (W, D, B, S))
+    bigr = rand_bf16((B, S, D + 16), g).to(DEV)
+    run_fused(ops, orc, bigr[:, :, 8:8 + D], gate, upd, sc, sh, 1e-5,
+              what="shared tables strided W=%d D=%d (%d,%d)" % (W, D, B, S))
+
+
 @pytest.mark.parametrize("B,S", [(1, 1), (3, 1), (1, 5), (3, 37), (2, 1024), (5, 301)])
 def test_fused_rows(ops, orc, B, S):
     g = torch.Generator().manual_seed(31 * B + S)
