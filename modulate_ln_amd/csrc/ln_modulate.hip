@@ -968,6 +968,11 @@ int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
   }
   if constexpr (V == 8) {
     if (unif) return launch_mw<V, NV, true, GATHER, RMS, TAIL>(a, W, st);
+  } else {
+    // 8-byte vectors: rows just past a multiple of 64 W vectors per lane step
+    // (D % 8 == 4) take an instantiation sized to their steps, which frees
+    // the registers of the unused ones
+    if (nvec <= (int64_t)10 * W * kWave) return launch_mw<V, 10, false, GATHER, RMS, TAIL>(a, W, st);
   }
   return launch_mw<V, NV, false, GATHER, RMS, TAIL>(a, W, st);
 }
