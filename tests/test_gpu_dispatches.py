@@ -1,0 +1,88 @@
+"""One call of an entry point is one kernel dispatch: the device kernels the torch profiler records
+around a prepared call (inputs and outputs made beforehand, so nothing else runs) are exactly
+one, and it is one of this library's kernels."""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+from test_gpu_parity import DEV, rand_bf16
+
+pytestmark = pytest.mark.gpu
+
+OURS = ("ln_modulate", "rga", "qk_", "gelu", "mod_", "temb")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import modulate_ln_amd as m
+
+    m._native.lib()  # fail loudly if the library is missing
+    return m
+
+
+def device_kernels(call):
+    """Names of the device kernels that run during call()."""
+    from torch.autograd import DeviceType
+    from torch.profiler import ProfilerActivity, profile
+
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        call()
+        torch.cuda.synchronize()
+    return [e.name for e in prof.events() if e.device_type == DeviceType.CUDA]
+
+
+def calls(ops):
+    g = torch.Generator().manual_seed(3)
+    B, S, D = 2, 256, 1024
+    x = rand_bf16((B, S, D), g).to(DEV)
+    xt = rand_bf16((B, D, S), g).to(DEV).transpose(1, 2)  # transposed storage, token stride 1
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+    upd = rand_bf16((B, S, D), g).to(DEV)
+    q = rand_bf16((B, S, 8, 128), g).to(DEV)
+    k = rand_bf16((B, S, 8, 128), g).to(DEV)
+    w = tuple(rand_bf16((128,), g, std=0.05).to(DEV) for _ in range(4))
+    qs = torch.tensor([0.25], dtype=torch.float32, device=DEV)
+    h = rand_bf16((512, 3072), g).to(DEV)
+    bias = rand_bf16((3072,), g, std=0.1).to(DEV)
+    table = torch.randn((6, D), generator=g).to(DEV)
+    temb = rand_bf16((B, S, 6, D), g).to(DEV)
+    ws = ops.ln_modulate_workspace(xt)
+    long_x = rand_bf16((1, 16, 16384), g).to(DEV)
+    long_s = rand_bf16((1, 16384), g, std=0.1).to(DEV)
+    return {
+        "ln_modulate": ops.ln_modulate(x, sc, sh, 1e-6, prepare=True),
+        "ln_modulate transposed": ops.ln_modulate(xt, sc, sh, 1e-6, prepare=True),
+        "ln_modulate_ws transposed": ops.ln_modulate(xt, sc, sh, 1e-6, workspace=ws, prepare=True),
+        "ln_modulate_noalloc transposed": ops.ln_modulate_noalloc(xt, sc, sh, 1e-6, out=torch.empty_like(x),
+                                                                  prepare=True),
+        "ln_modulate long rows": ops.ln_modulate(long_x, long_s, long_s, 1e-6, prepare=True),
+        "ln_modulate_fold": ops.ln_modulate_fold(x, sc, sh, 1e-6, prepare=True),
+        "ln_modulate_fp8": ops.ln_modulate_fp8(x, sc, sh, qs, 1e-6, prepare=True),
+        "rmsnorm_scale_shift": ops.rmsnorm_scale_shift(x, sc, sh, 1e-6, prepare=True),
+        "residual_gate_add": ops.residual_gate_add(x, gate, upd, prepare=True),
+        "residual_gate_add_ln_modulate": ops.residual_gate_add_ln_modulate(x, gate, upd, sc, sh, 1e-6,
+                                                                           prepare=True),
+        "qk_head_layernorm": ops.qk_head_layernorm(q, k, *w, 1e-6, prepare=True),
+        "qk_rmsnorm": ops.qk_rmsnorm(q, k, w[0], w[2], 1e-6, prepare=True),
+        "bias_gelu_tanh": ops.bias_gelu_tanh(h, bias, prepare=True),
+        "modulate_scale_shift": ops.modulate_scale_shift(x, sc, sh, prepare=True),
+        "temb_table_slices": ops.temb_table_slices(table, temb, prepare=True),
+    }
+
+
+def test_one_dispatch_per_call(ops):
+    prepared = calls(ops)
+    for p in prepared.values():  # first calls out of the way (module loads, lookups)
+        p()
+    torch.cuda.synchronize()
+    for name, p in prepared.items():
+        ks = device_kernels(p)
+        assert len(ks) == 1, (name, ks)
+        assert any(t in ks[0] for t in OURS), (name, ks)
