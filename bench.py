@@ -4,13 +4,16 @@
 A step is one pass of the GLM-Image (1, 4096, 4096) bf16 pair:
     h   = ln_modulate(x, scale, shift, eps=1e-5)
     out = residual_gate_add(x, gate, h)
-with inputs resident in HBM.  W untimed warm-up steps, then K timed steps
-between a synchronize on both sides.  Buffers rotate over enough sets
-(>= 1 GiB in total) that the 256 MB MALL cannot serve a step from cache.
+with inputs resident in HBM.  About 50 ms of back-to-back steps bring the
+device's clocks to their steady state after the host-side setup, then W
+untimed warm-up steps, then K timed steps between a synchronize on both
+sides.  Buffers rotate over enough sets (>= 1 GiB in total) that the 256 MB
+MALL cannot serve a step from cache.
 
 The step time comes from HIP events on the launch stream around the K
-timed steps.  Each kernel's average duration comes from its own loop of K
-back-to-back launches over the same rotated buffers, between events on the
+timed steps.  Each kernel's average duration comes from its own loop of
+back-to-back launches over the same rotated buffers (after two passes over
+every set and about 50 ms of the same launches), between events on the
 same stream; the roofline object reports the ln_modulate kernel (the
 kernel the headline metric names).  The CPU oracle
 (fixed-order fp32 mode) is timed on the host on the same step.
@@ -138,6 +141,21 @@ def main() -> int:
     log("workload %s, %d rotated buffer sets (%.2f GiB)" % (wl.name, NB, footprint / 2 ** 30))
 
     K, Wm = args.steps, args.warmup
+    # device warm-up before the W warm-up steps: about DEVICE_WARMUP_MS of back-to-back steps,
+    # so the timed steps do not run while the clocks are still rising from the host-side setup
+    # above (measured: a kernel takes ~10 % longer in its first tens of milliseconds of
+    # back-to-back work than from then on)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(5):
+        lnm_calls[i % NB]()
+        rga_calls[i % NB]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_ms = max(e0.elapsed_time(e1) / 5, 1e-4)
+    for i in range(int(min(20000, DEVICE_WARMUP_MS / per_ms))):
+        lnm_calls[i % NB]()
+        rga_calls[i % NB]()
     for i in range(Wm):
         lnm_calls[i % NB]()
         rga_calls[i % NB]()
@@ -182,7 +200,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) x with 1% x20 outliers, N(0,0.1) adaLN rows; see workloads.glm_square)",
         "config": {"workload": "ln_modulate + residual_gate_add, x (1,4096,4096) bf16, eps 1e-5",
-                   "B": B, "S": S, "D": D, "rotated_buffer_sets": NB,
+                   "B": B, "S": S, "D": D, "rotated_buffer_sets": NB, "device_warmup_ms": DEVICE_WARMUP_MS,
                    "step_bytes": lb + rb},
         "us_per_call": {"ln_modulate": round(lnm_us, 3), "residual_gate_add": round(rga_us, 3)},
         "achieved_GBps": {"ln_modulate": round(lnm_gbps, 1), "residual_gate_add": round(rga_gbps, 1)},
@@ -283,16 +301,31 @@ def stream_reference(dev, stream, log, nbytes=1 << 30):
     return out
 
 
-def time_loop(calls, n, stream, reps=20):
+DEVICE_WARMUP_MS = 50.0
+
+
+def time_loop(calls, n, stream, reps=20, warm_ms=DEVICE_WARMUP_MS):
     """µs per launch of back-to-back calls (rotating through calls): `reps` repetitions of
     n // reps launches each, events on the launch stream around every repetition, the
-    median repetition reported."""
+    median repetition reported.  Warm-up: two passes over every buffer set (at least 10
+    calls), so no set is touched for the first time inside the timed region, then about
+    `warm_ms` of back-to-back calls, so the device's clocks have left the state the host-side
+    setup between measurements leaves them in."""
     import statistics
 
     import torch
 
-    for c in calls[: min(len(calls), 4)]:
-        c()
+    for i in range(max(10, 2 * len(calls))):
+        calls[i % len(calls)]()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_ms = max(e0.elapsed_time(e1) / 10, 1e-4)
+    for i in range(int(min(20000, warm_ms / per_ms))):
+        calls[i % len(calls)]()
     reps = max(1, min(reps, n))
     per = max(1, n // reps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
