@@ -30,7 +30,7 @@ def device_kernels(call):
     from torch.profiler import ProfilerActivity, profile
 
     torch.cuda.synchronize()
-    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+    with profile(activities=[ProfilerActivity.CUDA], acc_events=True) as prof:
         call()
         torch.cuda.synchronize()
     return [e.name for e in prof.events() if e.device_type == DeviceType.CUDA]
