@@ -362,6 +362,20 @@ int launch_fused(const FusedArgs& a, hipStream_t st) {
   const int64_t target = per_cu * (cus > 0 ? cus : 256);
   int64_t bpb = (target + B - 1) / B;
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + kWpb - 1) / kWpb));
+  if constexpr (V == 8 && kWpb > 4) {
+    // 16-wave blocks of few rows would leave most compute units idle: one
+    // wave per row in blocks of their own (the long-row kernel at W = 1: the
+    // same lanes and merges, so the same bits) spreads them wider
+    if (2 * B * bpb < (cus > 0 ? cus : 256)) {
+      // that kernel's UNIF: all 8 of its steps full (D = 4096), not this one's NV
+      const dim3 grid((unsigned)std::min<int64_t>(a.R, (int64_t)1 << 20));
+      if (a.D == (int64_t)8 * V * kWave)
+        hipLaunchKernelGGL((rga_ln_modulate_mw<V, 8, true>), grid, dim3(kWave), 0, st, a);
+      else
+        hipLaunchKernelGGL((rga_ln_modulate_mw<V, 8, false>), grid, dim3(kWave), 0, st, a);
+      return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+    }
+  }
   hipLaunchKernelGGL((rga_ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)(B * bpb)), dim3(kWpb * kWave), lds,
                      st, a, (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;

@@ -98,6 +98,19 @@ def test_fused_waves_per_row(ops, orc, D, W):
     run_fused(ops, orc, bigr[:, :, 8:8 + D], gate, upd, sc, sh, 1e-5, what="strided W=%d D=%d" % (W, D))
 
 
+@pytest.mark.parametrize("D,S", [(4096, 64), (3584, 64), (3584, 300), (4096, 1024), (4096, 2048)])
+def test_fused_few_long_rows(ops, orc, D, S):
+    """Rows of 7-8 full vector steps, too few to fill the compute units with 16-wave blocks:
+    one wave per row in blocks of their own (same lanes and merges)."""
+    g = torch.Generator().manual_seed(3 * D + S)
+    res = rand_bf16((1, S, D), g, std=2.0).to(DEV)
+    upd = rand_bf16((1, S, D), g).to(DEV)
+    gate = rand_bf16((1, D), g, std=0.5).to(DEV)
+    sc = rand_bf16((1, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((1, D), g, std=0.1).to(DEV)
+    run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="few rows (1,%d,%d)" % (S, D))
+
+
 @pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (16384, 4), (12296, 4)])
 @pytest.mark.parametrize("B,S", [(1, 16), (3, 9)])
 def test_fused_waves_per_row_shared_tables(ops, orc, D, W, B, S):

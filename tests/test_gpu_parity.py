@@ -148,6 +148,18 @@ def test_ln_hidden_sizes(ops, orc, D):
     run_ln(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
 
 
+# rows of 7-8 full vector steps (D = 3584, 4096) take 16-wave blocks; with too few rows to fill
+# half the compute units that way they take the row kernel (same lanes and merges)
+@pytest.mark.parametrize("D", [3584, 4096])
+@pytest.mark.parametrize("B,S", [(1, 64), (2, 300), (1, 1024), (1, 2048)])
+def test_ln_few_long_rows(ops, orc, D, B, S):
+    g = torch.Generator().manual_seed(D + 7 * S + B)
+    x = rand_bf16((B, S, D), g, std=2.0, mean=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="few rows (%d,%d,%d)" % (B, S, D))
+
+
 # rows held by W = 1, 2, 4, 8, 16 waves (the cross-wave merge through LDS), with every lane
 # full (D = 4096 W) or a ragged last step (and V = 4 when D % 8 != 0)
 WAVE_ROWS = [(4096, 1), (4092, 1), (8192, 2), (4100, 2), (8200, 4), (16384, 4), (12296, 4), (32768, 8),

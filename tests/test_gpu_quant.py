@@ -73,6 +73,17 @@ def test_fp8_hidden_sizes(ops, orc, D):
     run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "D=%d" % D)
 
 
+@pytest.mark.parametrize("D,S", [(4096, 64), (3584, 300), (4096, 1024)])
+def test_fp8_few_long_rows(ops, orc, D, S):
+    """Rows of 7-8 full vector steps, too few to fill the compute units with 16-wave blocks:
+    the row kernel takes them (same lanes and merges)."""
+    g = torch.Generator().manual_seed(870 + D + S)
+    x = rand_bf16((1, S, D), g, std=3.0, mean=0.5).to(DEV)
+    sc = rand_bf16((1, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((1, D), g, std=0.1).to(DEV)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "few rows (1,%d,%d)" % (S, D))
+
+
 @pytest.mark.parametrize("D", [8192, 16384])
 def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D):
     """Rows of 2 and 4 waves, 19 per sample (blocks of 16 waves sharing the sample's tables,
