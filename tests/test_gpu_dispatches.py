@@ -86,3 +86,45 @@ def test_one_dispatch_per_call(ops):
         ks = device_kernels(p)
         assert len(ks) == 1, (name, ks)
         assert any(t in ks[0] for t in OURS), (name, ks)
+
+
+def test_kernel_choice(ops):
+    """The launch shape each layout class and size takes (on this device's compute units):
+    16-wave tabled blocks when they fill the chip, the row kernels when they would not, the
+    shared-table long-row kernel when its blocks fill three quarters of it, the workspace
+    kernel for transposed storage given a workspace."""
+    g = torch.Generator().manual_seed(5)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def ln(B, S, D):
+        x = rand_bf16((B, S, D), g).to(DEV)
+        s = rand_bf16((B, D), g, std=0.1).to(DEV)
+        return ops.ln_modulate(x, s, s, 1e-6, prepare=True)
+
+    def fused(B, S, D):
+        x = rand_bf16((B, S, D), g).to(DEV)
+        s = rand_bf16((B, D), g, std=0.1).to(DEV)
+        return ops.residual_gate_add_ln_modulate(x, s, x.clone(), s, s, 1e-6, prepare=True)
+
+    xt = rand_bf16((2, 2240, 1024), g).to(DEV).transpose(1, 2)
+    s2 = rand_bf16((2, 2240), g, std=0.1).to(DEV)
+    many = 16 * cus  # rows of 4096: 16-wave blocks, one per compute unit
+    long_rows = 4 * ((3 * cus + 3) // 4)  # rows of 16384: 4 per block, three quarters of the chip
+    expect = [
+        ("tabled", ln(1, many, 4096), "ln_modulate_tab<"),
+        ("few rows", ln(1, 128, 4096), "ln_modulate_rows<"),
+        ("shared tables", ln(1, long_rows, 16384), "ln_modulate_mwt<"),
+        ("few long rows", ln(1, 128, 16384), "ln_modulate_mw<"),
+        ("workspace", ops.ln_modulate(xt, s2, s2, 1e-6, workspace=ops.ln_modulate_workspace(xt), prepare=True),
+         "ln_modulate_trc<"),
+        ("transposed tiles", ops.ln_modulate(xt, s2, s2, 1e-6, prepare=True), "ln_modulate_tr<"),
+        ("fused tabled", fused(1, many, 4096), "rga_ln_modulate_tab<"),
+        ("fused few rows", fused(1, 128, 4096), "rga_ln_modulate_mw<"),
+        ("fused shared tables", fused(1, long_rows, 16384), "rga_ln_modulate_mwt<"),
+    ]
+    for name, p, kernel in expect:
+        p()
+    torch.cuda.synchronize()
+    for name, p, kernel in expect:
+        ks = device_kernels(p)
+        assert len(ks) == 1 and kernel in ks[0], (name, kernel, ks)

@@ -84,16 +84,19 @@ def test_fp8_few_long_rows(ops, orc, D, S):
     run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "few rows (1,%d,%d)" % (S, D))
 
 
-@pytest.mark.parametrize("D", [8192, 16384])
-def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D):
-    """Rows of 2 and 4 waves, 19 per sample (blocks of 16 waves sharing the sample's tables,
-    a partial last block per sample): the FP8 producer and the fold."""
+@pytest.mark.parametrize("D,W", [(8192, 2), (16384, 4)])
+def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D, W):
+    """Rows of 2 and 4 waves, enough per sample for blocks of 16 waves sharing the sample's
+    tables (a partial last block per sample): the FP8 producer and the fold."""
+    from test_gpu_parity import shared_table_rows
+
+    S = shared_table_rows(W, 2)
     g = torch.Generator().manual_seed(850 + D)
-    x = rand_bf16((2, 19, D), g, std=3.0, mean=0.5).to(DEV)
+    x = rand_bf16((2, S, D), g, std=3.0, mean=0.5).to(DEV)
     sc = rand_bf16((2, D), g, std=0.1).to(DEV)
     sh = rand_bf16((2, D), g, std=0.1).to(DEV)
-    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "shared tables D=%d" % D)
-    run_fold(ops, orc, x, sc, sh, 1e-6, "shared tables D=%d" % D)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "shared tables D=%d S=%d" % (D, S))
+    run_fold(ops, orc, x, sc, sh, 1e-6, "shared tables D=%d S=%d" % (D, S))
 
 
 def test_fp8_layouts_and_specials(ops, orc):

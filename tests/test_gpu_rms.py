@@ -80,12 +80,15 @@ def test_rms_hidden_sizes(ops, orc, D):
     run_rms(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
 
 
-@pytest.mark.parametrize("D", [8192, 16384])
-def test_rms_long_rows_shared_tables(ops, orc, D):
-    """Rows of 2 and 4 waves, 19 per sample: blocks of 16 waves hold 8 or 4 rows of a sample
-    and share its tables (a partial last block per sample)."""
+@pytest.mark.parametrize("D,W", [(8192, 2), (16384, 4)])
+def test_rms_long_rows_shared_tables(ops, orc, D, W):
+    """Rows of 2 and 4 waves, enough per sample that blocks of 16 waves hold 8 or 4 rows of a
+    sample and share its tables (a partial last block per sample)."""
+    from test_gpu_parity import shared_table_rows
+
+    S = shared_table_rows(W, 2)
     g = torch.Generator().manual_seed(950 + D)
-    x = rand_bf16((2, 19, D), g, std=3.0, mean=0.5).to(DEV)
+    x = rand_bf16((2, S, D), g, std=3.0, mean=0.5).to(DEV)
     sc = rand_bf16((2, D), g, std=0.1).to(DEV)
     sh = rand_bf16((2, D), g, std=0.1).to(DEV)
     run_rms(ops, orc, x, sc, sh, 1e-6, what="shared tables D=%d" % D)
