@@ -501,7 +501,7 @@ def test_gelu_wan_config_sampled_rows(ops, orc):
     bias = wl.tensors["bias"].to(DEV)
     y = ops.bias_gelu_tanh(x, bias)
     torch.cuda.synchronize()
-    rows = torch.linspace(0, x.shape[0] - 1, 2048).long()
+    rows = torch.linspace(0, x.shape[0] - 1, 4096).long()  # a quarter of the rows, first and last included
     want, val = orc.bias_gelu_tanh(bits(wl.tensors["x"][rows]), bits(wl.tensors["bias"]))
     got = f32(bits(y[rows.to(DEV)])).astype(np.float64)
     ref = f32(want).astype(np.float64)
