@@ -485,14 +485,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mw(LnArgs a) {
 // ln_modulate_mw's (the group's lanes g = 0 .. 64W - 1 in the same fixed
 // tree), and the tables hold the values its tail computes, so the bits are
 // the same.
-template <int NV, bool UNIF, bool RMS, int TAIL>
-__global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mwt(LnArgs a, int bps, int W) {
+template <int NV, bool UNIF, bool RMS, int TAIL, int TPB>
+__global__ __launch_bounds__(TPB) void ln_modulate_mwt(LnArgs a, int bps, int W) {
   constexpr int V = 8;
-  constexpr int kRuns = 2;  // adaLN vectors per thread: D <= 2 * 1024 * 8
+  constexpr int kRuns = (2048 + TPB - 1) / TPB;  // adaLN vectors per thread: D <= 2048 * 8
   extern __shared__ float4 tab[];  // [2][V / 4][D / V]
   __shared__ MwSlots slots;
   const int L = W * kWave;
-  const int P = kMaxWaves / W;
+  const int P = TPB / L;  // rows per block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = wave / W;              // the block's row group
   const int g = threadIdx.x - q * L;   // lane of the row's lane map
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mwt(LnArgs a, int 
   Vec<V> ts[kRuns], th[kRuns];
 #pragma unroll
   for (int i = 0; i < kRuns; ++i) {
-    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    const int j = i * TPB + (int)threadIdx.x;
 #pragma unroll
     for (int e = 0; e < V / 2; ++e) ts[i].w[e] = th[i].w[e] = 0u;
     if (j < nvec) {
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void ln_modulate_mwt(LnArgs a, int 
   }
 #pragma unroll
   for (int i = 0; i < kRuns; ++i) {
-    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    const int j = i * TPB + (int)threadIdx.x;
     if (j < nvec) put_tables<V>(tab, ts[i], th[i], j, nvec);
   }
   float mean, m2;
@@ -940,37 +940,50 @@ int launch_mw(const LnArgs& a, int W, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
-// 16-wave blocks of 16 / W rows of one sample, the sample's adaLN rows in LDS
-template <int NV, bool UNIF, bool RMS, int TAIL>
+// blocks of TPB threads holding TPB / (64 W) rows of one sample, the
+// sample's adaLN tables in LDS
+template <int NV, bool UNIF, bool RMS, int TAIL, int TPB>
 int launch_mwt(const LnArgs& a, int W, hipStream_t st) {
-  const int64_t P = kMaxWaves / W;
+  const int64_t P = TPB / (W * kWave);
   const int64_t B = a.R / a.S;
   const int64_t bps = (a.S + P - 1) / P;
   const size_t lds = (size_t)a.D * 2 * sizeof(float);
-  hipLaunchKernelGGL((ln_modulate_mwt<NV, UNIF, RMS, TAIL>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
-                     st, a, (int)bps, W);
+  hipLaunchKernelGGL((ln_modulate_mwt<NV, UNIF, RMS, TAIL, TPB>), dim3((unsigned)(B * bps)), dim3(TPB), lds, st, a,
+                     (int)bps, W);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
 // W waves per row (W = 2 .. 16): every lane holds at most 64 elements, NV
-// vector steps of V.  Vector-aligned rows of up to 16384 elements whose
-// samples have at least 16 / W rows share each sample's adaLN tables across
-// the rows of a block (ln_modulate_mwt; under 2^22 blocks of 1024 threads).
+// vector steps of V.  Vector-aligned rows of up to 16384 elements share each
+// sample's adaLN tables across the rows of a block (ln_modulate_mwt) when the
+// blocks fill at least three quarters of the compute units: 16-wave blocks
+// if they do (and leave no nearly empty last round), else 8-wave blocks of
+// half as many rows if those fill one round, else one row per block.
+// Measured, 16-wave blocks vs one row per block at D = 16384: 128 blocks
+// 10.66 vs 9.07 us, 192 blocks 11.38 vs 11.61, 256 13.4 vs 14.8, 320 (a
+// last round of 64) 21.5 vs 18.1, 384 22.6 vs 24.3, 512 26.3 vs 30.1;
+// 8-wave blocks of 2 rows at 256 blocks 8.02 vs 8.93.
 template <int V, bool GATHER, bool RMS, int TAIL>
 int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
   constexpr int NV = 64 / V;
   const int64_t nvec = a.D / V;
   const bool unif = V == 8 && nvec == (int64_t)NV * W * kWave;
   if constexpr (V == 8 && !GATHER) {
-    const int64_t P = kMaxWaves / W, blocks = (a.R / a.S) * ((a.S + P - 1) / P);
     const int cus = cu_count();
-    // (and only when those blocks fill at least three quarters of the compute
-    // units: fewer rows spread wider one per block.  Measured, shared tables vs
-    // one row per block: 128 blocks of 16384-element rows 10.66 vs 9.07 us,
-    // 192 blocks 11.38 vs 11.61; 8192-element rows 10.15 vs 9.14 and 10.84 vs
-    // 12.22)
-    if (W <= 4 && a.S >= P && blocks < ((int64_t)1 << 22) && 4 * blocks >= 3 * (cus > 0 ? cus : 256))
-      return unif ? launch_mwt<NV, true, RMS, TAIL>(a, W, st) : launch_mwt<NV, false, RMS, TAIL>(a, W, st);
+    const int64_t B = a.R / a.S;
+    const int64_t n = cus > 0 ? cus : 256;
+    // P rows per block: enough blocks for three quarters of the compute units,
+    // not too many for one launch, and (one block per compute unit at a time)
+    // a last round at least half full when there is more than one
+    auto fills = [&](int64_t P) {
+      const int64_t blocks = B * ((a.S + P - 1) / P), rem = blocks % n;
+      return a.S >= P && blocks < ((int64_t)1 << 22) && 4 * blocks >= 3 * n &&
+             (blocks <= n || rem == 0 || 2 * rem >= n);
+    };
+    if (W <= 4 && fills(kMaxWaves / W))
+      return unif ? launch_mwt<NV, true, RMS, TAIL, 1024>(a, W, st) : launch_mwt<NV, false, RMS, TAIL, 1024>(a, W, st);
+    if (W <= 4 && fills(kMaxWaves / 2 / W) && B * ((a.S + kMaxWaves / 2 / W - 1) / (kMaxWaves / 2 / W)) <= n)
+      return unif ? launch_mwt<NV, true, RMS, TAIL, 512>(a, W, st) : launch_mwt<NV, false, RMS, TAIL, 512>(a, W, st);
   }
   if constexpr (V == 8) {
     if (unif) return launch_mw<V, NV, true, GATHER, RMS, TAIL>(a, W, st);

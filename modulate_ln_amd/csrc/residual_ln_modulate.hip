@@ -261,14 +261,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mw(FusedArgs a
 // rows through the caches and widens and rounds them per element.  The gate
 // is needed before the statistics, so it comes through the caches as there.
 // Same lanes, merges and values, so the same bits.
-template <int NV, bool UNIF>
-__global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mwt(FusedArgs a, int bps, int W) {
+template <int NV, bool UNIF, int TPB>
+__global__ __launch_bounds__(TPB) void rga_ln_modulate_mwt(FusedArgs a, int bps, int W) {
   constexpr int V = 8;
-  constexpr int kRuns = 2;  // adaLN vectors per thread: D <= 2 * 1024 * 8
+  constexpr int kRuns = (2048 + TPB - 1) / TPB;  // adaLN vectors per thread: D <= 2048 * 8
   extern __shared__ float4 tab[];  // [2][V / 4][D / V]
   __shared__ MwSlots slots;
   const int L = W * kWave;
-  const int P = kMaxWaves / W;
+  const int P = TPB / L;  // rows per block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = wave / W;              // the block's row group
   const int g = threadIdx.x - q * L;   // lane of the row's lane map
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mwt(FusedArgs 
   Vec<V> ts[kRuns], th[kRuns];
 #pragma unroll
   for (int i = 0; i < kRuns; ++i) {
-    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    const int j = i * TPB + (int)threadIdx.x;
 #pragma unroll
     for (int e = 0; e < V / 2; ++e) ts[i].w[e] = th[i].w[e] = 0u;
     if (j < nvec) {
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rga_ln_modulate_mwt(FusedArgs 
   }
 #pragma unroll
   for (int i = 0; i < kRuns; ++i) {
-    const int j = i * (kMaxWaves * 64) + (int)threadIdx.x;
+    const int j = i * TPB + (int)threadIdx.x;
     if (j < nvec) put_tables<V>(tab, ts[i], th[i], j, nvec);
   }
   float mean, m2;
@@ -417,21 +417,39 @@ int dispatch_fused(const FusedArgs& a, hipStream_t st) {
 int dispatch_fused_mw(const FusedArgs& a, int W, hipStream_t st) {
   constexpr int V = 8, NV = 8;
   const bool unif = a.D / V == (int64_t)NV * W * kWave;
-  // rows of up to 16384 elements, samples of at least 16 / W rows: blocks of
-  // 16 waves sharing the sample's tables (under 2^22 blocks of 1024 threads)
-  const int64_t P = kMaxWaves / W, B = a.R / a.S, bps = (a.S + P - 1) / P;
+  // rows of up to 16384 elements: blocks holding several rows of one sample
+  // and sharing its tables when the blocks fill at least three quarters of the
+  // compute units (16 waves, else 8 in one round), else one row per block.
+  // Measured, 16-wave blocks vs one row per block at D = 16384: 128 blocks
+  // 20.37 vs 15.59 us, 256 blocks 25.6 vs 28.2, 320 (a last round of 64)
+  // 42.6 vs 36.7, 512 50.2 vs 54.0.
+  const int64_t B = a.R / a.S;
   const int cus = cu_count();
-  // (and only when those blocks fill at least three quarters of the compute
-  // units; fewer rows spread wider one per block: 128 blocks of 16384-element
-  // rows 20.37 vs 15.59 us, of 8192-element rows 19.41 vs 15.90)
-  if (W <= 4 && a.S >= P && B * bps < ((int64_t)1 << 22) && 4 * B * bps >= 3 * (cus > 0 ? cus : 256)) {
-    const size_t lds = (size_t)a.D * 2 * sizeof(float);
+  const size_t lds = (size_t)a.D * 2 * sizeof(float);
+  const int64_t n = cus > 0 ? cus : 256;
+  auto fills = [&](int64_t P) {  // as for ln_modulate's long rows
+    const int64_t blocks = B * ((a.S + P - 1) / P), rem = blocks % n;
+    return W <= 4 && a.S >= P && blocks < ((int64_t)1 << 22) && 4 * blocks >= 3 * n &&
+           (blocks <= n || rem == 0 || 2 * rem >= n);
+  };
+  if (fills(kMaxWaves / W)) {
+    const int64_t P = kMaxWaves / W, bps = (a.S + P - 1) / P;
     if (unif)
-      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, true>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
-                         st, a, (int)bps, W);
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, true, 1024>), dim3((unsigned)(B * bps)), dim3(1024), lds, st, a,
+                         (int)bps, W);
     else
-      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, false>), dim3((unsigned)(B * bps)), dim3(kMaxWaves * kWave), lds,
-                         st, a, (int)bps, W);
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, false, 1024>), dim3((unsigned)(B * bps)), dim3(1024), lds, st, a,
+                         (int)bps, W);
+    return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+  }
+  if (fills(kMaxWaves / 2 / W) && B * ((a.S + kMaxWaves / 2 / W - 1) / (kMaxWaves / 2 / W)) <= n) {
+    const int64_t P = kMaxWaves / 2 / W, bps = (a.S + P - 1) / P;
+    if (unif)
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, true, 512>), dim3((unsigned)(B * bps)), dim3(512), lds, st, a,
+                         (int)bps, W);
+    else
+      hipLaunchKernelGGL((rga_ln_modulate_mwt<NV, false, 512>), dim3((unsigned)(B * bps)), dim3(512), lds, st, a,
+                         (int)bps, W);
     return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
   }
   const unsigned blocks = (unsigned)std::min<int64_t>(a.R, (int64_t)1 << 20);

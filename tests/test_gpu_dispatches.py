@@ -110,17 +110,22 @@ def test_kernel_choice(ops):
     s2 = rand_bf16((2, 2240), g, std=0.1).to(DEV)
     many = 16 * cus  # rows of 4096: 16-wave blocks, one per compute unit
     long_rows = 4 * ((3 * cus + 3) // 4)  # rows of 16384: 4 per block, three quarters of the chip
+    half_rows = 2 * ((4 * cus + 4) // 5)  # 2 per 8-wave block fill 80 % of the chip, 4 per block too few
+    past_round = 4 * (cus + cus // 8)  # 4 per block: one round and an eighth
     expect = [
+        ("half-size shared tables", ln(1, half_rows, 16384), "ln_modulate_mwt<8, true, false, 0, 512>"),
+        ("nearly empty last round", ln(1, past_round, 16384), "ln_modulate_mw<"),
+        ("fused half-size shared tables", fused(1, half_rows, 16384), "rga_ln_modulate_mwt<8, true, 512>"),
         ("tabled", ln(1, many, 4096), "ln_modulate_tab<"),
         ("few rows", ln(1, 128, 4096), "ln_modulate_rows<"),
-        ("shared tables", ln(1, long_rows, 16384), "ln_modulate_mwt<"),
+        ("shared tables", ln(1, long_rows, 16384), "ln_modulate_mwt<8, true, false, 0, 1024>"),
         ("few long rows", ln(1, 128, 16384), "ln_modulate_mw<"),
         ("workspace", ops.ln_modulate(xt, s2, s2, 1e-6, workspace=ops.ln_modulate_workspace(xt), prepare=True),
          "ln_modulate_trc<"),
         ("transposed tiles", ops.ln_modulate(xt, s2, s2, 1e-6, prepare=True), "ln_modulate_tr<"),
         ("fused tabled", fused(1, many, 4096), "rga_ln_modulate_tab<"),
         ("fused few rows", fused(1, 128, 4096), "rga_ln_modulate_mw<"),
-        ("fused shared tables", fused(1, long_rows, 16384), "rga_ln_modulate_mwt<"),
+        ("fused shared tables", fused(1, long_rows, 16384), "rga_ln_modulate_mwt<8, true, 1024>"),
     ]
     for name, p, kernel in expect:
         p()

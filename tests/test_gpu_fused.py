@@ -112,7 +112,7 @@ def test_fused_few_long_rows(ops, orc, D, S):
 
 
 @pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (16384, 4), (12296, 4)])
-@pytest.mark.parametrize("B,S", [(1, None), (3, 9)])
+@pytest.mark.parametrize("B,S", [(1, None), (1, "half"), (3, 9)])
 def test_fused_waves_per_row_shared_tables(ops, orc, D, W, B, S):
     """Enough rows of up to 16384 elements: blocks of 16 waves hold 16 / W rows of one sample
     and build its tables once (whole blocks, then a partial last block per sample); with few
@@ -122,7 +122,7 @@ def test_fused_waves_per_row_shared_tables(ops, orc, D, W, B, S):
     from test_gpu_parity import shared_table_rows
 
     assert N.order_for(N.OP_RESIDUAL_GATE_ADD_LN_MODULATE, D).W == W
-    S = S if S is not None else shared_table_rows(W, B)
+    S = shared_table_rows(W, B, half=True) if S == "half" else (S if S is not None else shared_table_rows(W, B))
     g = torch.Generator().manual_seed(5 * D + S)
     res = rand_bf16((B, S, D), g, std=2.0).to(DEV)
     upd = rand_bf16((B, S, D), g).to(DEV)

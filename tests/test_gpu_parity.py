@@ -148,6 +148,18 @@ def test_ln_hidden_sizes(ops, orc, D):
     run_ln(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
 
 
+def test_ln_long_rows_last_round(ops, orc):
+    """16-wave blocks of 4 rows of 16384 elements would run one full round and an eighth of
+    another: one row per block instead (same lanes and merges)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = 4 * (cus + cus // 8)
+    g = torch.Generator().manual_seed(S)
+    x = rand_bf16((1, S, 16384), g, std=2.0).to(DEV)
+    sc = rand_bf16((1, 16384), g, std=0.1).to(DEV)
+    sh = rand_bf16((1, 16384), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="(1,%d,16384)" % S)
+
+
 # rows of 7-8 full vector steps (D = 3584, 4096) take 16-wave blocks; with too few rows to fill
 # half the compute units that way they take the row kernel (same lanes and merges)
 @pytest.mark.parametrize("D", [3584, 4096])
@@ -185,11 +197,17 @@ def test_ln_waves_per_row(ops, orc, D, W):
     run_ln(ops, orc, big[:, :, 1:1 + D], sc, sh, 1e-5, what="misaligned W=%d D=%d" % (W, D))
 
 
-def shared_table_rows(W: int, B: int) -> int:
+def shared_table_rows(W: int, B: int, half: bool = False) -> int:
     """Rows per sample that send rows of W = 2 or 4 waves to the shared-table kernel: blocks of
-    16 / W rows of one sample, at least three quarters of the compute units' worth of them, and
-    a partial last block in every sample."""
+    16 / W rows of one sample, at least three quarters of the compute units' worth of them (in
+    one round), and a partial last block in every sample.  half: 8-wave blocks of 8 / W rows
+    instead (too few rows for 16-wave blocks to fill three quarters of the compute units, enough
+    for 8-wave blocks to, in one round)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if half:
+        P = 8 // W
+        blocks = (4 * cus + 4) // 5  # 80 % of the compute units
+        return P * ((blocks + B - 1) // B) - 1
     P = 16 // W
     blocks = (3 * cus + 3) // 4
     return P * ((blocks + B - 1) // B) + P // 2
@@ -200,12 +218,12 @@ def shared_table_rows(W: int, B: int) -> int:
 # row per block, so the order (and the bits) stay the same.  Whole blocks, a partial last block
 # per sample, several samples; fewer rows per sample (S given) take one row per block.
 @pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (8200, 4), (16384, 4), (12296, 4)])
-@pytest.mark.parametrize("B,S", [(1, None), (2, None), (3, 9)])
+@pytest.mark.parametrize("B,S", [(1, None), (2, None), (1, "half"), (3, 9)])
 def test_ln_waves_per_row_shared_tables(ops, orc, D, W, B, S):
     from modulate_ln_amd import _native as N
 
     assert N.order_for(N.OP_LN_MODULATE, D).W == W
-    S = S if S is not None else shared_table_rows(W, B)
+    S = shared_table_rows(W, B, half=True) if S == "half" else (S if S is not None else shared_table_rows(W, B))
     g = torch.Generator().manual_seed(11 * D + S)
     x = rand_bf16((B, S, D), g, std=2.0, mean=0.25).to(DEV)
     sc = rand_bf16((B, D), g, std=0.1).to(DEV)
