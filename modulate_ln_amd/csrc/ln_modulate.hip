@@ -222,18 +222,30 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #ifndef ADALN_TAB_XF32_FP8
 #define ADALN_TAB_XF32_FP8 0
 #endif
-template <int NV, bool UNIF, bool RMS, int TAIL>
+// MANY: more rows than the 16-wave shape holds at one per wave (16 per
+// compute unit); those take the fold's shape instead, a prefetched next row
+// in 4-wave blocks at three per compute unit.  Measured at D = 4096, 16-wave
+// blocks vs the prefetch: 4352 rows 18.06 vs 14.08 us, 5120 rows 19.58 vs
+// 15.35, 8192 rows 26.28 vs 24.46; FP8 20.95 vs 15.25, 20.89 vs 16.02,
+// 23.82 vs 23.23 (at 4096 rows the 16-wave blocks stay: 11.52 vs 12.46).
+#ifndef ADALN_TAB_BPC_MANY
+#define ADALN_TAB_BPC_MANY 3
+#endif
+template <int NV, bool UNIF, bool RMS, int TAIL, bool MANY = false>
 struct TabShape {
   static constexpr bool kLong = NV == 7 || NV == 8;
-  static constexpr int kBpcLong = TAIL == kTailFp8    ? ADALN_TAB_BPC_FP8
+  static constexpr int kBpcLong = MANY                ? ADALN_TAB_BPC_MANY
+                                  : TAIL == kTailFp8  ? ADALN_TAB_BPC_FP8
                                   : TAIL == kTailFold ? ADALN_TAB_BPC_FOLD
                                   : RMS               ? ADALN_TAB_BPC_RMS
                                                       : ADALN_TAB_BPC_LN;
-  static constexpr bool kXf32Long = TAIL == kTailFp8    ? ADALN_TAB_XF32_FP8
+  static constexpr bool kXf32Long = MANY                ? false
+                                    : TAIL == kTailFp8  ? ADALN_TAB_XF32_FP8
                                     : TAIL == kTailFold ? ADALN_TAB_XF32_FOLD
                                     : RMS               ? ADALN_TAB_XF32_RMS
                                                         : ADALN_TAB_XF32_LN;
-  static constexpr bool kPfLong = TAIL == kTailFp8    ? ADALN_TAB_PF_FP8
+  static constexpr bool kPfLong = MANY                ? true
+                                  : TAIL == kTailFp8  ? ADALN_TAB_PF_FP8
                                   : TAIL == kTailFold ? ADALN_TAB_PF_FOLD
                                   : RMS               ? ADALN_TAB_PF_RMS
                                                       : ADALN_TAB_PF_LN;
@@ -258,11 +270,12 @@ struct TabShape {
 };
 
 
-template <int V, int NV, bool UNIF, bool RMS, int TAIL>
-__global__ __launch_bounds__((TabShape<NV, UNIF, RMS, TAIL>::kWpb * 64)) void ln_modulate_tab(LnArgs a, int bpb) {
-  constexpr int kWpb = TabShape<NV, UNIF, RMS, TAIL>::kWpb;
-  constexpr bool kPrefetch = TabShape<NV, UNIF, RMS, TAIL>::kPrefetch;
-  constexpr bool kXf32 = TabShape<NV, UNIF, RMS, TAIL>::kXf32;
+template <int V, int NV, bool UNIF, bool RMS, int TAIL, bool MANY = false>
+__global__ __launch_bounds__((TabShape<NV, UNIF, RMS, TAIL, MANY>::kWpb * 64)) void ln_modulate_tab(LnArgs a,
+                                                                                                  int bpb) {
+  constexpr int kWpb = TabShape<NV, UNIF, RMS, TAIL, MANY>::kWpb;
+  constexpr bool kPrefetch = TabShape<NV, UNIF, RMS, TAIL, MANY>::kPrefetch;
+  constexpr bool kXf32 = TabShape<NV, UNIF, RMS, TAIL, MANY>::kXf32;
   extern __shared__ float4 tab[];  // [2][V/4][nvec] float4: bf16(1+scale), then shift
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -996,14 +1009,16 @@ int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
   return launch_mw<V, NV, false, GATHER, RMS, TAIL>(a, W, st);
 }
 
-template <int V, int NV, bool UNIF, bool RMS, int TAIL>
+template <int V, int NV, bool UNIF, bool RMS, int TAIL, bool MANY = false>
 int launch_tab(const LnArgs& a, hipStream_t st) {
-  // TabShape<NV, UNIF, RMS, TAIL>::kBlocksPerCu blocks per compute unit in total, at least one row per wave
+  using Shape = TabShape<NV, UNIF, RMS, TAIL, MANY>;
+  // Shape::kBlocksPerCu blocks per compute unit in total, at least one row per wave
   const int64_t B = a.R / a.S;
   const int cus = cu_count();
-  const int64_t target = (int64_t)TabShape<NV, UNIF, RMS, TAIL>::kBlocksPerCu * (cus > 0 ? cus : 256);
+  const int64_t n = cus > 0 ? cus : 256;
+  const int64_t target = (int64_t)Shape::kBlocksPerCu * n;
   int64_t bpb = (target + B - 1) / B;
-  constexpr int kWpb = TabShape<NV, UNIF, RMS, TAIL>::kWpb;
+  constexpr int kWpb = Shape::kWpb;
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + kWpb - 1) / kWpb));
   const int64_t blocks = B * bpb;
   if constexpr (kWpb > 4) {
@@ -1012,11 +1027,13 @@ int launch_tab(const LnArgs& a, hipStream_t st) {
     // spreads them wider.  Measured at D = 4096, tabled vs row kernel: 128 rows
     // 7.80 vs 5.47 us, 1024 rows 8.28 vs 6.34, 2048 rows 8.57 vs 8.50, 3072
     // rows 9.36 vs 12.16.
-    if (2 * blocks < (cus > 0 ? cus : 256)) return launch_rows<V, 8, false, RMS, TAIL>(a, st);
+    if (2 * blocks < n) return launch_rows<V, 8, false, RMS, TAIL>(a, st);
+    // more rows than one per wave: the prefetching shape (MANY above)
+    if (a.R > (int64_t)kWpb * n) return launch_tab<V, NV, UNIF, RMS, TAIL, true>(a, st);
   }
   const size_t lds = (size_t)2 * a.D * sizeof(float);
-  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS, TAIL>), dim3((unsigned)blocks), dim3(kWpb * kWave), lds, st, a,
-                     (int)bpb);
+  hipLaunchKernelGGL((ln_modulate_tab<V, NV, UNIF, RMS, TAIL, MANY>), dim3((unsigned)blocks), dim3(kWpb * kWave), lds,
+                     st, a, (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 

@@ -90,7 +90,8 @@ def test_one_dispatch_per_call(ops):
 
 def test_kernel_choice(ops):
     """The launch shape each layout class and size takes (on this device's compute units):
-    16-wave tabled blocks when they fill the chip, the row kernels when they would not, the
+    16-wave tabled blocks when they fill the chip with one row per wave, 4-wave prefetching
+    ones for more rows, the row kernels when they would not fill it, the
     shared-table long-row kernel when its blocks fill three quarters of it, the workspace
     kernel for transposed storage given a workspace."""
     g = torch.Generator().manual_seed(5)
@@ -116,7 +117,8 @@ def test_kernel_choice(ops):
         ("half-size shared tables", ln(1, half_rows, 16384), "ln_modulate_mwt<8, true, false, 0, 512>"),
         ("nearly empty last round", ln(1, past_round, 16384), "ln_modulate_mw<"),
         ("fused half-size shared tables", fused(1, half_rows, 16384), "rga_ln_modulate_mwt<8, true, 512>"),
-        ("tabled", ln(1, many, 4096), "ln_modulate_tab<"),
+        ("tabled", ln(1, many, 4096), "ln_modulate_tab<8, 8, true, false, 0, false>"),
+        ("tabled, more rows than waves", ln(1, many + 64, 4096), "ln_modulate_tab<8, 8, true, false, 0, true>"),
         ("few rows", ln(1, 128, 4096), "ln_modulate_rows<"),
         ("shared tables", ln(1, long_rows, 16384), "ln_modulate_mwt<8, true, false, 0, 1024>"),
         ("few long rows", ln(1, 128, 16384), "ln_modulate_mw<"),

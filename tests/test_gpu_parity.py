@@ -172,6 +172,19 @@ def test_ln_few_long_rows(ops, orc, D, B, S):
     run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="few rows (%d,%d,%d)" % (B, S, D))
 
 
+# more rows of 7-8 full steps than 16-wave blocks hold at one per wave: 4-wave blocks that
+# prefetch the next row take them (same lanes and merges); ragged last blocks, several samples
+@pytest.mark.parametrize("D,B,extra", [(4096, 1, 257), (3584, 2, 3), (4096, 3, 1000)])
+def test_ln_many_long_rows(ops, orc, D, B, extra):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = (16 * cus + extra + B - 1) // B
+    g = torch.Generator().manual_seed(D + S + B)
+    x = rand_bf16((B, S, D), g, std=2.0, mean=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="many rows (%d,%d,%d)" % (B, S, D))
+
+
 # rows held by W = 1, 2, 4, 8, 16 waves (the cross-wave merge through LDS), with every lane
 # full (D = 4096 W) or a ragged last step (and V = 4 when D % 8 != 0)
 WAVE_ROWS = [(4096, 1), (4092, 1), (8192, 2), (4100, 2), (8200, 4), (16384, 4), (12296, 4), (32768, 8),

@@ -84,6 +84,19 @@ def test_fp8_few_long_rows(ops, orc, D, S):
     run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "few rows (1,%d,%d)" % (S, D))
 
 
+@pytest.mark.parametrize("D,B", [(4096, 1), (3584, 2)])
+def test_fp8_many_long_rows(ops, orc, D, B):
+    """More rows of 7-8 full vector steps than 16-wave blocks hold at one per wave: 4-wave
+    blocks that prefetch the next row (same lanes and merges)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = (16 * cus + 301 + B - 1) // B
+    g = torch.Generator().manual_seed(880 + D + S)
+    x = rand_bf16((B, S, D), g, std=3.0, mean=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "many rows (%d,%d,%d)" % (B, S, D))
+
+
 @pytest.mark.parametrize("D,W", [(8192, 2), (16384, 4)])
 def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D, W):
     """Rows of 2 and 4 waves, enough per sample for blocks of 16 waves sharing the sample's
