@@ -75,7 +75,12 @@ struct FusedArgs {
 #ifndef ADALN_FUSED_WPB
 #define ADALN_FUSED_WPB 16
 #endif
-template <int NV, bool UNIF>
+// MANY: more rows than 16-wave blocks hold at one per wave (16 per compute
+// unit) keep 4-wave blocks; a second round of 16-wave blocks starts only as
+// whole blocks drain.  At D = 4096, 16- vs 4-wave blocks: 4160 rows 33.1 vs
+// 27.5 us, 5120 rows 37.7 vs 32.5, 16384 rows 103.5 vs 100.0 (prefetching
+// the next row instead: 29.3, 33.6, 99.1).
+template <int NV, bool UNIF, bool MANY = false>
 struct FusedShape {
   static constexpr bool kPrefetch = NV <= ADALN_FUSED_PF_MAX;
   static constexpr bool kXf32 = NV <= ADALN_FUSED_XF32_MAX;
@@ -85,14 +90,14 @@ struct FusedShape {
   // unit ((1,4096,4096): 23.6 us, against 24.7 with 4-wave blocks and 30.6
   // with 12); rows with a partial last vector step or more than 8 vectors
   // per lane keep 4 (their VGPRs would not fit a larger block's budget)
-  static constexpr int kWpb = (!kPrefetch && UNIF && NV <= 8) ? ADALN_FUSED_WPB : 4;
+  static constexpr int kWpb = (!MANY && !kPrefetch && UNIF && NV <= 8) ? ADALN_FUSED_WPB : 4;
 };
 
-template <int V, int NV, bool UNIF>
-__global__ __launch_bounds__((FusedShape<NV, UNIF>::kWpb * 64)) void rga_ln_modulate_tab(FusedArgs a, int bpb) {
-  constexpr int kWpb = FusedShape<NV, UNIF>::kWpb;
-  constexpr bool kPrefetch = FusedShape<NV, UNIF>::kPrefetch;
-  constexpr bool kXf32 = FusedShape<NV, UNIF>::kXf32;
+template <int V, int NV, bool UNIF, bool MANY = false>
+__global__ __launch_bounds__((FusedShape<NV, UNIF, MANY>::kWpb * 64)) void rga_ln_modulate_tab(FusedArgs a, int bpb) {
+  constexpr int kWpb = FusedShape<NV, UNIF, MANY>::kWpb;
+  constexpr bool kPrefetch = FusedShape<NV, UNIF, MANY>::kPrefetch;
+  constexpr bool kXf32 = FusedShape<NV, UNIF, MANY>::kXf32;
   extern __shared__ float4 tab[];  // [3][V/4][nvec] float4: bf16(1+scale), shift, gate
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -349,13 +354,14 @@ __global__ __launch_bounds__(TPB) void rga_ln_modulate_mwt(FusedArgs a, int bps,
 
 constexpr int64_t kLdsPerCu = 160 * 1024;
 
-template <int V, int NV, bool UNIF>
+template <int V, int NV, bool UNIF, bool MANY = false>
 int launch_fused(const FusedArgs& a, hipStream_t st) {
+  using Shape = FusedShape<NV, UNIF, MANY>;
   const int64_t B = a.R / a.S;
   const size_t lds = (size_t)3 * a.D * sizeof(float);
-  constexpr int kWpb = FusedShape<NV, UNIF>::kWpb;
+  constexpr int kWpb = Shape::kWpb;
   // waves per compute unit: 4 per block of the 4-wave layout, as many blocks as LDS allows
-  const int64_t waves_per_cu = 4 * std::max<int64_t>(1, std::min<int64_t>(FusedShape<NV, UNIF>::kBlocksPerCu,
+  const int64_t waves_per_cu = 4 * std::max<int64_t>(1, std::min<int64_t>(Shape::kBlocksPerCu,
                                                                            kLdsPerCu / (int64_t)lds));
   const int64_t per_cu = std::max<int64_t>(1, waves_per_cu / kWpb);
   const int cus = cu_count();
@@ -375,8 +381,10 @@ int launch_fused(const FusedArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((rga_ln_modulate_mw<V, 8, false>), grid, dim3(kWave), 0, st, a);
       return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
     }
+    // more rows than one per wave: 4-wave blocks (MANY above)
+    if (a.R > (int64_t)kWpb * (cus > 0 ? cus : 256)) return launch_fused<V, NV, UNIF, true>(a, st);
   }
-  hipLaunchKernelGGL((rga_ln_modulate_tab<V, NV, UNIF>), dim3((unsigned)(B * bpb)), dim3(kWpb * kWave), lds,
+  hipLaunchKernelGGL((rga_ln_modulate_tab<V, NV, UNIF, MANY>), dim3((unsigned)(B * bpb)), dim3(kWpb * kWave), lds,
                      st, a, (int)bpb);
   return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }

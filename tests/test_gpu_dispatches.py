@@ -125,7 +125,8 @@ def test_kernel_choice(ops):
         ("workspace", ops.ln_modulate(xt, s2, s2, 1e-6, workspace=ops.ln_modulate_workspace(xt), prepare=True),
          "ln_modulate_trc<"),
         ("transposed tiles", ops.ln_modulate(xt, s2, s2, 1e-6, prepare=True), "ln_modulate_tr<"),
-        ("fused tabled", fused(1, many, 4096), "rga_ln_modulate_tab<"),
+        ("fused tabled", fused(1, many, 4096), "rga_ln_modulate_tab<8, 8, true, false>"),
+        ("fused tabled, more rows than waves", fused(1, many + 64, 4096), "rga_ln_modulate_tab<8, 8, true, true>"),
         ("fused few rows", fused(1, 128, 4096), "rga_ln_modulate_mw<"),
         ("fused shared tables", fused(1, long_rows, 16384), "rga_ln_modulate_mwt<8, true, 1024>"),
     ]

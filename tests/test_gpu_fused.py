@@ -111,6 +111,21 @@ def test_fused_few_long_rows(ops, orc, D, S):
     run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="few rows (1,%d,%d)" % (S, D))
 
 
+@pytest.mark.parametrize("D,B", [(4096, 1), (3584, 2), (4096, 3)])
+def test_fused_many_long_rows(ops, orc, D, B):
+    """More rows of 7-8 full vector steps than 16-wave blocks hold at one per wave: 4-wave
+    blocks (same lanes and merges); ragged last blocks, several samples."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = (16 * cus + 123 + B - 1) // B
+    g = torch.Generator().manual_seed(5 * D + S + B)
+    res = rand_bf16((B, S, D), g, std=2.0).to(DEV)
+    upd = rand_bf16((B, S, D), g).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="many rows (%d,%d,%d)" % (B, S, D))
+
+
 @pytest.mark.parametrize("D,W", [(8192, 2), (5120, 2), (16384, 4), (12296, 4)])
 @pytest.mark.parametrize("B,S", [(1, None), (1, "half"), (3, 9)])
 def test_fused_waves_per_row_shared_tables(ops, orc, D, W, B, S):
