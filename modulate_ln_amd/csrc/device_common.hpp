@@ -31,6 +31,23 @@ inline int cu_count() {
   return n;
 }
 
+// Blocks of one kernel that a compute unit of the current device holds at
+// once (its registers, LDS and waves; lds: the most dynamic LDS a block of it
+// asks for), cached per device in the caller's array; 0 when the query fails.
+// A launch sized for more blocks per compute unit than this runs its last
+// blocks in a second round.
+template <typename F>
+inline int resident_blocks_per_cu(std::atomic<int>* cache, F kernel, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n <= 0) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  A 32-bit word holds two consecutive bf16 elements: the
 // lower-addressed one in bits 0..15.

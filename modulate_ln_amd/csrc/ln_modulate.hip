@@ -1012,13 +1012,24 @@ int dispatch_mw(const LnArgs& a, int W, hipStream_t st) {
 template <int V, int NV, bool UNIF, bool RMS, int TAIL, bool MANY = false>
 int launch_tab(const LnArgs& a, hipStream_t st) {
   using Shape = TabShape<NV, UNIF, RMS, TAIL, MANY>;
-  // Shape::kBlocksPerCu blocks per compute unit in total, at least one row per wave
+  constexpr int kWpb = Shape::kWpb;
+  // Shape::kBlocksPerCu blocks per compute unit in total, at least one row per
+  // wave, and no more than a compute unit holds at once: the instantiations
+  // for rows with a partial last step take more registers (4-6 steps of 8:
+  // 100-122 VGPRs, 4 waves per SIMD where the launch is sized for 5; 7-8
+  // steps: 134-150 VGPRs, 3 where it is sized for 4).  Measured, sized vs
+  // capped: (1,5120,2240) 12.80 vs 10.97 us, (1,5120,1800) 10.44 vs 9.26,
+  // (1,4096,4000) 16.09 vs 14.73, (1,8192,4000) 29.71 vs 28.13; RMSNorm
+  // (1,4096,4000) 15.49 vs 13.36; FP8 (1,5120,2240) 14.23 vs 11.54.
+  static std::atomic<int> held[64];
+  const int h = resident_blocks_per_cu(held, ln_modulate_tab<V, NV, UNIF, RMS, TAIL, MANY>, kWpb * kWave,
+                                       (size_t)2 * NV * kWave * V * sizeof(float));
+  const int64_t bpc = h > 0 ? std::min<int64_t>(Shape::kBlocksPerCu, h) : Shape::kBlocksPerCu;
   const int64_t B = a.R / a.S;
   const int cus = cu_count();
   const int64_t n = cus > 0 ? cus : 256;
-  const int64_t target = (int64_t)Shape::kBlocksPerCu * n;
+  const int64_t target = bpc * n;
   int64_t bpb = (target + B - 1) / B;
-  constexpr int kWpb = Shape::kWpb;
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + kWpb - 1) / kWpb));
   const int64_t blocks = B * bpb;
   if constexpr (kWpb > 4) {

@@ -111,6 +111,19 @@ def test_fused_few_long_rows(ops, orc, D, S):
     run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="few rows (1,%d,%d)" % (S, D))
 
 
+@pytest.mark.parametrize("B,S,D", [(1, 4096, 2048), (1, 4096, 2240), (2, 2000, 3072)])
+def test_fused_held_blocks(ops, orc, B, S, D):
+    """One row per wave at the shape's own sizing, more blocks than a compute unit holds
+    (registers): the launch is sized to what is held, so some waves walk two rows."""
+    g = torch.Generator().manual_seed(7 * D + S + B)
+    res = rand_bf16((B, S, D), g, std=2.0).to(DEV)
+    upd = rand_bf16((B, S, D), g).to(DEV)
+    gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_fused(ops, orc, res, gate, upd, sc, sh, 1e-6, what="held blocks (%d,%d,%d)" % (B, S, D))
+
+
 @pytest.mark.parametrize("D,B", [(4096, 1), (3584, 2), (4096, 3)])
 def test_fused_many_long_rows(ops, orc, D, B):
     """More rows of 7-8 full vector steps than 16-wave blocks hold at one per wave: 4-wave

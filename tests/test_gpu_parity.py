@@ -185,6 +185,18 @@ def test_ln_many_long_rows(ops, orc, D, B, extra):
     run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="many rows (%d,%d,%d)" % (B, S, D))
 
 
+# rows with a partial last vector step whose instantiations hold fewer blocks per compute unit
+# than their shape asks for: the launch is sized to what is held (same lanes and merges), so
+# some waves walk two rows
+@pytest.mark.parametrize("B,S,D", [(1, 5120, 2240), (1, 4096, 4000), (2, 2600, 1800), (3, 1800, 3000)])
+def test_ln_ragged_rows_held_blocks(ops, orc, B, S, D):
+    g = torch.Generator().manual_seed(B * S + D)
+    x = rand_bf16((B, S, D), g, std=2.0, mean=0.5).to(DEV)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    run_ln(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="held blocks (%d,%d,%d)" % (B, S, D))
+
+
 # rows held by W = 1, 2, 4, 8, 16 waves (the cross-wave merge through LDS), with every lane
 # full (D = 4096 W) or a ragged last step (and V = 4 when D % 8 != 0)
 WAVE_ROWS = [(4096, 1), (4092, 1), (8192, 2), (4100, 2), (8200, 4), (16384, 4), (12296, 4), (32768, 8),

@@ -97,6 +97,15 @@ def test_fp8_many_long_rows(ops, orc, D, B):
     run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "many rows (%d,%d,%d)" % (B, S, D))
 
 
+def test_fp8_ragged_rows_held_blocks(ops, orc):
+    """Rows with a partial last step, the launch sized to the blocks a compute unit holds."""
+    g = torch.Generator().manual_seed(8855)
+    x = rand_bf16((1, 5120, 2240), g, std=3.0, mean=0.5).to(DEV)
+    sc = rand_bf16((1, 2240), g, std=0.1).to(DEV)
+    sh = rand_bf16((1, 2240), g, std=0.1).to(DEV)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.037, "held blocks (1,5120,2240)")
+
+
 @pytest.mark.parametrize("D,W", [(8192, 2), (16384, 4)])
 def test_fp8_and_fold_long_rows_shared_tables(ops, orc, D, W):
     """Rows of 2 and 4 waves, enough per sample for blocks of 16 waves sharing the sample's
