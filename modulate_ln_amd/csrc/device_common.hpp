@@ -25,7 +25,10 @@ inline int cu_count() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();  // not left for the launch check that follows
+      return 0;
+    }
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
@@ -42,7 +45,10 @@ inline int resident_blocks_per_cu(std::atomic<int>* cache, F kernel, int threads
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n <= 0) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();  // not left for the launch check that follows
+      return 0;
+    }
     cache[dev].store(n, std::memory_order_relaxed);
   }
   return n;

@@ -1178,7 +1178,10 @@ int coop_resident_blocks(int dev) {
   const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ln_modulate_trc<NV, ONE>, 512, 0) ==
                       hipSuccess &&
                   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
-  if ((cur != dev && hipSetDevice(cur) != hipSuccess) || !ok) return 0;
+  if ((cur != dev && hipSetDevice(cur) != hipSuccess) || !ok) {
+    (void)hipGetLastError();  // not left for the launch check that follows
+    return 0;
+  }
   v = per_cu * cus;
   if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
   return v;
