@@ -162,9 +162,11 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 // once, one row per wave and four waves per SIMD, with the fp32 copy (108
 // VGPRs): their VALU work per row is what the last waves to get their data
 // wait on, and a prefetched second row costs the fp32 copy (two waves per
-// SIMD would remain).  The FP8 stage runs every row in flight too, but
-// re-widens x (an fp32 copy would spill at 128 VGPRs): 13.23 us against
-// 13.40 with the prefetch at two blocks per compute unit (15.66 at three).
+// SIMD would remain).  The FP8 stage runs every row in flight too, with the
+// fp32 copy (104 VGPRs once its table values are read at their own step):
+// 12.57-12.75 us against 13.07-13.31 re-widening x, which once ran 13.23 us
+// against 13.40 with the prefetch at two blocks per compute unit (15.66 at
+// three).
 // The fold keeps the prefetch at three blocks per compute unit.  Shorter rows keep one buffer and an fp32
 // copy of x at five blocks per compute unit; longer rows (up to 16 vectors
 // per lane, 64 KiB of tables) keep one buffer and re-widen.
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void ln_modulate_rows(LnArgs a) {
 #define ADALN_TAB_BPC_FP8 2
 #endif
 #ifndef ADALN_TAB_XF32_FP8
-#define ADALN_TAB_XF32_FP8 0
+#define ADALN_TAB_XF32_FP8 1
 #endif
 // MANY: more rows than the 16-wave shape holds at one per wave (16 per
 // compute unit); those take the fold's shape instead, a prefetched next row

@@ -183,16 +183,22 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
   // branch that would split its schedule
   auto steps = [&](auto no_nan_c) {
     constexpr bool NO_NAN = decltype(no_nan_c)::value;
-    read_tab(0);
+    // the FP8 stage over rows of 7-8 steps with an fp32 copy of x reads each
+    // step's table values at that step: the look-ahead's 16 VGPRs would push
+    // it past the 128 of a 16-wave block (44 bytes of spill)
+    constexpr bool kAhead = !(TAIL == kTailFp8 && kXf32 && NV >= 7);
+    if constexpr (kAhead) read_tab(0);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
+      if constexpr (!kAhead) read_tab(k);
       float4 oc[V / 4], hc[V / 4];
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) {
         oc[q] = ot[q];
         hc[q] = ht[q];
       }
-      if (k + 1 < NV) read_tab(k + 1);
+      if constexpr (kAhead)
+        if (k + 1 < NV) read_tab(k + 1);
       const int v = k * kWave + lane;
       if (UNIF || v < nvec) {
         uint32_t o[V / 2];  // bf16 pairs
