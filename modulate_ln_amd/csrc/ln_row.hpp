@@ -183,14 +183,18 @@ __device__ __forceinline__ void normalize_row(const Vec<V>* buf, const float4* t
   // branch that would split its schedule
   auto steps = [&](auto no_nan_c) {
     constexpr bool NO_NAN = decltype(no_nan_c)::value;
-    // the FP8 stage over rows of 7-8 steps with an fp32 copy of x reads each
-    // step's table values at that step: the look-ahead's 16 VGPRs would push
-    // it past the 128 of a 16-wave block (44 bytes of spill).  So does RMSNorm
-    // over rows of 4-6 steps with a partial last step: 78-88 VGPRs instead of
-    // 96-118, 5 waves per SIMD as its launch asks ((1,5120,2240) 9.55 vs
-    // 8.51 us; the LayerNorm chain there gains too, but loses 2.3 % at
-    // (2,1024,2240), and keeps the look-ahead)
-    constexpr bool kAhead = !(TAIL == kTailFp8 && kXf32 && NV >= 7) && !(RMS && !UNIF && NV >= 4 && NV <= 6);
+    // Table values are read one step ahead, except where the registers that
+    // takes cost waves: the FP8 stage over rows of 7-8 steps with an fp32
+    // copy of x (the look-ahead would push it past the 128 VGPRs of a
+    // 16-wave block, 44 bytes of spill); rows of 7-8 steps with a partial
+    // last step (102-112 VGPRs instead of 138-150: 4 waves per SIMD, as the
+    // launch asks, instead of 3; (1,4096,3840) 14.24 vs 13.38 us, RMSNorm
+    // 12.85 vs 11.01); RMSNorm over rows of 4-6 steps with a partial last
+    // step (78-88 VGPRs instead of 96-118, 5 waves per SIMD: (1,5120,2240)
+    // 9.55 vs 8.51 us; the LayerNorm chain there gains too but loses 2.3 %
+    // at (2,1024,2240), and keeps the look-ahead).
+    constexpr bool kAhead = !(TAIL == kTailFp8 && kXf32 && NV >= 7) && !(RMS && !UNIF && NV >= 4 && NV <= 6) &&
+                            !(TAIL == kTailChain && !UNIF && NV >= 7);
     if constexpr (kAhead) read_tab(0);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {

@@ -188,7 +188,8 @@ def test_ln_many_long_rows(ops, orc, D, B, extra):
 # rows with a partial last vector step whose instantiations hold fewer blocks per compute unit
 # than their shape asks for: the launch is sized to what is held (same lanes and merges), so
 # some waves walk two rows
-@pytest.mark.parametrize("B,S,D", [(1, 5120, 2240), (1, 4096, 4000), (2, 2600, 1800), (3, 1800, 3000)])
+@pytest.mark.parametrize("B,S,D", [(1, 5120, 2240), (1, 4096, 4000), (2, 2600, 1800), (3, 1800, 3000),
+                                   (2, 2100, 3840)])
 def test_ln_ragged_rows_held_blocks(ops, orc, B, S, D):
     g = torch.Generator().manual_seed(B * S + D)
     x = rand_bf16((B, S, D), g, std=2.0, mean=0.5).to(DEV)

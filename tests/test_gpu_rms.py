@@ -80,14 +80,16 @@ def test_rms_hidden_sizes(ops, orc, D):
     run_rms(ops, orc, x, sc, sh, 1e-6, what="D=%d" % D)
 
 
-def test_rms_ragged_rows_held_blocks(ops, orc):
-    """Rows of 7-8 steps with a partial last step: the launch is sized to the 3 blocks a compute
-    unit holds rather than the shape's 4."""
-    g = torch.Generator().manual_seed(4000)
-    x = rand_bf16((1, 4096, 4000), g, std=2.0, mean=0.5).to(DEV)
-    sc = rand_bf16((1, 4000), g, std=0.1).to(DEV)
-    sh = rand_bf16((1, 4000), g, std=0.1).to(DEV)
-    run_rms(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="held blocks (1,4096,4000)")
+@pytest.mark.parametrize("S,D", [(4096, 4000), (4096, 3840), (5120, 2240)])
+def test_rms_ragged_rows_held_blocks(ops, orc, S, D):
+    """Rows with a partial last step, enough of them for one row per wave of the launch: their
+    instantiations read each step's table values at that step (no look-ahead), so the waves the
+    launch asks for fit."""
+    g = torch.Generator().manual_seed(S + D)
+    x = rand_bf16((1, S, D), g, std=2.0, mean=0.5).to(DEV)
+    sc = rand_bf16((1, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((1, D), g, std=0.1).to(DEV)
+    run_rms(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what="held blocks (1,%d,%d)" % (S, D))
 
 
 @pytest.mark.parametrize("D,W", [(8192, 2), (16384, 4)])
