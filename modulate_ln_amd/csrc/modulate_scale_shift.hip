@@ -247,6 +247,9 @@ __global__ __launch_bounds__(256) void mod_tab(ModArgs a, int bpb) {
         }
         store_vec_nt<V>(orow + v * V, ov);
       }
+      // one step's table values live at a time: hoisting every step's LDS
+      // reads took 167 VGPRs at 8 steps (3 waves per SIMD), 60 with this
+      __builtin_amdgcn_sched_barrier(0);
     }
     s += row_step;
     if (s >= S) break;
@@ -325,17 +328,16 @@ int launch_mod(const ModArgs& a, hipStream_t st) {
 
 // Row-per-wave layout for per-sample rows of up to kModTabMaxNv vectors per
 // lane (all sizes: ALL), blocks per compute unit in total, measured on
-// MI355X against the chunk and one-shot kernels: (1,4096,4096) 12.3 us (3
-// per CU; 14.7 at 4) vs 12.55; (4,4096,3072) 35.2 vs 36.2; (4,4096,4096)
-// 46.1 (4 per CU; 47.7 at 3) vs 49.5; (2,1024,2240) 5.1 vs 6.6.
+// MI355X against the chunk and one-shot kernels: (1,4096,4096) 11.5 us
+// (12.2 when the kernel held 3 waves per SIMD and took 3 blocks per CU) vs
+// 12.55; (4,4096,3072) 35.0 vs 36.2; (4,4096,4096) 45.7 vs 49.5;
+// (2,1024,2240) 4.9 vs 6.6.  6 blocks per CU: (1,8192,4096) 25.7 against
+// 24.1 at 4.
 #ifndef ADALN_MOD_TAB
 #define ADALN_MOD_TAB 1
 #endif
 #ifndef ADALN_MOD_TAB_BPC
 #define ADALN_MOD_TAB_BPC 4
-#endif
-#ifndef ADALN_MOD_TAB_BPC_LONG
-#define ADALN_MOD_TAB_BPC_LONG 3
 #endif
 #ifndef ADALN_MOD_TAB_ALL
 #define ADALN_MOD_TAB_ALL 1
@@ -347,11 +349,7 @@ int launch_mod_tab(const ModArgs& a, hipStream_t st) {
   const int64_t B = a.R / a.S;
   const int cus = cu_count();
   const int64_t ncu = cus > 0 ? cus : 256;
-  // Long rows: when the grid would hold every row at once (one row per
-  // wave), every store waits for the end of the read phase; one block per
-  // CU fewer leaves a third of the waves a second row
-  const bool one_row_each = a.R <= (int64_t)ADALN_MOD_TAB_BPC * 4 * ncu;
-  const int64_t target = (int64_t)(NV >= 7 && one_row_each ? ADALN_MOD_TAB_BPC_LONG : ADALN_MOD_TAB_BPC) * ncu;
+  const int64_t target = (int64_t)ADALN_MOD_TAB_BPC * ncu;
   int64_t bpb = (target + B - 1) / B;
   bpb = std::max<int64_t>(1, std::min<int64_t>(bpb, (a.S + 3) / 4));
   const size_t lds = (size_t)2 * a.D * sizeof(float);
