@@ -141,21 +141,16 @@ def main() -> int:
     log("workload %s, %d rotated buffer sets (%.2f GiB)" % (wl.name, NB, footprint / 2 ** 30))
 
     K, Wm = args.steps, args.warmup
-    # device warm-up before the W warm-up steps: about DEVICE_WARMUP_MS of back-to-back steps,
-    # so the timed steps do not run while the clocks are still rising from the host-side setup
-    # above (measured: a kernel takes ~10 % longer in its first tens of milliseconds of
-    # back-to-back work than from then on)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(5):
+    # device warm-up before the W warm-up steps: back-to-back steps until their time is steady
+    # (at least DEVICE_WARMUP_MS, at most STEP_WARMUP_MAX_MS), so the timed steps do not run
+    # while the clocks are still rising from the host-side setup above (measured: a kernel
+    # takes ~10 % longer in its first tens of milliseconds of back-to-back work than from then
+    # on, and on some boxes far longer)
+    def step_call(i):
         lnm_calls[i % NB]()
         rga_calls[i % NB]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    per_ms = max(e0.elapsed_time(e1) / 5, 1e-4)
-    for i in range(int(min(20000, DEVICE_WARMUP_MS / per_ms))):
-        lnm_calls[i % NB]()
-        rga_calls[i % NB]()
+
+    warm_ms = warm_until_steady(step_call, stream, max_ms=STEP_WARMUP_MAX_MS)
     for i in range(Wm):
         lnm_calls[i % NB]()
         rga_calls[i % NB]()
@@ -200,7 +195,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) x with 1% x20 outliers, N(0,0.1) adaLN rows; see workloads.glm_square)",
         "config": {"workload": "ln_modulate + residual_gate_add, x (1,4096,4096) bf16, eps 1e-5",
-                   "B": B, "S": S, "D": D, "rotated_buffer_sets": NB, "device_warmup_ms": DEVICE_WARMUP_MS,
+                   "B": B, "S": S, "D": D, "rotated_buffer_sets": NB, "device_warmup_ms": round(warm_ms, 1),
                    "step_bytes": lb + rb},
         "us_per_call": {"ln_modulate": round(lnm_us, 3), "residual_gate_add": round(rga_us, 3)},
         "achieved_GBps": {"ln_modulate": round(lnm_gbps, 1), "residual_gate_add": round(rga_gbps, 1)},
@@ -301,31 +296,61 @@ def stream_reference(dev, stream, log, nbytes=1 << 30):
     return out
 
 
-DEVICE_WARMUP_MS = 50.0
+DEVICE_WARMUP_MS = 50.0       # at least this much back-to-back work before a measurement
+DEVICE_WARMUP_MAX_MS = 1000.0  # ... and at most this much while the call time still moves
+STEP_WARMUP_MAX_MS = 3000.0    # the same bound before the headline step loop
+WARMUP_CHUNK_MS = 20.0
+WARMUP_TOL = 0.01
 
 
-def time_loop(calls, n, stream, reps=20, warm_ms=DEVICE_WARMUP_MS):
+def warm_until_steady(call, stream, min_ms=DEVICE_WARMUP_MS, max_ms=DEVICE_WARMUP_MAX_MS):
+    """Issue back-to-back calls (call(i) launches the i-th) in chunks of about WARMUP_CHUNK_MS
+    until, after at least min_ms, two consecutive chunks take the same time per call within
+    WARMUP_TOL, or max_ms have passed; returns the milliseconds spent.  Some boxes leave the
+    clocks low for far longer than the tens of milliseconds most need (one measured the
+    headline at 13.7 µs for the first seconds of the run, 11.4 µs once a long workload had
+    run), so a fixed warm-up is either too short there or wasted elsewhere."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spent = e0.elapsed_time(e1)
+    n = int(max(1, min(20000, WARMUP_CHUNK_MS / max(spent / 10, 1e-4))))
+    prev, k = None, 10
+    while True:
+        e0.record(stream)
+        for _ in range(n):
+            call(k)
+            k += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        spent += ms
+        per = ms / n
+        if spent >= max_ms or (spent >= min_ms and prev is not None and abs(per - prev) <= WARMUP_TOL * prev):
+            return spent
+        prev = per
+
+
+def time_loop(calls, n, stream, reps=20):
     """µs per launch of back-to-back calls (rotating through calls): `reps` repetitions of
     n // reps launches each, events on the launch stream around every repetition, the
     median repetition reported.  Warm-up: two passes over every buffer set (at least 10
-    calls), so no set is touched for the first time inside the timed region, then about
-    `warm_ms` of back-to-back calls, so the device's clocks have left the state the host-side
-    setup between measurements leaves them in."""
+    calls), so no set is touched for the first time inside the timed region, then
+    back-to-back calls until their time per call is steady (warm_until_steady), so the
+    device's clocks have left the state the host-side setup between measurements leaves
+    them in."""
     import statistics
 
     import torch
 
     for i in range(max(10, 2 * len(calls))):
         calls[i % len(calls)]()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(10):
-        calls[i % len(calls)]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    per_ms = max(e0.elapsed_time(e1) / 10, 1e-4)
-    for i in range(int(min(20000, warm_ms / per_ms))):
-        calls[i % len(calls)]()
+    warm_until_steady(lambda i: calls[i % len(calls)](), stream)
     reps = max(1, min(reps, n))
     per = max(1, n // reps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
