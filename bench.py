@@ -142,15 +142,16 @@ def main() -> int:
 
     K, Wm = args.steps, args.warmup
     # device warm-up before the W warm-up steps: back-to-back steps until their time is steady
-    # (at least DEVICE_WARMUP_MS, at most STEP_WARMUP_MAX_MS), so the timed steps do not run
+    # (at least STEP_WARMUP_MIN_MS, at most STEP_WARMUP_MAX_MS), so the timed steps do not run
     # while the clocks are still rising from the host-side setup above (measured: a kernel
     # takes ~10 % longer in its first tens of milliseconds of back-to-back work than from then
-    # on, and on some boxes far longer)
+    # on, and on some boxes far longer; a ramp that slow changes too little from one chunk to
+    # the next for the steadiness test alone, hence the floor)
     def step_call(i):
         lnm_calls[i % NB]()
         rga_calls[i % NB]()
 
-    warm_ms = warm_until_steady(step_call, stream, max_ms=STEP_WARMUP_MAX_MS)
+    warm_ms = warm_until_steady(step_call, stream, min_ms=STEP_WARMUP_MIN_MS, max_ms=STEP_WARMUP_MAX_MS)
     for i in range(Wm):
         lnm_calls[i % NB]()
         rga_calls[i % NB]()
@@ -298,7 +299,8 @@ def stream_reference(dev, stream, log, nbytes=1 << 30):
 
 DEVICE_WARMUP_MS = 50.0       # at least this much back-to-back work before a measurement
 DEVICE_WARMUP_MAX_MS = 1000.0  # ... and at most this much while the call time still moves
-STEP_WARMUP_MAX_MS = 3000.0    # the same bound before the headline step loop
+STEP_WARMUP_MIN_MS = 1000.0    # before the headline step loop: a floor a slow ramp cannot pass
+STEP_WARMUP_MAX_MS = 3000.0    # ... and the bound there
 WARMUP_CHUNK_MS = 20.0
 WARMUP_TOL = 0.01
 
