@@ -315,25 +315,34 @@ def warm_until_steady(call, stream, min_ms=DEVICE_WARMUP_MS, max_ms=DEVICE_WARMU
     import torch
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(10):
-        call(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    spent = e0.elapsed_time(e1)
-    n = int(max(1, min(20000, WARMUP_CHUNK_MS / max(spent / 10, 1e-4))))
-    prev, k = None, 10
-    while True:
+    k = 0
+
+    def run_chunk(n):  # n back-to-back calls; their milliseconds on the device
+        nonlocal k
         e0.record(stream)
         for _ in range(n):
             call(k)
             k += 1
         e1.record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        return e0.elapsed_time(e1)
+
+    return steady_chunks(run_chunk, min_ms, max_ms)
+
+
+def steady_chunks(run_chunk, min_ms, max_ms, chunk_ms=WARMUP_CHUNK_MS, tol=WARMUP_TOL):
+    """The loop of warm_until_steady, apart from the device: run_chunk(n) runs n calls and
+    returns their milliseconds.  10 calls size the chunks to about chunk_ms; then chunks until,
+    after at least min_ms in all, two in a row agree per call within tol, or max_ms have
+    passed.  Returns the milliseconds spent."""
+    spent = run_chunk(10)
+    n = int(max(1, min(20000, chunk_ms / max(spent / 10, 1e-4))))
+    prev = None
+    while True:
+        ms = run_chunk(n)
         spent += ms
         per = ms / n
-        if spent >= max_ms or (spent >= min_ms and prev is not None and abs(per - prev) <= WARMUP_TOL * prev):
+        if spent >= max_ms or (spent >= min_ms and prev is not None and abs(per - prev) <= tol * prev):
             return spent
         prev = per
 
