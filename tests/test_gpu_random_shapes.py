@@ -3,7 +3,8 @@ oracle -- bit for bit in the order the library reports (GELU: within one bf16 ul
 oracle).  Row lengths cover every kernel family (one wave, several waves, ragged last steps,
 8-byte vectors), storage covers contiguous, padded, misaligned, sample-padded and transposed
 views, and several samples with their own adaLN rows.  The draws come from the seed alone, so
-every case is reproducible from its id."""
+every case is reproducible from its id.  A second set draws thousands of rows (around one row
+per wave of the launch) for the norm kernels and the fused update."""
 
 from __future__ import annotations
 
@@ -96,6 +97,31 @@ def test_norm_family_random(ops, orc, seed):
     run_fold(ops, orc, x, sc, sh, eps, what)
     if layout != "transposed":  # the bare modulation takes rows of unit stride
         run_mod(ops, orc, x, sc, sh, what=what)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_norm_family_random_many_rows(ops, orc, seed):
+    """Thousands of rows of up to 4096 elements (around and past one row per wave of the
+    launch, where the launch shapes switch: prefetching blocks past one row per wave of the
+    16-wave shape, launches sized to the blocks a compute unit holds): LayerNorm, RMSNorm,
+    the FP8 producer and, on vector-aligned rows, the fused update."""
+    r = np.random.default_rng(5000 + seed)
+    g = torch.Generator().manual_seed(5000 + seed)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    D = int(r.choice([4 * int(r.integers(257, 1025)), int(r.choice([2240, 3072, 3584, 3840, 4000, 4096]))]))
+    B = int(r.integers(1, 3))
+    S = (int(r.integers(12 * cus, 24 * cus)) + B - 1) // B
+    x = make_x(r, g, "contiguous" if r.random() < 0.7 else "padded", B, S, D)
+    sc = rand_bf16((B, D), g, std=0.1).to(DEV)
+    sh = rand_bf16((B, D), g, std=0.1).to(DEV)
+    what = "seed %d: (%d,%d,%d)" % (seed, B, S, D)
+    run_ln(ops, orc, x, sc, sh, 1e-6, stats=True, check_fp64=False, what=what)
+    run_rms(ops, orc, x, sc, sh, 1e-6, check_fp64=False, what=what)
+    run_fp8(ops, orc, x, sc, sh, 1e-6, 0.05, what)
+    if D % 8 == 0:
+        upd = rand_bf16((B, S, D), g).to(DEV)
+        gate = rand_bf16((B, D), g, std=0.5).to(DEV)
+        run_fused(ops, orc, x.contiguous(), gate, upd, sc, sh, 1e-6, what=what)
 
 
 @pytest.mark.parametrize("seed", range(16))
